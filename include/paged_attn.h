@@ -1,0 +1,278 @@
+/*
+ * paged_attn.h - C ABI of the MI355X (gfx950) paged GQA decode-attention
+ * library (libpaged_attn.so).
+ *
+ * The operation is one decode step of grouped-query attention over a paged
+ * K/V pool, as the lucebox PR #555 page states it (Summary): a single query
+ * token per sequence, Hq query heads sharing Hkv K/V heads, K/V rows reached
+ * through a per-sequence table of fixed-size blocks, F16, Q8_0 or Q4_0 K and V
+ * (chosen independently), the context of each sequence split into partitions
+ * whose partial results are recombined by a numerically stable split-softmax
+ * merge. For each sequence b and query head h, with r = Hq/Hkv, kv head
+ * g = h / r and L = seq_len[b]:
+ *
+ *     out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K[b,g,t,:]) V[b,g,t,:]
+ *
+ * over t < L (a zero row when L == 0).
+ *
+ * Conventions for every call
+ *   - All tensors live in device memory owned by the caller; the library
+ *     allocates no device memory and keeps no state across calls beyond the
+ *     cached device properties and the caller's kv_pool objects.
+ *   - GPU work is enqueued on the caller's stream (`stream` is a hipStream_t,
+ *     NULL = the null stream) and is asynchronous; results are valid once the
+ *     stream has reached that point.
+ *   - Host-detectable problems return a negative PA_ERR_* code synchronously
+ *     and enqueue nothing; pa_last_error() then returns a message that names
+ *     the entry point (the mlxcel issue #2153 page, Proposed Solution: a
+ *     refused launch reports the entry point instead of computing garbage).
+ *   - Pools are addressed with 64-bit byte offsets everywhere, so a pool side
+ *     may hold more than 2^32 elements (mlxcel issue #2153, Problem and
+ *     Proposed Solution: the offset (row*block_size + slot)*stride +
+ *     kv_head*dim is widened before multiplying; a pool of exactly 2^32
+ *     elements addresses its last element). There is no size refusal for
+ *     large pools.
+ *
+ * Layouts (row-major, little endian)
+ *   q          float32 [B, Hq, D]
+ *   out        float32 [B, Hq, D]
+ *   k_pool     uint8   [nblocks, block_size, Hkv, row_bytes(k_type, D)]
+ *   v_pool     uint8   [nblocks, block_size, Hkv, row_bytes(v_type, D)]
+ *   block_table int32  [B, max_blocks]: physical block of each logical block;
+ *              only entries j < ceil(seq_len[b]/block_size) are ever read.
+ *   seq_len    int32   [B] (device memory)
+ *   One row holds the D values of one (token slot, kv head):
+ *     PA_F16  : D IEEE binary16 values                      (2*D bytes)
+ *     PA_Q8_0 : D/32 blocks {f16 d; int8 q[32]}, x = d*q    (34*D/32 bytes)
+ *     PA_Q4_0 : D/32 blocks {f16 d; uint8 n[16]}; element j of a block is
+ *               (n[j] & 15) - 8, element j+16 is (n[j] >> 4) - 8, times d
+ *                                                           (18*D/32 bytes)
+ *
+ * Supported shapes: D in {128, 256}; r = Hq/Hkv integral, 1 <= r <= 16;
+ * block_size a power of two in [16, 256]; 1 <= B <= 1024. Others return
+ * PA_ERR_UNSUPPORTED ("unsupported combinations fail explicitly", lucebox
+ * PR #555, Scope).
+ *
+ * Numerics: q is rounded to f16 after the softmax scale (and log2 e) is folded
+ * in; dequantised K/V values are rounded to f16; dot products, softmax and
+ * accumulation run in fp32. Live K/V values must lie inside the f16 range
+ * (true for any Q8_0/Q4_0 block quantised from f16-range data).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* K/V element formats (nine K/V pairs: lucebox PR #555, Validation). */
+enum { PA_F16 = 0, PA_Q8_0 = 1, PA_Q4_0 = 2 };
+
+/* Return codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* null pointer, inconsistent shape, ws too small, bad argument */
+  PA_ERR_UNSUPPORTED = -2,  /* a shape/type combination this build does not compile */
+  PA_ERR_CAPACITY = -3,     /* kv_pool: not enough free blocks (state unchanged) */
+  PA_ERR_STALE_HANDLE = -4, /* kv_pool: released, double-released or pre-reset handle */
+  PA_ERR_HIP = -5           /* a HIP runtime call failed */
+};
+
+/* Bits of the device status word (see paged_attn_status). */
+enum {
+  PA_STATUS_BAD_BLOCK_ID = 1, /* a live table entry was < 0 or >= nblocks; that
+                                 sequence's output rows are NaN */
+  PA_STATUS_BAD_SEQ_LEN = 2   /* seq_len[b] < 0 or longer than the plan admits
+                                 (min(max_blocks*block_size, p_max*psize), at
+                                 least plan->max_seq_len); it was clamped into
+                                 range */
+};
+
+typedef struct pa_shape {
+  int32_t B;          /* sequences in the batch */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* K/V heads; Hq % Hkv == 0 */
+  int32_t D;          /* head dimension */
+  int32_t block_size; /* token slots per block */
+  int32_t nblocks;    /* blocks in each pool */
+  int32_t max_blocks; /* columns of the block table */
+  int32_t k_type;     /* PA_F16 / PA_Q8_0 / PA_Q4_0 */
+  int32_t v_type;
+} pa_shape;
+
+/* A decode plan: fixed launch geometry and workspace size for one shape.
+ * Produced by paged_attn_plan; treat as read-only. */
+typedef struct pa_plan {
+  pa_shape shape;
+  float scale;          /* softmax scale applied to q.k */
+  int32_t psize;        /* tokens per context partition (multiple of 32) */
+  int32_t p_max;        /* partitions of the longest admissible sequence */
+  int32_t max_seq_len;  /* longest seq_len the plan admits */
+  int32_t grid;         /* workgroups launched by paged_attn_decode */
+  int32_t num_cus;      /* compute units the plan was sized for */
+  int32_t direct;       /* 1: p_max == 1, decode writes out, merge is a no-op */
+  int32_t reserved;
+  uint64_t ws_bytes;    /* workspace bytes paged_attn_decode/merge need */
+} pa_plan;
+
+/* Bytes of one encoded row of D values of `type`, or a negative PA_ERR_*. */
+int32_t pa_row_bytes(int32_t type, int32_t D);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * paged_attn_plan - choose the context partitioning and launch geometry.
+ *
+ * The partition size follows the lucebox PR #555 page (Summary:
+ * occupancy-aware context partitioning): it is sized from the number of
+ * compute units and the work in the batch, never below the size at which the
+ * partial-result traffic would exceed a few percent of the K/V bytes.
+ *   max_seq_len      longest seq_len any later decode with this plan will see
+ *                    (<= max_blocks*block_size)
+ *   total_tokens     sum of seq_len over the batch if known (sizes the grid for
+ *                    ragged batches); 0 = assume B*max_seq_len. Only speed
+ *                    depends on it: every live partition is processed for any
+ *                    value.
+ *   num_cus          compute units to size for; 0 = query the current device
+ *   force_partitions 0 = automatic; 1 = direct mode (one partition, no merge:
+ *                    the lucebox page's forced single partition); n > 1 = at
+ *                    most n partitions of equal size for the longest sequence
+ *   partition_tokens 0 = automatic, else the exact partition size (rounded up
+ *                    to a multiple of 32); overrides force_partitions
+ *   scale            softmax scale; 0 = 1/sqrt(D)
+ * Returns PA_OK and fills *plan, or a negative code.
+ */
+int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t total_tokens,
+                        int32_t num_cus, int32_t force_partitions, int32_t partition_tokens,
+                        float scale, pa_plan* plan);
+
+/*
+ * Workspace layout (ws, plan->ws_bytes bytes, device memory, 256-byte aligned):
+ *   [0, 4)      uint32 status word (PA_STATUS_* bits); must be zero before the
+ *               first decode; paged_attn_status reads and clears it
+ *   [4, 256)    reserved
+ *   partials    only when plan->direct == 0, at offset 256:
+ *               float o [B][Hq][p_max][D]  normalised output of each partition
+ *               float ml[B][Hq][p_max][2]  (m, l): m = max over the partition of
+ *                                          the base-2 logit log2(e)*scale*q.k,
+ *                                          l = sum of 2^(logit - m)
+ *               Partition p of sequence b covers tokens [p*psize,
+ *               min(seq_len, (p+1)*psize)); only p < ceil(seq_len/psize) is
+ *               written or read. A partition that met a bad block id holds
+ *               NaN in m.
+ */
+
+/*
+ * paged_attn_decode - attention of one decode step over the paged pool.
+ *
+ * Computes, for every live (sequence, K/V head, partition), the partial
+ * softmax statistics and normalised partial output of all r query heads of the
+ * group from one pass over the partition's K/V rows (lucebox PR #555, Summary:
+ * all GQA heads of a K/V group per K/V row loaded, exp2 softmax, partials
+ * stored normalised; mlxcel issue #2153: 64-bit pool offsets). In direct mode
+ * writes out[] instead of partials.
+ *   q, k_pool, v_pool, seq_len, out: as in the layout table above
+ *   block_table  NULL selects the contiguous layout: sequence b's logical
+ *                block j is physical block b*max_blocks + j (computed, not
+ *                read; the TensorFold PR #1418 page's null page table). The
+ *                same plan then gives bit-identical results to a table that
+ *                names the same rows.
+ *   ws, ws_bytes workspace of at least plan->ws_bytes bytes
+ *   out          written only in direct mode (may be NULL otherwise)
+ * Results are deterministic: fixed reduction order, no floating-point atomics.
+ * A live table entry outside [0, nblocks) is never dereferenced: the status
+ * bit is set and the rows of that sequence become NaN.
+ */
+int32_t paged_attn_decode(const pa_plan* plan, const float* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_len, void* ws, uint64_t ws_bytes, float* out,
+                          void* stream);
+
+/*
+ * paged_attn_merge - stable split-softmax merge of the partials in ws.
+ *
+ * For each (b, h) over its live partitions p < ceil(seq_len[b]/psize):
+ *   M = max_p m_p;  w_p = 2^(m_p - M) * l_p;  out = sum_p w_p o_p / sum_p w_p
+ * (lucebox PR #555, Summary; llama.cpp PR #13 HRX, Changes: per-block
+ * normalisation scale). seq_len = 0 gives a zero row; a NaN m gives a NaN
+ * row. A no-op returning PA_OK in direct mode.
+ */
+int32_t paged_attn_merge(const pa_plan* plan, const void* ws, uint64_t ws_bytes,
+                         const int32_t* seq_len, float* out, void* stream);
+
+/* paged_attn_step - paged_attn_decode followed by paged_attn_merge. */
+int32_t paged_attn_step(const pa_plan* plan, const float* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table,
+                        const int32_t* seq_len, void* ws, uint64_t ws_bytes, float* out,
+                        void* stream);
+
+/*
+ * paged_kv_gather - copy raw encoded rows out of a pool through the table,
+ * with the same 64-bit address computation the decode kernel uses (the
+ * mlxcel issue #2153 page, Scope: the gather path).
+ *   pool      k_pool (which = 0, row format k_type) or v_pool (which = 1)
+ *   b, t0, n  rows of tokens t0 .. t0+n-1 of sequence b; requires
+ *             0 <= t0, t0+n <= max_blocks*block_size and every table entry
+ *             they touch inside [0, nblocks) (checked on the device: rows
+ *             behind a bad entry are left untouched and the status bit is set)
+ *   dst       uint8 [n, Hkv, row_bytes]
+ *   ws        workspace whose status word records bad entries (may be NULL)
+ */
+int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
+                        const int32_t* block_table, int32_t b, int32_t t0, int32_t n, void* dst,
+                        void* ws, void* stream);
+
+/*
+ * paged_attn_status - synchronise `stream`, then read and clear the status
+ * word of ws into *flags (PA_STATUS_* bits).
+ */
+int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
+
+/*
+ * Fixed-block allocator over the block ids [0, nblocks) of a caller-owned
+ * pool (lucebox PR #555, Summary and Validation: exact fixed-block allocator,
+ * transactional allocation, stale-handle detection, immediate release, pool
+ * reset across requests). Host only; thread-safe per pool object.
+ *
+ * An allocation is a list of block ids, in the order they were handed out,
+ * named by a 64-bit handle (slot index and generation; 0 is never a valid
+ * handle). Blocks go back to the pool the moment their allocation is
+ * released. Any use of a handle that was released, released twice or issued
+ * before a reset returns PA_ERR_STALE_HANDLE and changes nothing.
+ */
+typedef struct kv_pool kv_pool;
+
+int32_t kv_pool_create(int32_t nblocks, kv_pool** pool);
+int32_t kv_pool_destroy(kv_pool* pool);
+
+/* Append n blocks to the allocation *handle (0 = open a new one and store its
+ * handle). All or nothing: with fewer than n free blocks returns
+ * PA_ERR_CAPACITY and leaves the pool and *handle unchanged. Writes the n new
+ * ids to ids_out (may be NULL when n == 0). */
+int32_t kv_pool_alloc(kv_pool* pool, int32_t n, int32_t* ids_out, uint64_t* handle);
+
+/* Return every block of the allocation to the pool; the handle goes stale. */
+int32_t kv_pool_release(kv_pool* pool, uint64_t handle);
+
+/* Return every block; every handle issued so far goes stale. */
+int32_t kv_pool_reset(kv_pool* pool);
+
+/* Free blocks (>= 0) or a negative code. */
+int32_t kv_pool_free_count(const kv_pool* pool);
+
+/* Blocks held by an allocation (>= 0) or a negative code. */
+int32_t kv_pool_count(const kv_pool* pool, uint64_t handle);
+
+/* Copy up to cap ids of an allocation, in order, to ids_out; returns the
+ * number held (may exceed cap) or a negative code. */
+int32_t kv_pool_blocks(const kv_pool* pool, uint64_t handle, int32_t* ids_out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,221 @@
+"""Python binding of libpaged_attn (paged GQA decode attention on MI355X).
+
+Argument marshalling only: every function forwards to the C-ABI entry point of
+the same name in libpaged_attn.so (declared in include/paged_attn.h); all
+computation happens in the library's HIP kernels. Torch tensors are accepted
+for device buffers (their data_ptr() is passed) and the current torch stream
+is used when no stream is given. Importing this package fails loudly when the
+library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+
+PA_F16, PA_Q8_0, PA_Q4_0 = 0, 1, 2
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_CAPACITY, PA_ERR_STALE_HANDLE, PA_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+PA_STATUS_BAD_BLOCK_ID, PA_STATUS_BAD_SEQ_LEN = 1, 2
+TYPES = {"f16": PA_F16, "q8_0": PA_Q8_0, "q4_0": PA_Q4_0}
+
+__all__ = ["PaShape", "PaPlan", "PaError", "lib", "pa_row_bytes", "pa_last_error",
+           "paged_attn_plan", "paged_attn_decode", "paged_attn_merge", "paged_attn_step",
+           "paged_kv_gather", "paged_attn_status", "KvPool", "workspace", "shape_of"]
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("nblocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("k_type", ctypes.c_int32), ("v_type", ctypes.c_int32)]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [("shape", PaShape), ("scale", ctypes.c_float), ("psize", ctypes.c_int32),
+                ("p_max", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("direct", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ws_bytes", ctypes.c_uint64)]
+
+    def __repr__(self):
+        s = self.shape
+        return (f"PaPlan(B={s.B}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D}, bs={s.block_size}, "
+                f"psize={self.psize}, p_max={self.p_max}, grid={self.grid}, "
+                f"direct={self.direct}, ws_bytes={self.ws_bytes})")
+
+
+class PaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+            "or python paged_kv_gqa_attn_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, u32, u64, i64, vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
+    P = ctypes.POINTER
+    sig = {
+        "pa_row_bytes": (i32, [i32, i32]),
+        "pa_last_error": (ctypes.c_char_p, []),
+        "paged_attn_plan": (i32, [P(PaShape), i32, i64, i32, i32, i32, ctypes.c_float, P(PaPlan)]),
+        "paged_attn_decode": (i32, [P(PaPlan), vp, vp, vp, vp, vp, vp, u64, vp, vp]),
+        "paged_attn_merge": (i32, [P(PaPlan), vp, u64, vp, vp, vp]),
+        "paged_attn_step": (i32, [P(PaPlan), vp, vp, vp, vp, vp, vp, u64, vp, vp]),
+        "paged_kv_gather": (i32, [P(PaPlan), vp, i32, vp, i32, i32, i32, vp, vp, vp]),
+        "paged_attn_status": (i32, [vp, vp, P(u32)]),
+        "kv_pool_create": (i32, [i32, P(vp)]),
+        "kv_pool_destroy": (i32, [vp]),
+        "kv_pool_alloc": (i32, [vp, i32, P(i32), P(u64)]),
+        "kv_pool_release": (i32, [vp, u64]),
+        "kv_pool_reset": (i32, [vp]),
+        "kv_pool_free_count": (i32, [vp]),
+        "kv_pool_count": (i32, [vp, u64]),
+        "kv_pool_blocks": (i32, [vp, u64, P(i32), i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def pa_last_error() -> str:
+    return lib.pa_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise PaError(rc, pa_last_error())
+    return rc
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def pa_row_bytes(type_: int, D: int) -> int:
+    return _check(lib.pa_row_bytes(type_, D))
+
+
+def shape_of(B, Hq, Hkv, D, block_size, nblocks, max_blocks, k_type, v_type) -> PaShape:
+    kt = TYPES.get(k_type, k_type)
+    vt = TYPES.get(v_type, v_type)
+    return PaShape(B, Hq, Hkv, D, block_size, nblocks, max_blocks, kt, vt)
+
+
+def paged_attn_plan(shape: PaShape, max_seq_len: int, total_tokens: int = 0, num_cus: int = 0,
+                    force_partitions: int = 0, partition_tokens: int = 0,
+                    scale: float = 0.0) -> PaPlan:
+    plan = PaPlan()
+    _check(lib.paged_attn_plan(ctypes.byref(shape), max_seq_len, total_tokens, num_cus,
+                               force_partitions, partition_tokens, scale, ctypes.byref(plan)))
+    return plan
+
+
+def paged_attn_decode(plan: PaPlan, q, k_pool, v_pool, block_table, seq_len, ws, out=None,
+                      stream=None, ws_bytes: Optional[int] = None) -> None:
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib.paged_attn_decode(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(block_table), _ptr(seq_len), _ptr(ws), nb, _ptr(out),
+                                 _stream(stream)))
+
+
+def paged_attn_merge(plan: PaPlan, ws, seq_len, out, stream=None,
+                     ws_bytes: Optional[int] = None) -> None:
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib.paged_attn_merge(ctypes.byref(plan), _ptr(ws), nb, _ptr(seq_len), _ptr(out),
+                                _stream(stream)))
+
+
+def paged_attn_step(plan: PaPlan, q, k_pool, v_pool, block_table, seq_len, ws, out,
+                    stream=None, ws_bytes: Optional[int] = None) -> None:
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib.paged_attn_step(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(block_table), _ptr(seq_len), _ptr(ws), nb, _ptr(out),
+                               _stream(stream)))
+
+
+def paged_kv_gather(plan: PaPlan, pool, which: int, block_table, b: int, t0: int, n: int, dst,
+                    ws=None, stream=None) -> None:
+    _check(lib.paged_kv_gather(ctypes.byref(plan), _ptr(pool), which, _ptr(block_table), b, t0,
+                               n, _ptr(dst), _ptr(ws), _stream(stream)))
+
+
+def paged_attn_status(ws, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(lib.paged_attn_status(_ptr(ws), _stream(stream), ctypes.byref(flags)))
+    return flags.value
+
+
+def workspace(plan: PaPlan, device="cuda", extra: int = 0):
+    """A zero-filled uint8 workspace tensor of plan.ws_bytes (+ extra) bytes."""
+    import torch
+    return torch.zeros(int(plan.ws_bytes) + extra, dtype=torch.uint8, device=device)
+
+
+class KvPool:
+    """Handle-based fixed-block allocator (kv_pool_* entry points)."""
+
+    def __init__(self, nblocks: int):
+        h = ctypes.c_void_p()
+        _check(lib.kv_pool_create(nblocks, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            _check(lib.kv_pool_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int, handle: int = 0):
+        ids = (ctypes.c_int32 * max(n, 1))()
+        h = ctypes.c_uint64(handle)
+        _check(lib.kv_pool_alloc(self._h, n, ids, ctypes.byref(h)))
+        return h.value, list(ids[:n])
+
+    def release(self, handle: int) -> None:
+        _check(lib.kv_pool_release(self._h, handle))
+
+    def reset(self) -> None:
+        _check(lib.kv_pool_reset(self._h))
+
+    def free_count(self) -> int:
+        return _check(lib.kv_pool_free_count(self._h))
+
+    def count(self, handle: int) -> int:
+        return _check(lib.kv_pool_count(self._h, handle))
+
+    def blocks(self, handle: int):
+        n = _check(lib.kv_pool_blocks(self._h, handle, None, 0))
+        ids = (ctypes.c_int32 * max(n, 1))()
+        _check(lib.kv_pool_blocks(self._h, handle, ids, n))
+        return list(ids[:n])

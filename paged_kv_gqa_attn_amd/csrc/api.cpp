@@ -1,0 +1,290 @@
+// C ABI of libpaged_attn: planning, host-side validation and dispatch of the
+// decode, merge and gather kernels. Host-detectable problems are refused
+// synchronously with a message naming the entry point (mlxcel issue #2153,
+// Proposed Solution and Implementation Notes: refused launches report the
+// entry point; the pool itself is never refused for its size).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/paged_attn.h"
+#include "pa_host.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_err;
+
+constexpr int kMaxB = 1024;
+constexpr int kMaxR = 16;
+constexpr int kTileTokens = 32;
+constexpr int kWavesPerUnit = 4;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int ilog2_exact(int32_t v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) != v) ++s;
+  return s;
+}
+
+// Validates a shape; `who` names the entry point in messages.
+int32_t check_shape(const pa_shape* s, const char* who) {
+  if (!s) return fail(PA_ERR_INVALID, "%s: null shape", who);
+  if (s->B < 1 || s->Hq < 1 || s->Hkv < 1 || s->D < 1 || s->nblocks < 1 || s->max_blocks < 1)
+    return fail(PA_ERR_INVALID, "%s: B, Hq, Hkv, D, nblocks and max_blocks must be >= 1", who);
+  if (s->Hq % s->Hkv)
+    return fail(PA_ERR_INVALID, "%s: Hq (%d) is not a multiple of Hkv (%d)", who, s->Hq, s->Hkv);
+  for (int32_t t : {s->k_type, s->v_type})
+    if (t < PA_F16 || t > PA_Q4_0) return fail(PA_ERR_INVALID, "%s: unknown K/V type %d", who, t);
+  const int bs_shift = ilog2_exact(s->block_size);
+  if (bs_shift < 0) return fail(PA_ERR_INVALID, "%s: block_size %d is not a power of two", who, s->block_size);
+  if (s->D != 128 && s->D != 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head dimension D=%d is not compiled (supported: 128, 256)", who, s->D);
+  if (s->Hq / s->Hkv > kMaxR)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per K/V head (at most %d)", who, s->Hq / s->Hkv, kMaxR);
+  if (s->block_size < 16 || s->block_size > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d outside [16, 256]", who, s->block_size);
+  if (s->B > kMaxB) return fail(PA_ERR_UNSUPPORTED, "%s: B=%d above %d", who, s->B, kMaxB);
+  if (int64_t(s->max_blocks) * s->block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID, "%s: max_blocks*block_size exceeds the int32 token range", who);
+  return PA_OK;
+}
+
+int32_t check_plan(const pa_plan* p, const char* who) {
+  if (!p) return fail(PA_ERR_INVALID, "%s: null plan", who);
+  int32_t rc = check_shape(&p->shape, who);
+  if (rc) return rc;
+  if (p->psize < kTileTokens || p->psize % kTileTokens || p->p_max < 1 || p->grid < 1 ||
+      !(p->scale == p->scale) || p->direct != (p->p_max == 1))
+    return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_plan", who);
+  return PA_OK;
+}
+
+uint64_t ws_bytes_for(const pa_shape& s, int p_max, bool direct) {
+  uint64_t bytes = 256;
+  if (!direct) bytes += uint64_t(s.B) * s.Hq * p_max * uint64_t(s.D + 2) * 4u;
+  return (bytes + 255) & ~uint64_t(255);
+}
+
+}  // namespace
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+void clear_error() { g_err.clear(); }
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" const char* pa_last_error(void) { return g_err.c_str(); }
+
+extern "C" int32_t pa_row_bytes(int32_t type, int32_t D) {
+  if (D < 1) return fail(PA_ERR_INVALID, "pa_row_bytes: D must be >= 1");
+  switch (type) {
+    case PA_F16: return 2 * D;
+    case PA_Q8_0:
+    case PA_Q4_0:
+      if (D % 32) return fail(PA_ERR_INVALID, "pa_row_bytes: quantised rows need D %% 32 == 0");
+      return (type == PA_Q8_0 ? 34 : 18) * (D / 32);
+  }
+  return fail(PA_ERR_INVALID, "pa_row_bytes: unknown type %d", type);
+}
+
+extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t total_tokens,
+                                   int32_t num_cus, int32_t force_partitions,
+                                   int32_t partition_tokens, float scale, pa_plan* plan) {
+  const char* who = "paged_attn_plan";
+  if (!plan) return fail(PA_ERR_INVALID, "%s: null plan", who);
+  int32_t rc = check_shape(shape, who);
+  if (rc) return rc;
+  const pa_shape& s = *shape;
+  const int64_t cap = int64_t(s.max_blocks) * s.block_size;
+  if (max_seq_len < 0 || max_seq_len > cap)
+    return fail(PA_ERR_INVALID, "%s: max_seq_len %d outside [0, max_blocks*block_size=%lld]", who,
+                max_seq_len, (long long)cap);
+  if (total_tokens < 0 || force_partitions < 0 || partition_tokens < 0)
+    return fail(PA_ERR_INVALID, "%s: negative total_tokens/force_partitions/partition_tokens", who);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(PA_ERR_HIP, "%s: could not query the device's compute-unit count", who);
+  }
+  if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
+
+  const int64_t L = max_seq_len;
+  const int64_t rbk = pa_row_bytes(s.k_type, s.D), rbv = pa_row_bytes(s.v_type, s.D);
+  int64_t psize;
+  if (partition_tokens > 0) {
+    psize = round_up(partition_tokens, kTileTokens);
+  } else if (force_partitions >= 1) {
+    psize = round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
+  } else {
+    // Occupancy-aware partitioning (lucebox PR #555, Summary): aim for about
+    // four workgroups per compute unit over the whole batch, but never split
+    // so finely that partial results (written and read once more by the merge)
+    // exceed ~4% of the K/V bytes of a partition.
+    const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
+    const int64_t units_target = int64_t(num_cus) * 4;
+    const int64_t per_unit = kTileTokens * kWavesPerUnit;
+    const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * s.Hkv, units_target)), per_unit);
+    const double part_bytes = double(s.Hq) * (s.D + 2) * 4.0 * 2.0;
+    const double kv_per_token = double(s.Hkv) * double(rbk + rbv);
+    const int64_t floor_tok = round_up(int64_t(std::ceil(part_bytes / (0.04 * kv_per_token))), per_unit);
+    psize = std::max(bal, floor_tok);
+  }
+  if (psize >= L) psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
+  if (psize > INT32_MAX - kTileTokens) return fail(PA_ERR_INVALID, "%s: partition size overflows", who);
+  const int64_t p_max = std::max<int64_t>(1, ceil_div(L, psize));
+  const bool direct = p_max == 1;
+  int64_t bp_upper = int64_t(s.B) * p_max;
+  if (total_tokens > 0) bp_upper = std::min(bp_upper, ceil_div(total_tokens, psize) + s.B);
+  const int64_t units = std::max<int64_t>(1, bp_upper * s.Hkv);
+  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * 8);
+
+  std::memset(plan, 0, sizeof *plan);
+  plan->shape = s;
+  plan->scale = scale == 0.0f ? float(1.0 / std::sqrt(double(s.D))) : scale;
+  plan->psize = int32_t(psize);
+  plan->p_max = int32_t(p_max);
+  plan->max_seq_len = max_seq_len;
+  plan->grid = int32_t(grid);
+  plan->num_cus = num_cus;
+  plan->direct = direct ? 1 : 0;
+  plan->ws_bytes = ws_bytes_for(s, int(p_max), direct);
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table,
+                                     const int32_t* seq_len, void* ws, uint64_t ws_bytes,
+                                     float* out, void* stream) {
+  const char* who = "paged_attn_decode";
+  int32_t rc = check_plan(plan, who);
+  if (rc) return rc;
+  if (!q || !k_pool || !v_pool || !seq_len || !ws)
+    return fail(PA_ERR_INVALID, "%s: null q, k_pool, v_pool, seq_len or ws", who);
+  if (plan->direct && !out) return fail(PA_ERR_INVALID, "%s: direct mode needs out", who);
+  if (ws_bytes < plan->ws_bytes)
+    return fail(PA_ERR_INVALID, "%s: workspace of %llu bytes, plan needs %llu", who,
+                (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
+  const pa_shape& s = plan->shape;
+  DecodeArgs a{};
+  a.q = q;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.table = block_table;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.status = static_cast<uint32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 256);
+  a.part_ml = a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D;
+  a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.r = s.Hq / s.Hkv;
+  a.nblocks = s.nblocks; a.max_blocks = s.max_blocks; a.block_size = s.block_size;
+  a.bs_shift = ilog2_exact(s.block_size);
+  a.psize = plan->psize; a.p_max = plan->p_max; a.grid = plan->grid;
+  a.cap_tokens = int32_t(std::min<int64_t>(int64_t(s.max_blocks) * s.block_size,
+                                           int64_t(plan->p_max) * plan->psize));
+  a.k_type = s.k_type; a.v_type = s.v_type;
+  a.direct = plan->direct;
+  a.qscale = float(double(plan->scale) * 1.4426950408889634);   // scale * log2(e)
+  hipError_t e = launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_attn_merge(const pa_plan* plan, const void* ws, uint64_t ws_bytes,
+                                    const int32_t* seq_len, float* out, void* stream) {
+  const char* who = "paged_attn_merge";
+  int32_t rc = check_plan(plan, who);
+  if (rc) return rc;
+  if (plan->direct) { clear_error(); return PA_OK; }
+  if (!ws || !seq_len || !out) return fail(PA_ERR_INVALID, "%s: null ws, seq_len or out", who);
+  if (ws_bytes < plan->ws_bytes)
+    return fail(PA_ERR_INVALID, "%s: workspace of %llu bytes, plan needs %llu", who,
+                (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
+  const pa_shape& s = plan->shape;
+  MergeArgs a{};
+  a.part_o = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + 256);
+  a.part_ml = a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.B = s.B; a.Hq = s.Hq; a.D = s.D; a.psize = plan->psize; a.p_max = plan->p_max;
+  a.cap_tokens = int32_t(std::min<int64_t>(int64_t(s.max_blocks) * s.block_size,
+                                           int64_t(plan->p_max) * plan->psize));
+  hipError_t e = launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_attn_step(const pa_plan* plan, const float* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const int32_t* seq_len, void* ws, uint64_t ws_bytes, float* out,
+                                   void* stream) {
+  if (!out) return fail(PA_ERR_INVALID, "paged_attn_step: null out");
+  int32_t rc = paged_attn_decode(plan, q, k_pool, v_pool, block_table, seq_len, ws, ws_bytes, out, stream);
+  if (rc) return rc;
+  return paged_attn_merge(plan, ws, ws_bytes, seq_len, out, stream);
+}
+
+extern "C" int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
+                                   const int32_t* block_table, int32_t b, int32_t t0, int32_t n,
+                                   void* dst, void* ws, void* stream) {
+  const char* who = "paged_kv_gather";
+  int32_t rc = check_plan(plan, who);
+  if (rc) return rc;
+  const pa_shape& s = plan->shape;
+  if (!pool || (n > 0 && !dst)) return fail(PA_ERR_INVALID, "%s: null pool or dst", who);
+  if (which != 0 && which != 1) return fail(PA_ERR_INVALID, "%s: which must be 0 (K) or 1 (V)", who);
+  if (b < 0 || b >= s.B) return fail(PA_ERR_INVALID, "%s: sequence %d outside [0, B)", who, b);
+  if (t0 < 0 || n < 0 || int64_t(t0) + n > int64_t(s.max_blocks) * s.block_size)
+    return fail(PA_ERR_INVALID, "%s: tokens [%d, %d+%d) outside the table", who, t0, t0, n);
+  GatherArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.table = block_table;
+  a.dst = static_cast<uint8_t*>(dst);
+  a.status = static_cast<uint32_t*>(ws);
+  a.b = b; a.t0 = t0; a.n = n;
+  a.Hkv = s.Hkv;
+  a.row_bytes = pa_row_bytes(which == 0 ? s.k_type : s.v_type, s.D);
+  a.nblocks = s.nblocks; a.max_blocks = s.max_blocks; a.block_size = s.block_size;
+  a.bs_shift = ilog2_exact(s.block_size);
+  hipError_t e = launch_gather(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags) {
+  const char* who = "paged_attn_status";
+  if (!ws || !flags) return fail(PA_ERR_INVALID, "%s: null ws or flags", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemsetAsync(ws, 0, sizeof v, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+  *flags = v;
+  clear_error();
+  return PA_OK;
+}

@@ -1,0 +1,643 @@
+// Paged GQA decode attention: the partition kernel.
+//
+// What it computes (lucebox PR #555, Summary): for each live (sequence b,
+// K/V head g, context partition p) the r = Hq/Hkv query heads of the group
+// attend over the partition's tokens; the kernel writes each head's running
+// max m (base-2 logits), sum l and normalised output o, or the final output
+// when a single partition covers the sequence ("direct" mode).
+//
+// How it maps onto gfx950 (the lucebox design - one warp per K/V group, q8_1
+// pre-quantised Q, 32-token score tiles, exp2 softmax - is prior art; this
+// is a CDNA4 design around the fact that decode attention is HBM-bound):
+//   * Workgroup = 4 wave64s working on one (b, g, p) unit. Wave w takes the
+//     32-token tiles w, w+4, w+8, ... of the partition and the four partial
+//     softmax states are combined through LDS at the end, so a unit gets four
+//     tiles in flight without more partial-result traffic.
+//   * The r query heads of the group form the N side of 16x16x32 f16 MFMAs
+//     (padded to 16 columns). Scores: S^T[t,h] = K[t,:] . Q[h,:]. PV:
+//     O^T[d,h] += V^T[d,t] P^T[t,h]; the score MFMA's output layout (lane
+//     holds head lane%16, tokens 4*(lane/16)+i) is exactly the B operand of
+//     the PV MFMA, and both MFMAs keep head = lane%16, so the online softmax
+//     never moves data between lanes except for two xor-shuffle reductions.
+//   * K/V rows stream from HBM straight into registers in MFMA operand
+//     order, double-buffered per wave: the next tile's loads are in flight
+//     while the current tile is computed. The contraction index of the score
+//     MFMA (the head dimension) is permuted per format so every lane reads
+//     whole 16-byte chunks (F16) or whole ggml blocks (Q8_0/Q4_0); Q is laid
+//     out with the same permutation. V is transposed in registers (v_perm).
+//   * The block table is read once per 16-row group (block_size >= 16) with a
+//     scalar load; the row address is 64-bit (mlxcel issue #2153).
+//   * Dead slots (t >= seq_len in the last block, or a clamped group past the
+//     end) are never used: their scores are selected to -inf and their V
+//     values zeroed before the PV MFMA, so NaN/Inf junk cannot leak.
+//   * Units are spread over the grid with an XCD-aware swizzle so the Hkv
+//     units of one (b, p) - which share cache lines of the pool for the
+//     quantised formats - run on the same XCD and L2.
+#include "pa_device.h"
+#include "pa_host.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;       // tokens per tile = two 16-row MFMA groups
+constexpr uint32_t kMagic = 0x64006400u;   // f16 1024.0 in both halves
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x2 splat2(f16 x) { return f16x2{x, x}; }
+
+// ---------------------------------------------------------------------------
+// Signed int8 pair -> f16: bytes b0,b2 of `q` (or b1,b3 after >>8) as exact
+// f16 integers, then one rounding when multiplied by the block scale.
+// (x ^ 0x80) placed under exponent 0x64 is 1024 + x + 128.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f16x2 i8pair_to_f16(uint32_t u_shifted, f16x2 d2) {
+  const uint32_t v = (u_shifted & 0x00FF00FFu) | kMagic;
+  return (bitcast<f16x2>(v) - f16x2{1152.0f16, 1152.0f16}) * d2;
+}
+// Two 4-bit values at bits 0-3 and 16-19 -> (n - 8) * d.
+__device__ __forceinline__ f16x2 nib_pair_to_f16(uint32_t w_shifted, f16x2 d2) {
+  const uint32_t v = (w_shifted & 0x000F000Fu) | kMagic;
+  return (bitcast<f16x2>(v) - f16x2{1032.0f16, 1032.0f16}) * d2;
+}
+
+__device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ===========================================================================
+// K formats: the A operand of the score MFMA. Lane (m = lane%16, j = lane/16)
+// holds token row m of a 16-row group and, for MFMA step s, 8 head-dimension
+// values at positions dslot(j, s, 0..7).
+// ===========================================================================
+template <int KT, int D> struct KFmt;
+
+template <int D> struct KFmt<kF16, D> {
+  static constexpr int RB = 2 * D;
+  static constexpr int S = D / 32;
+  struct Raw { u32x4 c[S]; };
+  // chunk s of lane j = bytes [64s + 16j, +16): 64 contiguous bytes per row
+  // per instruction across the 4 lanes of a row.
+  __device__ static void load(Raw& r, const uint8_t* row, int j) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) r.c[s] = ld_u32x4(row + 64 * s + 16 * j);
+  }
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t) { return bitcast<f16x8>(r.c[s]); }
+  __host__ __device__ static int dslot(int j, int s, int i) { return 32 * s + 8 * j + i; }
+  __device__ static uint32_t shift(int) { return 0; }
+};
+
+// Quantised K: lane j owns the contiguous bytes [j*LB, (j+1)*LB) of the row,
+// i.e. whole ggml blocks (2 blocks at D=256, 1 at D=128).
+template <int KT, int D> struct KQuantBase {
+  static constexpr int RB = row_bytes_of(KT, D);
+  static constexpr int S = D / 32;
+  static constexpr int LB = RB / 4;
+  static constexpr bool kAligned = (LB % 4) == 0;        // every lane window 4-aligned
+  static constexpr int NW = kAligned ? LB / 4 : (LB + 2 + 3) / 4;
+  struct Raw { uint32_t w[NW]; };
+  __device__ static uint32_t shift(int j) { return uint32_t(j * LB) & 3u; }
+  __device__ static void load(Raw& r, const uint8_t* row, int j) {
+    const uint8_t* p = row + ((j * LB) & ~3);
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= NW; i += 4) {
+      const u32x4 v = ld_u32x4_a4(p + 4 * i);
+      r.w[i] = v[0]; r.w[i + 1] = v[1]; r.w[i + 2] = v[2]; r.w[i + 3] = v[3];
+    }
+#pragma unroll
+    for (; i < NW; ++i) r.w[i] = ld_u32(p + 4 * i);
+  }
+  // dword at lane byte c (c even, compile-time after unrolling), given the
+  // lane window's misalignment sh in {0, 2}.
+  __device__ static uint32_t dw(const Raw& r, int c, uint32_t sh) {
+    if (c % 4 == 0) {
+      const uint32_t a0 = r.w[c / 4];
+      if (kAligned) return a0;
+      return sh ? align_bytes(r.w[c / 4 + 1], r.w[c / 4], 2) : a0;
+    }
+    const uint32_t a0 = align_bytes(r.w[c / 4 + 1], r.w[c / 4], 2);
+    if (kAligned) return a0;
+    return sh ? r.w[c / 4 + 1] : a0;
+  }
+  // f16 at lane byte c (c even).
+  __device__ static f16 half_at(const Raw& r, int c, uint32_t sh) {
+    uint32_t w;
+    if (c % 4 == 0) {
+      w = (kAligned || !sh) ? r.w[c / 4] : (r.w[c / 4] >> 16);
+    } else {
+      w = (kAligned || !sh) ? (r.w[c / 4] >> 16) : r.w[c / 4 + 1];
+    }
+    return bitcast<f16>(uint16_t(w & 0xFFFFu));
+  }
+};
+
+template <int D> struct KFmt<kQ8_0, D> : KQuantBase<kQ8_0, D> {
+  using B = KQuantBase<kQ8_0, D>;
+  using typename B::Raw;
+  static constexpr int NBL = D / 128;   // ggml blocks per lane
+  // step s: block s/4 of the lane, quants 8*(s%4) .. +7, emitted in the order
+  // (0,2),(1,3),(4,6),(5,7) by the byte-pair conversion.
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh) {
+    const int blk = s / 4, base = 8 * (s % 4);
+    const f16x2 d2 = splat2(B::half_at(r, 34 * blk, sh));
+    const uint32_t u0 = B::dw(r, 34 * blk + 2 + base, sh) ^ 0x80808080u;
+    const uint32_t u1 = B::dw(r, 34 * blk + 2 + base + 4, sh) ^ 0x80808080u;
+    return pack8(i8pair_to_f16(u0, d2), i8pair_to_f16(u0 >> 8, d2),
+                 i8pair_to_f16(u1, d2), i8pair_to_f16(u1 >> 8, d2));
+  }
+  __host__ __device__ static int dslot(int j, int s, int i) {
+    const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    return 32 * (j * NBL + s / 4) + 8 * (s % 4) + order[i];
+  }
+};
+
+template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
+  using B = KQuantBase<kQ4_0, D>;
+  using typename B::Raw;
+  static constexpr int NBL = D / 128;
+  // step s: block s/4, nibble bytes 4c..4c+3 (c = s%4) -> elements
+  // 4c, 4c+2, 16+4c, 18+4c, 4c+1, 4c+3, 17+4c, 19+4c.
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh) {
+    const int blk = s / 4, c = s % 4;
+    const f16x2 d2 = splat2(B::half_at(r, 18 * blk, sh));
+    const uint32_t w = B::dw(r, 18 * blk + 2 + 4 * c, sh);
+    return pack8(nib_pair_to_f16(w, d2), nib_pair_to_f16(w >> 4, d2),
+                 nib_pair_to_f16(w >> 8, d2), nib_pair_to_f16(w >> 12, d2));
+  }
+  __host__ __device__ static int dslot(int j, int s, int i) {
+    const int c = s % 4;
+    const int order[8] = {0, 2, 16, 18, 1, 3, 17, 19};
+    return 32 * (j * NBL + s / 4) + 4 * c + order[i];
+  }
+};
+
+// ===========================================================================
+// V formats: the A operand of the PV MFMA is V^T. Lane (m, j) holds, for
+// d-tile e, head-dimension position dv(m, e) of the lane's 8 token rows
+// (rows 4j..4j+3 of group 0 and 16+4j..16+4j+3 of group 1).
+// ===========================================================================
+template <int VT, int D> struct VFmt;
+
+template <int D> struct VFmt<kF16, D> {
+  static constexpr int RB = 2 * D;
+  static constexpr int E = D / 16;       // d-tiles
+  static constexpr int NCH = D / 128;    // 16-byte chunks per row per lane
+  static constexpr bool kQuant = false;
+  struct Lane { int m; };
+  struct Raw { u32x4 c[NCH]; };
+  __device__ static Lane lane(int m) { return Lane{m}; }
+  // 16 lanes m read 256 contiguous bytes of a row per instruction.
+  __device__ static void load(Raw& r, const uint8_t* row, const Lane& L) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) r.c[c] = ld_u32x4(row + 16 * (L.m + 16 * c));
+  }
+  __device__ static void kill(Raw& r) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) r.c[c] = u32x4{0, 0, 0, 0};
+  }
+  __host__ __device__ static int dv(int m, int e) { return 8 * (m + 16 * (e / 8)) + e % 8; }
+  // Pack half k of chunk e/8 of rows (2p, 2p+1) into dword p.
+  __device__ static f16x8 op(const Raw* R, const f16x2*, int e) {
+    const int c = e / 8, k = e % 8;
+    const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = perm_bytes(R[2 * p + 1].c[c][k / 2], R[2 * p].c[c][k / 2], sel);
+    return bitcast<f16x8>(o);
+  }
+};
+
+// Quantised V: lane m covers EPL = D/16 head positions, all inside one ggml
+// block; the quant bytes are fetched through a dword window and realigned.
+template <int VT, int D> struct VQuantBase {
+  static constexpr int RB = row_bytes_of(VT, D);
+  static constexpr int E = D / 16;
+  static constexpr int EPL = D / 16;           // positions per lane
+  static constexpr bool kQuant = true;
+  static constexpr int BB = (VT == kQ8_0) ? 34 : 18;       // ggml block bytes
+  static constexpr int QB = (VT == kQ8_0) ? EPL : EPL / 2; // quant bytes per lane
+  static constexpr int ND = QB / 4;            // realigned quant dwords
+  static constexpr int NW = ND + 1;            // window dwords (covers a 2-byte skew)
+  struct Lane { uint32_t woff, sh, doff, last; int m; };
+  struct Raw { uint32_t w[NW]; f16 d; };
+  __device__ static Lane lane(int m) {
+    // quant bytes of lane m start at byte qoff of the row
+    const int per_blk = (VT == kQ8_0) ? 32 : 16;           // quant bytes per block
+    const int qidx = m * QB;
+    const int blk = qidx / per_blk, st = qidx % per_blk;
+    const uint32_t qoff = uint32_t(BB * blk + 2 + st);
+    Lane L;
+    L.woff = qoff & ~3u;
+    L.sh = qoff & 3u;
+    L.doff = uint32_t(BB * blk);
+    // the last window dword is only needed when sh != 0; keep its address in
+    // the row so the last row of the pool is never over-read
+    const uint32_t lastoff = L.woff + 4u * (NW - 1);
+    L.last = lastoff + 4u <= uint32_t(RB) ? lastoff : uint32_t(RB) - 4u;
+    L.m = m;
+    return L;
+  }
+  __device__ static void load(Raw& r, const uint8_t* row, const Lane& L) {
+#pragma unroll
+    for (int i = 0; i < NW - 1; ++i) r.w[i] = ld_u32(row + L.woff + 4 * i);
+    r.w[NW - 1] = ld_u32(row + L.last);
+    r.d = bitcast<f16>(ld_u16(row + L.doff));
+  }
+  __device__ static void kill(Raw& r) { r.d = f16(0); }
+  __device__ static void realign(const Raw& r, uint32_t sh, uint32_t* q) {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) q[i] = align_bytes(r.w[i + 1], r.w[i], sh);
+  }
+};
+
+template <int D> struct VFmt<kQ8_0, D> : VQuantBase<kQ8_0, D> {
+  using B = VQuantBase<kQ8_0, D>;
+  __host__ __device__ static int dv(int m, int e) { return m * B::EPL + e; }
+  // q: realigned quant dwords of the 8 rows [row][ND]; dd[p] = (d_2p, d_2p+1)
+  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e) {
+    const int k = e % 4, i = e / 4;
+    const uint32_t sel = uint32_t(k) | (0x0Cu << 8) | (uint32_t(4 + k) << 16) | (0x0Cu << 24);
+    f16x2 o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel) ^ 0x00800080u;
+      o[p] = (bitcast<f16x2>(x | kMagic) - f16x2{1152.0f16, 1152.0f16}) * dd[p];
+    }
+    return pack8(o[0], o[1], o[2], o[3]);
+  }
+};
+
+template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
+  using B = VQuantBase<kQ4_0, D>;
+  // e < QB: low nibble of quant byte e; e >= QB: high nibble of byte e-QB.
+  __host__ __device__ static int dv(int m, int e) {
+    const int qidx = m * B::QB;
+    const int blk = qidx / 16, st = qidx % 16;
+    return 32 * blk + (e < B::QB ? st + e : 16 + st + (e - B::QB));
+  }
+  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e) {
+    const bool hi = e >= B::QB;
+    const int byte = hi ? e - B::QB : e;
+    const int k = byte % 4, i = byte / 4;
+    const uint32_t sel = uint32_t(k) | (0x0Cu << 8) | (uint32_t(4 + k) << 16) | (0x0Cu << 24);
+    f16x2 o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel);
+      o[p] = nib_pair_to_f16(hi ? (x >> 4) : x, dd[p]);
+    }
+    return pack8(o[0], o[1], o[2], o[3]);
+  }
+};
+
+// ===========================================================================
+// The kernel
+// ===========================================================================
+template <int KT, int VT, int D>
+struct Tile {
+  using KF = KFmt<KT, D>;
+  using VF = VFmt<VT, D>;
+  typename KF::Raw k[2];
+  typename VF::Raw v[8];
+  int32_t bad;
+};
+
+struct Unit {
+  int b, g, p, t_begin, t_end;
+};
+
+template <int KT, int VT, int D>
+__global__ void __launch_bounds__(kThreads)
+decode_kernel(const DecodeArgs a) {
+  using KF = KFmt<KT, D>;
+  using VF = VFmt<VT, D>;
+  using T = Tile<KT, VT, D>;
+  constexpr int S = D / 32;      // score MFMA steps
+  constexpr int E = D / 16;      // PV d-tiles
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  // LDS: [units prefix: B+1 ints][seq_len clamped: B ints][flags: 4 ints]
+  //      [combine: 3 waves x (r*D acc + 2*16 (m,l)) floats]
+  int32_t* unit_start = reinterpret_cast<int32_t*>(smem);
+  int32_t* lens = unit_start + (a.B + 1);
+  int32_t* flags = lens + a.B;
+  const int pre_ints = ((2 * a.B + 1 + 4) + 3) & ~3;
+  float* comb = reinterpret_cast<float*>(smem) + pre_ints;
+  const int comb_stride = a.r * D + 32;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = lane & 15;
+  const int j = lane >> 4;
+
+  // ---- per-workgroup prefix of live partitions per sequence -------------
+  {
+    const int per = (a.B + kThreads - 1) / kThreads;
+    const int b0 = tid * per;
+    const int cap = a.cap_tokens;
+    int local = 0;
+    uint32_t st = 0;
+    for (int b = b0; b < b0 + per && b < a.B; ++b) {
+      int L = a.seq_len[b];
+      if (L < 0 || L > cap) { st |= 2u; L = L < 0 ? 0 : cap; }
+      lens[b] = L;
+      local += (L + a.psize - 1) / a.psize;
+    }
+    if (st && blockIdx.x == 0) atomicOr(a.status, st);
+    // block-wide exclusive scan of `local` (Hillis-Steele over LDS)
+    int* scan = reinterpret_cast<int*>(comb);    // kThreads ints, reused below
+    scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    int run = scan[tid] - local;
+    for (int b = b0; b < b0 + per && b < a.B; ++b) {
+      unit_start[b] = run;
+      run += (lens[b] + a.psize - 1) / a.psize;
+    }
+    if (tid == kThreads - 1) unit_start[a.B] = scan[tid];
+    __syncthreads();
+  }
+  const int n_bp = unit_start[a.B];
+  const int n_units = n_bp * a.Hkv;
+  const int G = gridDim.x;
+
+  // In direct mode no merge follows: an empty sequence's rows are zeroed here.
+  if (a.direct) {
+    for (int b = blockIdx.x; b < a.B; b += G) {
+      if (lens[b] != 0) continue;
+      float* o = a.out + int64_t(b) * a.Hq * D;
+      for (int i = tid; i < a.Hq * D; i += kThreads) o[i] = 0.0f;
+    }
+  }
+
+  // ---- XCD-aware order: consecutive logical units land on one XCD -------
+  const int xcd = blockIdx.x % 8, kk = blockIdx.x / 8;
+  const int cb = G / 8, rem = G % 8;
+  const int logical = xcd * cb + (xcd < rem ? xcd : rem) + kk;
+
+  const uint32_t kstride = uint32_t(a.Hkv) * KF::RB;   // bytes between token rows
+  const uint32_t vstride = uint32_t(a.Hkv) * VF::RB;
+  const uint32_t ksh = KF::shift(j);
+  const auto vl = VF::lane(m);
+
+  for (int u = logical; u < n_units; u += G) {
+    // ---- locate the unit ---------------------------------------------------
+    const int bp = u / a.Hkv;
+    Unit U;
+    U.g = u - bp * a.Hkv;
+    {
+      int lo = 0, hi = a.B - 1;            // largest b with unit_start[b] <= bp
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (unit_start[mid] <= bp) lo = mid; else hi = mid - 1;
+      }
+      U.b = lo;
+    }
+    U.p = bp - unit_start[U.b];
+    U.t_begin = U.p * a.psize;
+    U.t_end = min(lens[U.b], U.t_begin + a.psize);
+    const int ntiles = (U.t_end - U.t_begin + kTile - 1) / kTile;
+
+    // ---- Q operand: heads g*r .. g*r+r-1 in columns n = lane%16 ----------
+    f16x8 qop[S];
+    {
+      const int n = m;
+      const bool live = n < a.r;
+      const float* qrow = a.q + (int64_t(U.b) * a.Hq + U.g * a.r + (live ? n : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = live ? qrow[KF::dslot(j, s, i)] * a.qscale : 0.0f;
+          qop[s][i] = f16(x);
+        }
+      }
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
+
+    // ---- tile loader ------------------------------------------------------
+    auto load_tile = [&](T& t, int k) __attribute__((always_inline)) {
+      const int t0 = U.t_begin + k * kTile;
+      t.bad = 0;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int tg = t0 + 16 * gi;
+        const bool live = tg < U.t_end;
+        const int tq = live ? tg : U.t_end - 1;
+        const int jb = tq >> a.bs_shift;
+        int32_t id = block_of(a.table, U.b, a.max_blocks, jb);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { t.bad = 1; id = 0; }
+        const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
+        const uint8_t* kb = a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, KF::RB);
+        const uint8_t* vb = a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, VF::RB);
+        KF::load(t.k[gi], kb + m * kstride, j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) VF::load(t.v[4 * gi + i], vb + (4 * j + i) * vstride, vl);
+      }
+    };
+
+    // ---- tile compute: scores, online softmax (exp2), PV ------------------
+    auto compute_tile = [&](T& t, int k) __attribute__((always_inline)) {
+      const int t0 = U.t_begin + k * kTile;
+      bad |= t.bad;
+      const bool full = t0 + kTile <= U.t_end;
+      if (!full) {
+        // zero V rows past the end so 0 * junk never reaches the PV MFMA
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 16 * gi + 4 * j + i >= U.t_end) VF::kill(t.v[4 * gi + i]);
+      }
+      f32x4 sc[2];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) s4 = mfma(KF::op(t.k[gi], s, ksh), qop[s], s4);
+        sc[gi] = s4;
+      }
+      if (!full) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 16 * gi + 4 * j + i >= U.t_end) sc[gi][i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      // skip the accumulator rescale when no head's max moved (lucebox PR
+      // #555, Summary: skip-if-unchanged rescale)
+      if (__any(m_new != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= alpha;
+        m_run = m_new;
+      }
+      float p[8];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[4 * gi + i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_run);
+      float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run += ps;
+      f16x8 pop;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pop[i] = f16(p[i]);
+
+      if constexpr (VF::kQuant) {
+        uint32_t q[8][VF::ND];
+        f16x2 dd[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) VF::realign(t.v[i], vl.sh, q[i]);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) dd[pp] = f16x2{t.v[2 * pp].d, t.v[2 * pp + 1].d};
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op_q(q, dd, e), pop, acc[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op(t.v, nullptr, e), pop, acc[e]);
+      }
+    };
+
+    // ---- wave w streams tiles w, w+4, ... with one tile prefetched --------
+    int k = wave;
+    if (k < ntiles) {
+      T A, Bt;
+      load_tile(A, k);
+      while (true) {
+        if (k + kWaves < ntiles) load_tile(Bt, k + kWaves);
+        compute_tile(A, k);
+        k += kWaves;
+        if (k >= ntiles) break;
+        if (k + kWaves < ntiles) load_tile(A, k + kWaves);
+        compute_tile(Bt, k);
+        k += kWaves;
+        if (k >= ntiles) break;
+      }
+    }
+
+    // ---- combine the four waves through LDS -------------------------------
+    const int n = m;
+    if (wave > 0) {
+      float* cw = comb + (wave - 1) * comb_stride;
+      if (n < a.r) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cw[n * D + VF::dv(4 * j + i, e)] = acc[e][i];
+        if (j == 0) {
+          cw[a.r * D + n] = m_run;
+          cw[a.r * D + 16 + n] = l_run;
+        }
+      }
+      if (lane == 0) flags[wave] = bad;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int any_bad = bad | flags[1] | flags[2] | flags[3];
+      float M = m_run;
+      float mw[3], lw[3];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const float* cw = comb + w * comb_stride;
+        mw[w] = n < a.r ? cw[a.r * D + n] : -INFINITY;
+        lw[w] = n < a.r ? cw[a.r * D + 16 + n] : 0.0f;
+        M = fmaxf(M, mw[w]);
+      }
+      const float c0 = __builtin_amdgcn_exp2f(m_run - M);
+      float cwt[3];
+      float l = l_run * c0;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        cwt[w] = __builtin_amdgcn_exp2f(mw[w] - M);
+        l += lw[w] * cwt[w];
+      }
+      const float inv = 1.0f / l;
+      const int h = U.g * a.r + n;
+      if (any_bad && lane == 0) atomicOr(a.status, 1u);
+      if (n < a.r) {
+        float* dst;
+        if (a.direct) {
+          dst = a.out + (int64_t(U.b) * a.Hq + h) * D;
+        } else {
+          const int64_t row = (int64_t(U.b) * a.Hq + h) * a.p_max + U.p;
+          dst = a.part_o + row * D;
+          if (j == 0) {
+            a.part_ml[2 * row] = any_bad ? __builtin_nanf("") : M;
+            a.part_ml[2 * row + 1] = l;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = VF::dv(4 * j + i, e);
+            float v = acc[e][i] * c0;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) v += comb[w * comb_stride + n * D + d] * cwt[w];
+            dst[d] = any_bad ? __builtin_nanf("") : v * inv;
+          }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int KT, int VT, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int pre_ints = ((2 * a.B + 1 + 4) + 3) & ~3;
+  const int comb_floats = 3 * (a.r * D + 32);
+  const int scan_floats = kThreads;
+  const size_t lds = size_t(pre_ints + (comb_floats > scan_floats ? comb_floats : scan_floats)) * 4;
+  hipLaunchKernelGGL((decode_kernel<KT, VT, D>), dim3(a.grid), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  switch (a.k_type * 3 + a.v_type) {
+    case 0: return launch_typed<kF16, kF16, D>(a, s);
+    case 1: return launch_typed<kF16, kQ8_0, D>(a, s);
+    case 2: return launch_typed<kF16, kQ4_0, D>(a, s);
+    case 3: return launch_typed<kQ8_0, kF16, D>(a, s);
+    case 4: return launch_typed<kQ8_0, kQ8_0, D>(a, s);
+    case 5: return launch_typed<kQ8_0, kQ4_0, D>(a, s);
+    case 6: return launch_typed<kQ4_0, kF16, D>(a, s);
+    case 7: return launch_typed<kQ4_0, kQ8_0, D>(a, s);
+    case 8: return launch_typed<kQ4_0, kQ4_0, D>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.D == 256) return launch_d<256>(a, stream);
+  if (a.D == 128) return launch_d<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the decode and gather kernels: vector types,
+// the pool row address, and small bit-manipulation wrappers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte vector whose address is only guaranteed 4-byte aligned (ggml block
+// rows are 2- or 4-byte aligned inside a row).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+enum : int { kF16 = 0, kQ8_0 = 1, kQ4_0 = 2 };
+
+__host__ __device__ constexpr int row_bytes_of(int type, int D) {
+  return type == kF16 ? 2 * D : (type == kQ8_0 ? 34 * (D / 32) : 18 * (D / 32));
+}
+
+// Physical block of logical block j of sequence b; a null table is the
+// contiguous layout (sequence b's block j is block b*max_blocks + j).
+__device__ __forceinline__ int32_t block_of(const int32_t* __restrict__ table, int32_t b,
+                                            int32_t max_blocks, int32_t j) {
+  const int64_t idx = int64_t(b) * max_blocks + j;
+  return table ? table[idx] : int32_t(idx);
+}
+
+// Byte offset of the first row of block `id`, slot `slot`, kv head `g` in a
+// [nblocks, block_size, Hkv, row_bytes] pool:
+//   ((id*block_size + slot)*Hkv + g) * row_bytes
+// computed in 64 bits, widened before the first multiply (mlxcel issue #2153,
+// Proposed Solution and Implementation Notes).
+__device__ __forceinline__ uint64_t row_offset(int32_t id, int32_t slot, int32_t bs_shift,
+                                               int32_t Hkv, int32_t g, int32_t row_bytes) {
+  const uint64_t row = (uint64_t(uint32_t(id)) << bs_shift) + uint32_t(slot);
+  return (row * uint32_t(Hkv) + uint32_t(g)) * uint64_t(uint32_t(row_bytes));
+}
+
+__device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+__device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld_u32x4_a4(const uint8_t* p) {
+  u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p);
+  return u32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint16_t ld_u16(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// Bytes [sh, sh+4) of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t sh) {
+  return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+// v_perm_b32: byte selectors 0-3 pick bytes of `lo`, 4-7 bytes of `hi`, 12 gives 0x00.
+__device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <typename T, typename F>
+__device__ __forceinline__ T bitcast(F x) {
+  return __builtin_bit_cast(T, x);
+}
+
+}  // namespace pa

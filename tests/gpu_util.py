@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare with the fp64 oracle on the same seeded bytes."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+TOL = {"f16": 2e-3, "q8_0": 5e-3, "q4_0": 5e-3}
+
+
+def tol_for(case):
+    return max(TOL[case.k_fmt], TOL[case.v_fmt])
+
+
+def pa_mod():
+    import paged_kv_gqa_attn_amd as pa
+    return pa
+
+
+def shape_for(case):
+    pa = pa_mod()
+    return pa.shape_of(case.B, case.Hq, case.Hkv, case.D, case.block_size, case.nblocks,
+                       case.max_blocks, case.k_fmt, case.v_fmt)
+
+
+def plan_for(case, **kw):
+    pa = pa_mod()
+    kw.setdefault("total_tokens", sum(case.seq_lens))
+    return pa.paged_attn_plan(shape_for(case), max(max(case.seq_lens), 0), **kw)
+
+
+def run(case_dev, plan, table="case", ws=None, canary=0):
+    """One decode step (decode + merge) on the GPU. Returns (out, ws)."""
+    pa = pa_mod()
+    dev = case_dev.q.device
+    if ws is None:
+        ws = pa.workspace(plan, dev, extra=canary)
+        if canary:
+            ws[int(plan.ws_bytes):] = 0xA5
+    out = torch.full((case_dev.B, case_dev.Hq, case_dev.D), float("nan"), dtype=torch.float32,
+                     device=dev)
+    tab = case_dev.table if table == "case" else table
+    pa.paged_attn_step(plan, case_dev.q, case_dev.k_pool, case_dev.v_pool, tab, case_dev.seq_len,
+                       ws, out)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def rel_err_rows(got, ref):
+    """Per-row max_d |got-ref| / max_d |ref| (zero rows compared absolutely)."""
+    got = np.asarray(got, dtype=np.float64)
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    return num / den
+
+
+def check_parity(case, out, heads=None):
+    """Compare out [B,Hq,D] with the oracle (all rows, or selected (b,g) groups)."""
+    got = out.detach().cpu().double().numpy()
+    tol = tol_for(case)
+    if heads is None:
+        ref = oracle.decode_case(case)
+        err = rel_err_rows(got, ref)
+        assert np.isfinite(got).all(), "non-finite output"
+        worst = float(err.max())
+        assert worst <= tol, f"max row error {worst:.3e} > {tol}"
+        return worst
+    res = oracle.decode_case(case, heads=heads)
+    r = case.Hq // case.Hkv
+    worst = 0.0
+    for (b, g), ref in res.items():
+        gg = got[b, g * r:(g + 1) * r]
+        assert np.isfinite(gg).all(), f"non-finite output at b={b} g={g}"
+        e = float(rel_err_rows(gg, ref).max())
+        worst = max(worst, e)
+        assert e <= tol, f"b={b} g={g}: max row error {e:.3e} > {tol}"
+    return worst

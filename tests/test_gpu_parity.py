@@ -1,0 +1,209 @@
+"""GPU parity of the HIP decode path against the fp64 oracle, through the C ABI.
+
+Tolerance (on the per-row max-abs error relative to the row's max-abs
+output): 2e-3 when K and V are F16, 5e-3 when either is quantised. Indexing
+(the raw gather) is compared bit for bit; paged and contiguous layouts, and
+repeated runs, must agree bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_parity, plan_for, run, shape_for, pa_mod, rel_err_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+PAIRS = [(k, v) for k in synth.FORMATS for v in synth.FORMATS]
+
+
+def _case(lens, **kw):
+    kw.setdefault("junk", "nan")
+    return synth.make_case(lens, **kw)
+
+
+def test_tiny_f16_workload_all_partitionings():
+    case = synth.workload("tiny_f16", seed=1000)
+    g = case.to(DEV)
+    for force in (0, 1, 2, 3, 7):
+        plan = plan_for(case, force_partitions=force)
+        out, ws = run(g, plan)
+        check_parity(case, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
+def test_nine_type_pairs(pair, D):
+    k_fmt, v_fmt = pair
+    Hq, Hkv = (24, 4) if D == 256 else (32, 8)
+    lens = [200, 1, 16, 17, 33, 0, 95]
+    case = _case(lens, Hq=Hq, Hkv=Hkv, D=D, block_size=16, k_fmt=k_fmt, v_fmt=v_fmt,
+                 seed=7 + D + 3 * synth.FORMATS.index(k_fmt) + synth.FORMATS.index(v_fmt))
+    g = case.to(DEV)
+    for force in (1, 3):
+        out, _ = run(g, plan_for(case, force_partitions=force))
+        check_parity(case, out)
+        assert np.all(out[5].cpu().numpy() == 0.0), "empty sequence must give a zero row"
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 31, 32, 33, 64, 65, 200, 511, 1000])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_block_boundaries(L, bs):
+    case = _case([L, L + 1], block_size=bs, k_fmt="q4_0", v_fmt="q8_0", seed=L * 3 + bs)
+    g = case.to(DEV)
+    for force in (0, 1, 2):
+        out, _ = run(g, plan_for(case, force_partitions=force))
+        check_parity(case, out)
+
+
+def test_gather_bit_exact_paged_and_contiguous():
+    pa = pa_mod()
+    for k_fmt, v_fmt in [("f16", "q4_0"), ("q8_0", "f16")]:
+        case = _case([70, 33, 130], k_fmt=k_fmt, v_fmt=v_fmt, seed=5)
+        g = case.to(DEV)
+        plan = plan_for(case)
+        for which, fmt, pool in ((0, k_fmt, case.k_pool), (1, v_fmt, case.v_pool)):
+            rb = synth.row_bytes(fmt, case.D)
+            flat = pool.reshape(-1, case.Hkv, rb)
+            for b, L in enumerate(case.seq_lens):
+                dst = torch.zeros((L, case.Hkv, rb), dtype=torch.uint8, device=DEV)
+                pa.paged_kv_gather(plan, g.k_pool if which == 0 else g.v_pool, which, g.table, b, 0,
+                                   L, dst)
+                torch.cuda.synchronize()
+                t = torch.arange(L)
+                rows = case.table[b, t // case.block_size].long() * case.block_size + t % case.block_size
+                assert torch.equal(dst.cpu(), flat[rows])
+        # contiguous layout (null table)
+        cc = synth.contiguous_copy(case)
+        gc = cc.to(DEV)
+        plan_c = plan_for(cc)
+        rb = synth.row_bytes(k_fmt, case.D)
+        for b, L in enumerate(case.seq_lens):
+            dst = torch.zeros((L, case.Hkv, rb), dtype=torch.uint8, device=DEV)
+            pa.paged_kv_gather(plan_c, gc.k_pool, 0, None, b, 0, L, dst)
+            torch.cuda.synchronize()
+            flat = cc.k_pool.reshape(-1, case.Hkv, rb)
+            t = torch.arange(L)
+            rows = (b * cc.max_blocks + t // case.block_size) * case.block_size + t % case.block_size
+            assert torch.equal(dst.cpu(), flat[rows])
+
+
+@pytest.mark.parametrize("pair", [("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "q4_0")])
+def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
+    case = _case([700, 333, 1, 64], k_fmt=pair[0], v_fmt=pair[1], seed=11)
+    cc = synth.contiguous_copy(case)
+    g, gc = case.to(DEV), cc.to(DEV)
+    for force in (0, 1, 3):
+        plan = plan_for(case, force_partitions=force)
+        out_p, _ = run(g, plan)
+        out_p2, _ = run(g, plan)
+        plan_c = plan_for(cc, force_partitions=force)
+        assert plan_c.psize == plan.psize
+        out_c, _ = run(gc, plan_c, table=None)
+        assert torch.equal(out_p, out_p2), "repeated runs differ"
+        assert torch.equal(out_p, out_c), "paged and contiguous runs differ"
+        check_parity(case, out_p)
+
+
+def test_bad_block_id_sets_status_and_nans_only_that_sequence():
+    pa = pa_mod()
+    case = _case([100, 64, 40], k_fmt="f16", v_fmt="q4_0", seed=13)
+    g = case.to(DEV)
+    for force in (1, 0, 3):
+        plan = plan_for(case, force_partitions=force)
+        for badid in (-1, case.nblocks, 2**31 - 1):
+            tab = g.table.clone()
+            tab[1, 2] = badid
+            out, ws = run(g, plan, table=tab)
+            assert pa.paged_attn_status(ws) & pa.PA_STATUS_BAD_BLOCK_ID
+            o = out.cpu().numpy()
+            assert np.isnan(o[1]).all(), "rows of the corrupt sequence must be NaN"
+            ref = oracle.decode_case(case)
+            for b in (0, 2):
+                assert float(rel_err_rows(o[b], ref[b]).max()) <= tol_for(case)
+            assert pa.paged_attn_status(ws) == 0, "status must clear after reading"
+
+
+def test_seq_len_beyond_capacity_is_clamped_and_flagged():
+    pa = pa_mod()
+    case = _case([64, 40], k_fmt="q8_0", v_fmt="q8_0", seed=17, max_blocks=4)
+    g = case.to(DEV)
+    plan = plan_for(case, force_partitions=1)
+    sl = g.seq_len.clone()
+    sl[0] = 10_000          # beyond max_blocks*block_size = 64
+    out, ws = pa_run_with_seq_len(g, plan, sl)
+    assert pa.paged_attn_status(ws) & pa.PA_STATUS_BAD_SEQ_LEN
+    check_parity(case, out)   # clamped to 64 = the case's own length
+
+
+def pa_run_with_seq_len(g, plan, sl):
+    pa = pa_mod()
+    ws = pa.workspace(plan, DEV)
+    out = torch.full((g.B, g.Hq, g.D), float("nan"), device=DEV)
+    pa.paged_attn_step(plan, g.q, g.k_pool, g.v_pool, g.table, sl, ws, out)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+@pytest.mark.parametrize("junk", ["nan", "big", "random"])
+def test_junk_in_dead_slots_never_leaks(junk):
+    case = _case([33, 17, 1, 250], k_fmt="q4_0", v_fmt="f16", seed=19, junk=junk)
+    g = case.to(DEV)
+    for force in (0, 1, 2):
+        out, _ = run(g, plan_for(case, force_partitions=force))
+        check_parity(case, out)
+
+
+def test_merge_kernel_on_oracle_partials():
+    """Write the oracle's own partials into the documented workspace layout and
+    check the GPU merge against the oracle merge."""
+    pa = pa_mod()
+    case = _case([300, 0, 97, 31], k_fmt="f16", v_fmt="q8_0", seed=23, Hq=8, Hkv=2)
+    plan = plan_for(case, partition_tokens=64)
+    kp, vp = case.k_pool.numpy().reshape(-1), case.v_pool.numpy().reshape(-1)
+    m, l, o, n = oracle.partials(case.q, kp, vp, case.table, case.seq_len, Hkv=case.Hkv, D=case.D,
+                                 block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
+                                 nblocks=case.nblocks, max_blocks=case.max_blocks,
+                                 psize=plan.psize, scale=case.scale)
+    B, Hq, P, D = o.shape
+    assert P == plan.p_max
+    ws = pa.workspace(plan, "cpu")
+    body = ws[256:256 + B * Hq * P * (D + 2) * 4].view(torch.float32)
+    body[: B * Hq * P * D] = torch.from_numpy(o.reshape(-1)).float()
+    ml = np.stack([m, l], axis=-1).reshape(-1)
+    body[B * Hq * P * D:] = torch.from_numpy(ml).float()
+    wsd = ws.to(DEV)
+    out = torch.full((B, Hq, D), float("nan"), device=DEV)
+    pa.paged_attn_merge(plan, wsd, case.seq_len.to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.merge(m, l, o, n)
+    err = rel_err_rows(out.cpu().double().numpy(), ref)
+    assert float(err.max()) <= 1e-5
+    assert np.all(out[1].cpu().numpy() == 0.0)
+
+
+def test_workspace_canary_untouched():
+    case = _case([1000, 517, 3], k_fmt="q4_0", v_fmt="q4_0", seed=29)
+    g = case.to(DEV)
+    for force in (0, 1, 5):
+        plan = plan_for(case, force_partitions=force)
+        out, ws = run(g, plan, canary=4096)
+        tail = ws[int(plan.ws_bytes):].cpu()
+        assert torch.all(tail == 0xA5), "decode or merge wrote past plan.ws_bytes"
+        check_parity(case, out)
+
+
+def test_red_control_wrong_table_fails_parity():
+    """A table whose first entry names a later block of the sequence must make
+    the GPU result disagree with the oracle on the true table (TensorFold PR
+    #1418, Kernel contract: the red control)."""
+    case = _case([128], k_fmt="f16", v_fmt="f16", seed=31)
+    g = case.to(DEV)
+    tab = g.table.clone()
+    tab[0, 0] = tab[0, 3]
+    out, _ = run(g, plan_for(case, force_partitions=1), table=tab)
+    ref = oracle.decode_case(case)
+    assert float(rel_err_rows(out.cpu().double().numpy(), ref).max()) > 1e-2
