@@ -1,0 +1,374 @@
+#!/usr/bin/env python
+"""Benchmark of one paged GQA decode step on one MI355X.
+
+A step is paged_attn_decode + paged_attn_merge for a whole batch of one layer
+on seeded synthetic inputs already resident in HBM. The default workload is
+the long-context batch the target is stated for: B=8 sequences of 131072
+tokens, D=256, Hq=24, Hkv=4, 16-token blocks, Q4_0 K and V, blocks shuffled
+through one pool (the lucebox PR #555 page's uniform-batch benchmark at its
+128K column). Other workloads: --workload NAME (see WORKLOADS).
+
+To keep the 256 MB MALL from serving a step out of cache, the timed loop
+rotates over enough independent pool copies that each copy is at least 4x
+the MALL between two uses.
+
+Prints ONE JSON line: metric/value (achieved algorithmic HBM GB/s of the
+whole step), ms_per_step, a roofline object for the decode kernel (achieved
+GB/s against 8 TB/s from hipEvents on the launch stream) and a cpu_baseline
+object (the fp64 oracle timed on a bounded sample on the host cores).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --summarize-stats DIR --label NAME   (rocprofv3 --stats CSV -> profiles/)
+  python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, public figure
+MALL_BYTES = 256 << 20
+METRIC = "paged decode step µs + achieved HBM GB/s (% of peak), D=256 Hq=24 Hkv=4"
+
+# name -> (synth workload, B, L, description)
+WORKLOADS = {
+    "uniform_q4_0_128k_b8": ("uniform_q4_0", 8, 131072, "uniform Q4_0 B=8 L=131072"),
+    "uniform_q4_0_32k_b8": ("uniform_q4_0", 8, 32768, "uniform Q4_0 B=8 L=32768"),
+    "uniform_q8_0_4k_b8": ("uniform_q8_0", 8, 4096, "uniform Q8_0 B=8 L=4096"),
+    "ragged_q4_0": ("ragged_q4_0", 8, 131072, "ragged Q4_0 131072+7x8192"),
+    "ragged_small_q4_0": ("ragged_small_q4_0", 8, 4096, "ragged Q4_0 4096+7x256"),
+    "tiny_f16": ("tiny_f16", 1, 200, "tiny F16 B=1 L=200"),
+    "slab_f16": ("slab_f16", 8, 65536, "F16 D=128 Hq=32 Hkv=8 bs=32 B=8 L=65536, pool past 2^32 elements"),
+}
+DEFAULT = "uniform_q4_0_128k_b8"
+DECODE_SRC = os.path.join(ROOT, "paged_kv_gqa_attn_amd", "csrc", "decode.hip")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "pa_device.h", "pa_host.h"):
+        with open(os.path.join(ROOT, "paged_kv_gqa_attn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case, plan):
+    """HBM bytes one step must move: live K/V rows, table entries, seq_len, q,
+    partials (written by decode, read by merge) and out. Returns
+    (decode_bytes, merge_bytes)."""
+    import synth
+    rbk = synth.row_bytes(case.k_fmt, case.D)
+    rbv = synth.row_bytes(case.v_fmt, case.D)
+    kv = sum(case.seq_lens) * case.Hkv * (rbk + rbv)
+    table = sum(-(-L // case.block_size) for L in case.seq_lens) * 4
+    q = 4 * case.B * case.Hq * case.D
+    out = 4 * case.B * case.Hq * case.D
+    seq = 4 * case.B
+    if plan.direct:
+        return kv + table + seq + q + out, 0
+    parts = sum(-(-L // plan.psize) for L in case.seq_lens) * case.Hq * (case.D + 2) * 4
+    return kv + table + seq + q + parts, parts + seq + out
+
+
+def build_cases(name, seed, device, min_bytes):
+    import synth
+    wl, B, L, _ = WORKLOADS[name]
+    first = synth.workload(wl, B=B, L=L, seed=seed, device=device, junk="zero")
+    live = first.k_pool.numel() + first.v_pool.numel()
+    copies = max(1, math.ceil(min_bytes / max(1, live)))
+    if name == "slab_f16":
+        copies = 1            # 18 GB of pools; its live rows (2.1 GB) already dwarf the MALL
+    cases = [first] + [synth.workload(wl, B=B, L=L, seed=seed + 17 * i, device=device, junk="zero")
+                       for i in range(1, copies)]
+    return cases
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the workload (whole (b, g)
+    groups, in order, until about budget_s of CPU work)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    import synth
+    kp = case.k_pool.cpu().numpy().reshape(-1)
+    vp = case.v_pool.cpu().numpy().reshape(-1)
+    tab = case.table.cpu()
+    sl = case.seq_len.cpu()
+    q = case.q.cpu()
+    rbk, rbv = synth.row_bytes(case.k_fmt, case.D), synth.row_bytes(case.v_fmt, case.D)
+    kw = dict(Hkv=case.Hkv, D=case.D, block_size=case.block_size, k_fmt=case.k_fmt,
+              v_fmt=case.v_fmt, nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
+    items = [(b, g) for b in range(case.B) for g in range(case.Hkv) if case.seq_lens[b] > 0]
+    done, nbytes, t0 = [], 0, time.perf_counter()
+    cpu0 = time.process_time()
+    for it in items:
+        oracle.decode_heads(q, kp, vp, tab, sl, items=[it], **kw)
+        done.append(it)
+        nbytes += case.seq_lens[it[0]] * (rbk + rbv)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    wall = time.perf_counter() - t0
+    eff = (time.process_time() - cpu0) / max(wall, 1e-9)
+    toks = sum(case.seq_lens[b] for b, _ in done)
+    return {
+        "value": round(nbytes / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle over {len(done)} of {len(items)} (sequence, kv-head) groups "
+                   f"({toks} token rows, {nbytes} K/V bytes) in {wall:.1f} s; "
+                   f"BLAS threads {threads}, mean busy cores {eff:.1f}"),
+    }
+
+
+def traffic_from_profiles(label):
+    """Counter-measured HBM bytes per decode dispatch, if a summary for this
+    workload exists and was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{label}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def run_bench(args):
+    import torch
+    import paged_kv_gqa_attn_amd as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    cases = build_cases(name, args.seed, dev, 4 * MALL_BYTES)
+    c0 = cases[0]
+    shape = pa.shape_of(c0.B, c0.Hq, c0.Hkv, c0.D, c0.block_size, c0.nblocks, c0.max_blocks,
+                        c0.k_fmt, c0.v_fmt)
+    plan = pa.paged_attn_plan(shape, max(c0.seq_lens), total_tokens=sum(c0.seq_lens),
+                              force_partitions=args.force_partitions)
+    ws = pa.workspace(plan, dev)
+    out = torch.empty((c0.B, c0.Hq, c0.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(c, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        pa.paged_attn_decode(plan, c.q, c.k_pool, c.v_pool, c.table, c.seq_len, ws, out, stream=sptr)
+        if evs is not None:
+            evs[1].record(stream)
+        pa.paged_attn_merge(plan, ws, c.seq_len, out, stream=sptr)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(cases[i % len(cases)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(cases[i % len(cases)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mrg_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    if pa.paged_attn_status(ws) != 0:
+        raise SystemExit("bench: device status word set (bad table or seq_len)")
+
+    dec_bytes, mrg_bytes = algorithmic_bytes(c0, plan)
+    ms_per_step = wall * 1e3 / args.steps
+    value = (dec_bytes + mrg_bytes) / (ms_per_step * 1e-3) / 1e9
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
+    med = sorted(step_ms)[len(step_ms) // 2]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[name][3],
+            "name": name,
+            "B": c0.B, "Hq": c0.Hq, "Hkv": c0.Hkv, "D": c0.D, "block_size": c0.block_size,
+            "k_type": c0.k_fmt, "v_type": c0.v_fmt, "seq_lens": sorted(set(c0.seq_lens)),
+            "live_tokens": sum(c0.seq_lens), "psize": plan.psize, "p_max": plan.p_max,
+            "grid": plan.grid, "pool_copies": len(cases),
+            "step_us_median_events": round(med * 1e3, 2),
+            "decode_us_mean": round(dec_avg * 1e3, 2),
+            "merge_us_mean": round(sum(mrg_ms) / len(mrg_ms) * 1e3, 2),
+            "step_pct_of_peak": round(100 * value / PEAK_GBS, 2),
+            "algorithmic_bytes_per_step": dec_bytes + mrg_bytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(name),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c0, budget_s=args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (text under profiles/)
+# ---------------------------------------------------------------------------
+
+def _csvs(d, suffix):
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize_stats(d, label, cmd):
+    rows = []
+    for path in _csvs(d, "kernel_stats.csv"):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    lines = [f"# rocprofv3 kernel statistics: {label}", f"# command: {cmd}",
+             f"# source_hash = {source_hash()}",
+             "# name | calls | total_ns | average_ns | min_ns | max_ns | percent"]
+    for r in rows:
+        nm = r.get("Name", r.get("KernelName", "?"))
+        lines.append(" | ".join([nm[:110], r.get("Calls", ""), r.get("TotalDurationNs", ""),
+                                 r.get("AverageNs", ""), r.get("MinNs", ""), r.get("MaxNs", ""),
+                                 r.get("Percentage", "")]))
+    out = os.path.join(ROOT, "profiles", f"decode_{label}_stats.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def summarize_pmc(d, label, cmd, calib_bytes):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernel, scaled
+    by what the same counters read for the calibration copy of calib_bytes."""
+    per = {}
+    for path in _csvs(d, "counter_collection.csv"):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                nm = r.get("Kernel_Name", "")
+                cn = r.get("Counter_Name", "")
+                val = float(r.get("Counter_Value", "0") or 0)
+                did = r.get("Dispatch_Id", "")
+                per.setdefault((nm, did), {}).setdefault(cn, 0.0)
+                per[(nm, did)][cn] += val
+    if not per:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    dec = [v for (nm, _), v in per.items() if "decode_kernel" in nm]
+    cpy = [v for (nm, _), v in per.items() if "decode_kernel" not in nm and "merge" not in nm
+           and "gather" not in nm]
+    lines = [f"# rocprofv3 counters: {label}", f"# command: {cmd}", f"source_hash = {source_hash()}"]
+    result = {}
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        dv = [v[cn] for v in dec if cn in v]
+        cv = [v[cn] for v in cpy if cn in v]
+        if not dv:
+            continue
+        dec_kib = sum(dv) / len(dv)
+        lines.append(f"decode_{cn}_KiB_per_dispatch = {dec_kib:.1f}")
+        if cv:
+            big = max(cv)
+            factor = calib_bytes / (big * 1024.0)
+            lines.append(f"calib_copy_{cn}_KiB = {big:.1f}  (copy of {calib_bytes} bytes)")
+            lines.append(f"calib_factor_{cn} = {factor:.4f}")
+            result[cn] = dec_kib * 1024.0 * factor
+        else:
+            result[cn] = dec_kib * 1024.0
+    if result:
+        tot = sum(result.values())
+        lines.append(f"traffic_bytes_per_dispatch = {tot:.0f}")
+    out = os.path.join(ROOT, "profiles", f"decode_{label}_pmc.txt")
+    prev = []
+    if os.path.exists(out):
+        with open(out) as f:
+            prev = [l.rstrip("\n") for l in f if l.startswith("decode_") or l.startswith("calib")]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def pmc_pass(args):
+    """Counter pass: a calibration copy of known size, then a few decode steps."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = args.calib_bytes
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    args.no_cpu_baseline = True
+    run_bench(args)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=1000)
+    ap.add_argument("--force-partitions", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--label", default=DEFAULT)
+    ap.add_argument("--cmd", default="")
+    args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.label, args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.label, args.cmd, args.calib_bytes)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the decode step is measured at its one-GPU shape", file=sys.stderr)
+        sys.exit(2)
+    if args.pmc_pass:
+        pmc_pass(args)
+        return
+    run_bench(args)
+
+
+if __name__ == "__main__":
+    main()

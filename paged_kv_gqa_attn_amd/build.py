@@ -17,7 +17,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 SOURCES = ["api.cpp", "kv_pool.cpp", "decode.hip", "merge.hip", "gather.hip"]
 # Packed fp32 VALU ops are kept off: the compiler must not form them.
-COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-slp-vectorize",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
 

@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;       // tokens per tile = two 16-row MFMA groups
 constexpr uint32_t kMagic = 0x64006400u;   // f16 1024.0 in both halves
+constexpr float kSlack = 8.0f;             // lazy-rescale slack (log2 units)
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -51,17 +52,19 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f16x2 splat2(f16 x) { return f16x2{x, x}; }
 
 // ---------------------------------------------------------------------------
-// Signed int8 pair -> f16: bytes b0,b2 of `q` (or b1,b3 after >>8) as exact
-// f16 integers, then one rounding when multiplied by the block scale.
-// (x ^ 0x80) placed under exponent 0x64 is 1024 + x + 128.
+// Integer -> f16 conversion: a byte or nibble placed under the f16 exponent
+// of 1024 (0x64xx) reads as 1024 + x exactly; subtracting the offset is exact,
+// so the only rounding is the multiplication by the block scale d.
+// `mg` is 0x64006400 held in a VGPR (see and_or).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f16x2 i8pair_to_f16(uint32_t u_shifted, f16x2 d2) {
-  const uint32_t v = (u_shifted & 0x00FF00FFu) | kMagic;
+// Signed int8 bytes 0 and 2 of `u` (already XORed with 0x80) -> d * q.
+__device__ __forceinline__ f16x2 i8pair_to_f16(uint32_t u_shifted, f16x2 d2, uint32_t mg) {
+  const uint32_t v = and_or(u_shifted, 0x00FF00FFu, mg);
   return (bitcast<f16x2>(v) - f16x2{1152.0f16, 1152.0f16}) * d2;
 }
-// Two 4-bit values at bits 0-3 and 16-19 -> (n - 8) * d.
-__device__ __forceinline__ f16x2 nib_pair_to_f16(uint32_t w_shifted, f16x2 d2) {
-  const uint32_t v = (w_shifted & 0x000F000Fu) | kMagic;
+// Nibbles at bits 0-3 and 16-19 -> (n - 8) * d.
+__device__ __forceinline__ f16x2 nib_pair_to_f16(uint32_t w_shifted, f16x2 d2, uint32_t mg) {
+  const uint32_t v = and_or(w_shifted, 0x000F000Fu, mg);
   return (bitcast<f16x2>(v) - f16x2{1032.0f16, 1032.0f16}) * d2;
 }
 
@@ -72,7 +75,8 @@ __device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // ===========================================================================
 // K formats: the A operand of the score MFMA. Lane (m = lane%16, j = lane/16)
 // holds token row m of a 16-row group and, for MFMA step s, 8 head-dimension
-// values at positions dslot(j, s, 0..7).
+// values at positions dslot(j, s, 0..7). Loads go through a buffer resource
+// whose base is the group's first row; `voff` is the lane's fixed offset.
 // ===========================================================================
 template <int KT, int D> struct KFmt;
 
@@ -82,11 +86,12 @@ template <int D> struct KFmt<kF16, D> {
   struct Raw { u32x4 c[S]; };
   // chunk s of lane j = bytes [64s + 16j, +16): 64 contiguous bytes per row
   // per instruction across the 4 lanes of a row.
-  __device__ static void load(Raw& r, const uint8_t* row, int j) {
+  __device__ static uint32_t lane_off(int j) { return 16u * j; }
+  __device__ static void load(Raw& r, rsrc_t R, uint32_t voff) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) r.c[s] = ld_u32x4(row + 64 * s + 16 * j);
+    for (int s = 0; s < S; ++s) r.c[s] = buf_u32x4(R, voff + 64 * s, 0);
   }
-  __device__ static f16x8 op(const Raw& r, int s, uint32_t) { return bitcast<f16x8>(r.c[s]); }
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t, uint32_t) { return bitcast<f16x8>(r.c[s]); }
   __host__ __device__ static int dslot(int j, int s, int i) { return 32 * s + 8 * j + i; }
   __device__ static uint32_t shift(int) { return 0; }
 };
@@ -101,16 +106,16 @@ template <int KT, int D> struct KQuantBase {
   static constexpr int NW = kAligned ? LB / 4 : (LB + 2 + 3) / 4;
   struct Raw { uint32_t w[NW]; };
   __device__ static uint32_t shift(int j) { return uint32_t(j * LB) & 3u; }
-  __device__ static void load(Raw& r, const uint8_t* row, int j) {
-    const uint8_t* p = row + ((j * LB) & ~3);
+  __device__ static uint32_t lane_off(int j) { return uint32_t(j * LB) & ~3u; }
+  __device__ static void load(Raw& r, rsrc_t R, uint32_t voff) {
     int i = 0;
 #pragma unroll
     for (; i + 4 <= NW; i += 4) {
-      const u32x4 v = ld_u32x4_a4(p + 4 * i);
+      const u32x4 v = buf_u32x4(R, voff + 4 * i, 0);
       r.w[i] = v[0]; r.w[i + 1] = v[1]; r.w[i + 2] = v[2]; r.w[i + 3] = v[3];
     }
 #pragma unroll
-    for (; i < NW; ++i) r.w[i] = ld_u32(p + 4 * i);
+    for (; i < NW; ++i) r.w[i] = buf_u32(R, voff + 4 * i, 0);
   }
   // dword at lane byte c (c even, compile-time after unrolling), given the
   // lane window's misalignment sh in {0, 2}.
@@ -142,13 +147,13 @@ template <int D> struct KFmt<kQ8_0, D> : KQuantBase<kQ8_0, D> {
   static constexpr int NBL = D / 128;   // ggml blocks per lane
   // step s: block s/4 of the lane, quants 8*(s%4) .. +7, emitted in the order
   // (0,2),(1,3),(4,6),(5,7) by the byte-pair conversion.
-  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh) {
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh, uint32_t mg) {
     const int blk = s / 4, base = 8 * (s % 4);
     const f16x2 d2 = splat2(B::half_at(r, 34 * blk, sh));
     const uint32_t u0 = B::dw(r, 34 * blk + 2 + base, sh) ^ 0x80808080u;
     const uint32_t u1 = B::dw(r, 34 * blk + 2 + base + 4, sh) ^ 0x80808080u;
-    return pack8(i8pair_to_f16(u0, d2), i8pair_to_f16(u0 >> 8, d2),
-                 i8pair_to_f16(u1, d2), i8pair_to_f16(u1 >> 8, d2));
+    return pack8(i8pair_to_f16(u0, d2, mg), i8pair_to_f16(u0 >> 8, d2, mg),
+                 i8pair_to_f16(u1, d2, mg), i8pair_to_f16(u1 >> 8, d2, mg));
   }
   __host__ __device__ static int dslot(int j, int s, int i) {
     const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
@@ -162,12 +167,12 @@ template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
   static constexpr int NBL = D / 128;
   // step s: block s/4, nibble bytes 4c..4c+3 (c = s%4) -> elements
   // 4c, 4c+2, 16+4c, 18+4c, 4c+1, 4c+3, 17+4c, 19+4c.
-  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh) {
+  __device__ static f16x8 op(const Raw& r, int s, uint32_t sh, uint32_t mg) {
     const int blk = s / 4, c = s % 4;
     const f16x2 d2 = splat2(B::half_at(r, 18 * blk, sh));
     const uint32_t w = B::dw(r, 18 * blk + 2 + 4 * c, sh);
-    return pack8(nib_pair_to_f16(w, d2), nib_pair_to_f16(w >> 4, d2),
-                 nib_pair_to_f16(w >> 8, d2), nib_pair_to_f16(w >> 12, d2));
+    return pack8(nib_pair_to_f16(w, d2, mg), nib_pair_to_f16(w >> 4, d2, mg),
+                 nib_pair_to_f16(w >> 8, d2, mg), nib_pair_to_f16(w >> 12, d2, mg));
   }
   __host__ __device__ static int dslot(int j, int s, int i) {
     const int c = s % 4;
@@ -179,7 +184,9 @@ template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
 // ===========================================================================
 // V formats: the A operand of the PV MFMA is V^T. Lane (m, j) holds, for
 // d-tile e, head-dimension position dv(m, e) of the lane's 8 token rows
-// (rows 4j..4j+3 of group 0 and 16+4j..16+4j+3 of group 1).
+// (rows 4j..4j+3 of group 0 and 16+4j..16+4j+3 of group 1). A load names the
+// lane's first row by `voff`; row i of the group is reached with the scalar
+// offset i*stride.
 // ===========================================================================
 template <int VT, int D> struct VFmt;
 
@@ -188,13 +195,13 @@ template <int D> struct VFmt<kF16, D> {
   static constexpr int E = D / 16;       // d-tiles
   static constexpr int NCH = D / 128;    // 16-byte chunks per row per lane
   static constexpr bool kQuant = false;
-  struct Lane { int m; };
+  struct Lane { uint32_t voff, sh; };
   struct Raw { u32x4 c[NCH]; };
-  __device__ static Lane lane(int m) { return Lane{m}; }
   // 16 lanes m read 256 contiguous bytes of a row per instruction.
-  __device__ static void load(Raw& r, const uint8_t* row, const Lane& L) {
+  __device__ static Lane lane(int m, uint32_t row0) { return Lane{row0 + 16u * m, 0}; }
+  __device__ static void load(Raw& r, rsrc_t R, const Lane& L, uint32_t soff) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) r.c[c] = ld_u32x4(row + 16 * (L.m + 16 * c));
+    for (int c = 0; c < NCH; ++c) r.c[c] = buf_u32x4(R, L.voff + 256 * c, soff);
   }
   __device__ static void kill(Raw& r) {
 #pragma unroll
@@ -202,7 +209,7 @@ template <int D> struct VFmt<kF16, D> {
   }
   __host__ __device__ static int dv(int m, int e) { return 8 * (m + 16 * (e / 8)) + e % 8; }
   // Pack half k of chunk e/8 of rows (2p, 2p+1) into dword p.
-  __device__ static f16x8 op(const Raw* R, const f16x2*, int e) {
+  __device__ static f16x8 op(const Raw* R, int e) {
     const int c = e / 8, k = e % 8;
     const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
     u32x4 o;
@@ -223,30 +230,38 @@ template <int VT, int D> struct VQuantBase {
   static constexpr int QB = (VT == kQ8_0) ? EPL : EPL / 2; // quant bytes per lane
   static constexpr int ND = QB / 4;            // realigned quant dwords
   static constexpr int NW = ND + 1;            // window dwords (covers a 2-byte skew)
-  struct Lane { uint32_t woff, sh, doff, last; int m; };
+  struct Lane { uint32_t voff, last, doff, sh; };
   struct Raw { uint32_t w[NW]; f16 d; };
-  __device__ static Lane lane(int m) {
+  __device__ static Lane lane(int m, uint32_t row0) {
     // quant bytes of lane m start at byte qoff of the row
     const int per_blk = (VT == kQ8_0) ? 32 : 16;           // quant bytes per block
     const int qidx = m * QB;
     const int blk = qidx / per_blk, st = qidx % per_blk;
     const uint32_t qoff = uint32_t(BB * blk + 2 + st);
+    const uint32_t woff = qoff & ~3u;
+    // the last window dword is only needed when the window is skewed; keep
+    // its address inside the row so the last row of a pool is never over-read
+    const uint32_t lastoff = woff + 4u * (NW - 1);
     Lane L;
-    L.woff = qoff & ~3u;
+    L.voff = row0 + woff;
+    L.last = row0 + (lastoff + 4u <= uint32_t(RB) ? lastoff : uint32_t(RB) - 4u);
+    L.doff = row0 + uint32_t(BB * blk);
     L.sh = qoff & 3u;
-    L.doff = uint32_t(BB * blk);
-    // the last window dword is only needed when sh != 0; keep its address in
-    // the row so the last row of the pool is never over-read
-    const uint32_t lastoff = L.woff + 4u * (NW - 1);
-    L.last = lastoff + 4u <= uint32_t(RB) ? lastoff : uint32_t(RB) - 4u;
-    L.m = m;
     return L;
   }
-  __device__ static void load(Raw& r, const uint8_t* row, const Lane& L) {
+  __device__ static void load(Raw& r, rsrc_t R, const Lane& L, uint32_t soff) {
+    if constexpr (NW - 1 == 4) {
+      const u32x4 v = buf_u32x4(R, L.voff, soff);
+      r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+    } else if constexpr (NW - 1 == 2) {
+      const u32x2 v = buf_u32x2(R, L.voff, soff);
+      r.w[0] = v[0]; r.w[1] = v[1];
+    } else {
 #pragma unroll
-    for (int i = 0; i < NW - 1; ++i) r.w[i] = ld_u32(row + L.woff + 4 * i);
-    r.w[NW - 1] = ld_u32(row + L.last);
-    r.d = bitcast<f16>(ld_u16(row + L.doff));
+      for (int i = 0; i < NW - 1; ++i) r.w[i] = buf_u32(R, L.voff + 4 * i, soff);
+    }
+    r.w[NW - 1] = buf_u32(R, L.last, soff);
+    r.d = bitcast<f16>(buf_u16(R, L.doff, soff));
   }
   __device__ static void kill(Raw& r) { r.d = f16(0); }
   __device__ static void realign(const Raw& r, uint32_t sh, uint32_t* q) {
@@ -258,15 +273,17 @@ template <int VT, int D> struct VQuantBase {
 template <int D> struct VFmt<kQ8_0, D> : VQuantBase<kQ8_0, D> {
   using B = VQuantBase<kQ8_0, D>;
   __host__ __device__ static int dv(int m, int e) { return m * B::EPL + e; }
-  // q: realigned quant dwords of the 8 rows [row][ND]; dd[p] = (d_2p, d_2p+1)
-  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e) {
+  // q: realigned quant dwords of the 8 rows [row][ND]; dd[p] = (d_2p, d_2p+1).
+  // perm gives (q_A, 0, q_B, 0); XOR 0x64806480 flips the sign bits and
+  // plants the exponent bytes in one instruction.
+  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e, uint32_t) {
     const int k = e % 4, i = e / 4;
     const uint32_t sel = uint32_t(k) | (0x0Cu << 8) | (uint32_t(4 + k) << 16) | (0x0Cu << 24);
     f16x2 o[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel) ^ 0x00800080u;
-      o[p] = (bitcast<f16x2>(x | kMagic) - f16x2{1152.0f16, 1152.0f16}) * dd[p];
+      const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel) ^ 0x64806480u;
+      o[p] = (bitcast<f16x2>(x) - f16x2{1152.0f16, 1152.0f16}) * dd[p];
     }
     return pack8(o[0], o[1], o[2], o[3]);
   }
@@ -280,7 +297,7 @@ template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
     const int blk = qidx / 16, st = qidx % 16;
     return 32 * blk + (e < B::QB ? st + e : 16 + st + (e - B::QB));
   }
-  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e) {
+  __device__ static f16x8 op_q(const uint32_t (*q)[B::ND], const f16x2* dd, int e, uint32_t mg) {
     const bool hi = e >= B::QB;
     const int byte = hi ? e - B::QB : e;
     const int k = byte % 4, i = byte / 4;
@@ -289,7 +306,7 @@ template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel);
-      o[p] = nib_pair_to_f16(hi ? (x >> 4) : x, dd[p]);
+      o[p] = nib_pair_to_f16(hi ? (x >> 4) : x, dd[p], mg);
     }
     return pack8(o[0], o[1], o[2], o[3]);
   }
@@ -304,12 +321,24 @@ struct Tile {
   using VF = VFmt<VT, D>;
   typename KF::Raw k[2];
   typename VF::Raw v[8];
-  int32_t bad;
 };
 
 struct Unit {
   int b, g, p, t_begin, t_end;
 };
+
+
+// LDS layout of a workgroup (in 4-byte words):
+//   unit_start[B+1] | lens[B] | pad | ids[kNid+1] | qs[r*D] | comb[3*(r*D+32)]
+// comb doubles as the scratch of the start-up prefix scan (needs kThreads).
+constexpr int kNid = 2048;     // block ids staged per segment of a partition
+
+__host__ __device__ inline int lds_words(int B, int r, int D) {
+  const int pre = ((2 * B + 1) + 3) & ~3;
+  const int ids = (kNid + 1 + 3) & ~3;
+  const int comb = 3 * (r * D + 32) > kThreads ? 3 * (r * D + 32) : kThreads;
+  return pre + ids + r * D + comb;
+}
 
 template <int KT, int VT, int D>
 __global__ void __launch_bounds__(kThreads)
@@ -321,18 +350,16 @@ decode_kernel(const DecodeArgs a) {
   constexpr int E = D / 16;      // PV d-tiles
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // LDS: [units prefix: B+1 ints][seq_len clamped: B ints][flags: 4 ints]
-  //      [combine: 3 waves x (r*D acc + 2*16 (m,l)) floats]
   int32_t* unit_start = reinterpret_cast<int32_t*>(smem);
   int32_t* lens = unit_start + (a.B + 1);
-  int32_t* flags = lens + a.B;
-  const int pre_ints = ((2 * a.B + 1 + 4) + 3) & ~3;
-  float* comb = reinterpret_cast<float*>(smem) + pre_ints;
+  int32_t* ids = reinterpret_cast<int32_t*>(smem) + (((2 * a.B + 1) + 3) & ~3);
+  float* qs = reinterpret_cast<float*>(ids + ((kNid + 1 + 3) & ~3));
+  float* comb = qs + a.r * D;
   const int comb_stride = a.r * D + 32;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int m = lane & 15;
   const int j = lane >> 4;
 
@@ -350,8 +377,8 @@ decode_kernel(const DecodeArgs a) {
       local += (L + a.psize - 1) / a.psize;
     }
     if (st && blockIdx.x == 0) atomicOr(a.status, st);
-    // block-wide exclusive scan of `local` (Hillis-Steele over LDS)
-    int* scan = reinterpret_cast<int*>(comb);    // kThreads ints, reused below
+    // block-wide inclusive scan of `local` (Hillis-Steele over LDS)
+    int* scan = reinterpret_cast<int*>(comb);
     scan[tid] = local;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
@@ -368,7 +395,7 @@ decode_kernel(const DecodeArgs a) {
     if (tid == kThreads - 1) unit_start[a.B] = scan[tid];
     __syncthreads();
   }
-  const int n_bp = unit_start[a.B];
+  const int n_bp = __builtin_amdgcn_readfirstlane(unit_start[a.B]);
   const int n_units = n_bp * a.Hkv;
   const int G = gridDim.x;
 
@@ -389,7 +416,11 @@ decode_kernel(const DecodeArgs a) {
   const uint32_t kstride = uint32_t(a.Hkv) * KF::RB;   // bytes between token rows
   const uint32_t vstride = uint32_t(a.Hkv) * VF::RB;
   const uint32_t ksh = KF::shift(j);
-  const auto vl = VF::lane(m);
+  const uint32_t kvoff = m * kstride + KF::lane_off(j);
+  const auto vl = VF::lane(m, 4u * j * vstride);
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int seg_tokens = kNid << a.bs_shift;
 
   for (int u = logical; u < n_units; u += G) {
     // ---- locate the unit ---------------------------------------------------
@@ -402,140 +433,165 @@ decode_kernel(const DecodeArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (unit_start[mid] <= bp) lo = mid; else hi = mid - 1;
       }
-      U.b = lo;
+      U.b = __builtin_amdgcn_readfirstlane(lo);
     }
-    U.p = bp - unit_start[U.b];
+    U.p = bp - __builtin_amdgcn_readfirstlane(unit_start[U.b]);
     U.t_begin = U.p * a.psize;
-    U.t_end = min(lens[U.b], U.t_begin + a.psize);
-    const int ntiles = (U.t_end - U.t_begin + kTile - 1) / kTile;
+    U.t_end = min(__builtin_amdgcn_readfirstlane(lens[U.b]), U.t_begin + a.psize);
 
-    // ---- Q operand: heads g*r .. g*r+r-1 in columns n = lane%16 ----------
-    f16x8 qop[S];
+    // ---- stage the group's r query rows (scaled by scale*log2 e) ----------
     {
-      const int n = m;
-      const bool live = n < a.r;
-      const float* qrow = a.q + (int64_t(U.b) * a.Hq + U.g * a.r + (live ? n : 0)) * D;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x = live ? qrow[KF::dslot(j, s, i)] * a.qscale : 0.0f;
-          qop[s][i] = f16(x);
-        }
+      const float* qg = a.q + (int64_t(U.b) * a.Hq + U.g * a.r) * D;
+      for (int i = tid; i < a.r * D / 4; i += kThreads) {
+        float4 v = reinterpret_cast<const float4*>(qg)[i];
+        v.x *= a.qscale; v.y *= a.qscale; v.z *= a.qscale; v.w *= a.qscale;
+        reinterpret_cast<float4*>(qs)[i] = v;
       }
     }
 
+    f16x8 qop[S];
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     int bad = 0;
 
-    // ---- tile loader ------------------------------------------------------
-    auto load_tile = [&](T& t, int k) __attribute__((always_inline)) {
-      const int t0 = U.t_begin + k * kTile;
-      t.bad = 0;
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        const int tg = t0 + 16 * gi;
-        const bool live = tg < U.t_end;
-        const int tq = live ? tg : U.t_end - 1;
-        const int jb = tq >> a.bs_shift;
-        int32_t id = block_of(a.table, U.b, a.max_blocks, jb);
-        if (uint32_t(id) >= uint32_t(a.nblocks)) { t.bad = 1; id = 0; }
-        const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
-        const uint8_t* kb = a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, KF::RB);
-        const uint8_t* vb = a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, VF::RB);
-        KF::load(t.k[gi], kb + m * kstride, j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) VF::load(t.v[4 * gi + i], vb + (4 * j + i) * vstride, vl);
+    for (int seg_t0 = U.t_begin; seg_t0 < U.t_end; seg_t0 += seg_tokens) {
+      const int seg_t1 = min(U.t_end, seg_t0 + seg_tokens);
+      const int jb0 = seg_t0 >> a.bs_shift;
+      const int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // earlier readers of ids[] are done
+      int badl = 0;
+      for (int i = tid; i < nb; i += kThreads) {
+        int32_t id = block_of(a.table, U.b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
       }
-    };
+      bad |= __syncthreads_or(badl);         // also publishes ids[] and qs[]
 
-    // ---- tile compute: scores, online softmax (exp2), PV ------------------
-    auto compute_tile = [&](T& t, int k) __attribute__((always_inline)) {
-      const int t0 = U.t_begin + k * kTile;
-      bad |= t.bad;
-      const bool full = t0 + kTile <= U.t_end;
-      if (!full) {
-        // zero V rows past the end so 0 * junk never reaches the PV MFMA
+      if (seg_t0 == U.t_begin) {
+        // Q operand: column n = lane%16 holds head g*r+n (zero when n >= r)
+        const int n = m < a.r ? m : a.r - 1;
+        const float keep = m < a.r ? 1.0f : 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qop[s][i] = f16(qs[n * D + KF::dslot(j, s, i)] * keep);
+      }
+
+      const int ntiles = (seg_t1 - seg_t0 + kTile - 1) / kTile;
+
+      // ---- tile loader (block ids come from LDS, one per 16-row group) ----
+      // A tile index past the segment still issues its loads, through a
+      // zero-size buffer resource: they return 0 without touching memory, so
+      // every path through the loop has the same loads in flight and the
+      // compiler's wait counts stay exact.
+      auto load_tile = [&](T& t, int kt) __attribute__((always_inline)) {
+        const bool valid = kt < ntiles;
+        const int t0 = seg_t0 + (valid ? kt : ntiles - 1) * kTile;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const int tg = t0 + 16 * gi;
+          const bool live = tg < U.t_end;
+          const int tq = live ? tg : U.t_end - 1;
+          const int32_t id = __builtin_amdgcn_readfirstlane(ids[(tq >> a.bs_shift) - jb0]);
+          const int slot0 = live ? (tg & bs_mask) : 0;
+          const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, KF::RB),
+                                      valid ? 16u * kstride : 0u);
+          const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, U.g, VF::RB),
+                                      valid ? 16u * vstride : 0u);
+          KF::load(t.k[gi], kr, kvoff);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) VF::load(t.v[4 * gi + i], vr, vl, i * vstride);
+        }
+      };
+
+      // ---- tile compute: scores, online softmax (exp2), PV ----------------
+      auto compute_tile = [&](T& t, int t0) __attribute__((always_inline)) {
+        const bool full = t0 + kTile <= U.t_end;
+        if (!full) {
+          // zero V rows past the end so 0 * junk never reaches the PV MFMA
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + 16 * gi + 4 * j + i >= U.t_end) VF::kill(t.v[4 * gi + i]);
+        }
+        f32x4 sc[2];
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < S; ++s) s4 = mfma(KF::op(t.k[gi], s, ksh, mg), qop[s], s4);
+          sc[gi] = s4;
+        }
+        if (!full) {
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + 16 * gi + 4 * j + i >= U.t_end) sc[gi][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Lazy rescale: the softmax is invariant to the reference m, so m_run
+        // only moves when some head's max exceeds it by more than kSlack
+        // (then p <= 2^kSlack, safe in f16) - the accumulators are rescaled
+        // a handful of times per partition instead of at most tiles (the
+        // lucebox page skips the rescale when the max is unchanged).
+        if (__any(mx > m_run + kSlack)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] *= alpha;
+          m_run = m_new;
+        }
+        float p[8];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * gi + 4 * j + i >= U.t_end) VF::kill(t.v[4 * gi + i]);
-      }
-      f32x4 sc[2];
+          for (int i = 0; i < 4; ++i) p[4 * gi + i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_run);
+        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l_run += ps;
+        f16x8 pop;
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < S; ++s) s4 = mfma(KF::op(t.k[gi], s, ksh), qop[s], s4);
-        sc[gi] = s4;
-      }
-      if (!full) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * gi + 4 * j + i >= U.t_end) sc[gi][i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      // skip the accumulator rescale when no head's max moved (lucebox PR
-      // #555, Summary: skip-if-unchanged rescale)
-      if (__any(m_new != m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] *= alpha;
-        m_run = m_new;
-      }
-      float p[8];
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[4 * gi + i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_run);
-      float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run += ps;
-      f16x8 pop;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pop[i] = f16(p[i]);
+        for (int i = 0; i < 8; ++i) pop[i] = f16(p[i]);
 
-      if constexpr (VF::kQuant) {
-        uint32_t q[8][VF::ND];
-        f16x2 dd[4];
+        if constexpr (VF::kQuant) {
+          uint32_t q[8][VF::ND];
+          f16x2 dd[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) VF::realign(t.v[i], vl.sh, q[i]);
+          for (int i = 0; i < 8; ++i) VF::realign(t.v[i], vl.sh, q[i]);
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) dd[pp] = f16x2{t.v[2 * pp].d, t.v[2 * pp + 1].d};
+          for (int pp = 0; pp < 4; ++pp) dd[pp] = f16x2{t.v[2 * pp].d, t.v[2 * pp + 1].d};
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op_q(q, dd, e), pop, acc[e]);
-      } else {
+          for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op_q(q, dd, e, mg), pop, acc[e]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op(t.v, nullptr, e), pop, acc[e]);
-      }
-    };
+          for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op(t.v, e), pop, acc[e]);
+        }
+      };
 
-    // ---- wave w streams tiles w, w+4, ... with one tile prefetched --------
-    int k = wave;
-    if (k < ntiles) {
-      T A, Bt;
-      load_tile(A, k);
-      while (true) {
-        if (k + kWaves < ntiles) load_tile(Bt, k + kWaves);
-        compute_tile(A, k);
-        k += kWaves;
-        if (k >= ntiles) break;
-        if (k + kWaves < ntiles) load_tile(A, k + kWaves);
-        compute_tile(Bt, k);
-        k += kWaves;
-        if (k >= ntiles) break;
+      // ---- wave w streams tiles w, w+4, ... with one tile prefetched ------
+      int k = wave;
+      if (k < ntiles) {
+        T A, Bt;
+        load_tile(A, k);
+        while (true) {
+          load_tile(Bt, k + kWaves);
+          compute_tile(A, seg_t0 + k * kTile);
+          k += kWaves;
+          if (k >= ntiles) break;
+          load_tile(A, k + kWaves);
+          compute_tile(Bt, seg_t0 + k * kTile);
+          k += kWaves;
+          if (k >= ntiles) break;
+        }
       }
     }
 
@@ -553,11 +609,9 @@ decode_kernel(const DecodeArgs a) {
           cw[a.r * D + 16 + n] = l_run;
         }
       }
-      if (lane == 0) flags[wave] = bad;
     }
     __syncthreads();
     if (wave == 0) {
-      const int any_bad = bad | flags[1] | flags[2] | flags[3];
       float M = m_run;
       float mw[3], lw[3];
 #pragma unroll
@@ -577,7 +631,7 @@ decode_kernel(const DecodeArgs a) {
       }
       const float inv = 1.0f / l;
       const int h = U.g * a.r + n;
-      if (any_bad && lane == 0) atomicOr(a.status, 1u);
+      if (bad && lane == 0) atomicOr(a.status, 1u);
       if (n < a.r) {
         float* dst;
         if (a.direct) {
@@ -586,7 +640,7 @@ decode_kernel(const DecodeArgs a) {
           const int64_t row = (int64_t(U.b) * a.Hq + h) * a.p_max + U.p;
           dst = a.part_o + row * D;
           if (j == 0) {
-            a.part_ml[2 * row] = any_bad ? __builtin_nanf("") : M;
+            a.part_ml[2 * row] = bad ? __builtin_nanf("") : M;
             a.part_ml[2 * row + 1] = l;
           }
         }
@@ -598,7 +652,7 @@ decode_kernel(const DecodeArgs a) {
             float v = acc[e][i] * c0;
 #pragma unroll
             for (int w = 0; w < 3; ++w) v += comb[w * comb_stride + n * D + d] * cwt[w];
-            dst[d] = any_bad ? __builtin_nanf("") : v * inv;
+            dst[d] = bad ? __builtin_nanf("") : v * inv;
           }
       }
     }
@@ -608,10 +662,7 @@ decode_kernel(const DecodeArgs a) {
 
 template <int KT, int VT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const int pre_ints = ((2 * a.B + 1 + 4) + 3) & ~3;
-  const int comb_floats = 3 * (a.r * D + 32);
-  const int scan_floats = kThreads;
-  const size_t lds = size_t(pre_ints + (comb_floats > scan_floats ? comb_floats : scan_floats)) * 4;
+  const size_t lds = size_t(lds_words(a.B, a.r, D)) * 4;
   hipLaunchKernelGGL((decode_kernel<KT, VT, D>), dim3(a.grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
