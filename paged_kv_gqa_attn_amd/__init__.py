@@ -55,6 +55,10 @@ class PaError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7);
+    # importing torch first makes this library bind to that copy, so device
+    # memory and streams handed over from torch live in the same runtime.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "

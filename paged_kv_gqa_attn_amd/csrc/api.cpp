@@ -143,7 +143,9 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
     // exceed ~4% of the K/V bytes of a partition.
     const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
     const int64_t units_target = int64_t(num_cus) * 4;
-    const int64_t per_unit = kTileTokens * kWavesPerUnit;
+    // the decode kernel's tile: 64 tokens when K and V are both Q4_0, else 32
+    const int64_t tile = (s.k_type == PA_Q4_0 && s.v_type == PA_Q4_0) ? 64 : kTileTokens;
+    const int64_t per_unit = tile * kWavesPerUnit;
     const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * s.Hkv, units_target)), per_unit);
     const double part_bytes = double(s.Hq) * (s.D + 2) * 4.0 * 2.0;
     const double kv_per_token = double(s.Hkv) * double(rbk + rbv);

@@ -41,7 +41,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;       // tokens per tile = two 16-row MFMA groups
 constexpr uint32_t kMagic = 0x64006400u;   // f16 1024.0 in both halves
 constexpr float kSlack = 8.0f;             // lazy-rescale slack (log2 units)
 
@@ -50,6 +49,24 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ f16x2 splat2(f16 x) { return f16x2{x, x}; }
+
+// Reductions over the four lanes that hold the same head (lane, lane^16,
+// lane^32, lane^48). v_permlane16_swap / v_permlane32_swap with both operands
+// set to x leave {own value, partner value} in the two results, so each
+// butterfly step is one VALU swap and one max/add (no LDS round trip), and
+// every lane of a head ends with the bitwise-same result.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // ---------------------------------------------------------------------------
 // Integer -> f16 conversion: a byte or nibble placed under the f16 exponent
@@ -315,12 +332,19 @@ template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
 // ===========================================================================
 // The kernel
 // ===========================================================================
+// 16-row groups per tile: 4 (64 tokens) when both formats are Q4_0, whose
+template <int KT, int VT>
+struct TileGroups {
+  static constexpr int value = 2;
+};
+
 template <int KT, int VT, int D>
 struct Tile {
   using KF = KFmt<KT, D>;
   using VF = VFmt<VT, D>;
-  typename KF::Raw k[2];
-  typename VF::Raw v[8];
+  static constexpr int NG = TileGroups<KT, VT>::value;
+  typename KF::Raw k[NG];
+  typename VF::Raw v[NG / 2][8];   // per group pair: the lane's 8 token rows
 };
 
 struct Unit {
@@ -340,14 +364,24 @@ __host__ __device__ inline int lds_words(int B, int r, int D) {
   return pre + ids + r * D + comb;
 }
 
+// Workgroups per CU the register allocation is held to: two (256 VGPRs per
+// wave, two waves per SIMD) where the kernel fits without spilling - small
+// rows (Q4_0 K and V) or D=128 - else one.
 template <int KT, int VT, int D>
-__global__ void __launch_bounds__(kThreads)
+struct MinBlocks {
+  static constexpr int value = (D == 128 || (KT == kQ4_0 && VT == kQ4_0)) ? 2 : 1;
+};
+
+template <int KT, int VT, int D>
+__global__ void __launch_bounds__(kThreads, (MinBlocks<KT, VT, D>::value))
 decode_kernel(const DecodeArgs a) {
   using KF = KFmt<KT, D>;
   using VF = VFmt<VT, D>;
   using T = Tile<KT, VT, D>;
   constexpr int S = D / 32;      // score MFMA steps
   constexpr int E = D / 16;      // PV d-tiles
+  constexpr int NG = T::NG;      // 16-row groups per tile
+  constexpr int kTile = 16 * NG; // tokens per tile
 
   extern __shared__ __align__(16) unsigned char smem[];
   int32_t* unit_start = reinterpret_cast<int32_t*>(smem);
@@ -490,7 +524,7 @@ decode_kernel(const DecodeArgs a) {
         const bool valid = kt < ntiles;
         const int t0 = seg_t0 + (valid ? kt : ntiles - 1) * kTile;
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+        for (int gi = 0; gi < NG; ++gi) {
           const int tg = t0 + 16 * gi;
           const bool live = tg < U.t_end;
           const int tq = live ? tg : U.t_end - 1;
@@ -502,7 +536,7 @@ decode_kernel(const DecodeArgs a) {
                                       valid ? 16u * vstride : 0u);
           KF::load(t.k[gi], kr, kvoff);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) VF::load(t.v[4 * gi + i], vr, vl, i * vstride);
+          for (int i = 0; i < 4; ++i) VF::load(t.v[gi / 2][4 * (gi % 2) + i], vr, vl, i * vstride);
         }
       };
 
@@ -512,30 +546,30 @@ decode_kernel(const DecodeArgs a) {
         if (!full) {
           // zero V rows past the end so 0 * junk never reaches the PV MFMA
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi)
+          for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (t0 + 16 * gi + 4 * j + i >= U.t_end) VF::kill(t.v[4 * gi + i]);
+              if (t0 + 16 * gi + 4 * j + i >= U.t_end) VF::kill(t.v[gi / 2][4 * (gi % 2) + i]);
         }
-        f32x4 sc[2];
+        f32x4 sc[NG];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int gi = 0; gi < NG; ++gi) sc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < S; ++s) s4 = mfma(KF::op(t.k[gi], s, ksh, mg), qop[s], s4);
-          sc[gi] = s4;
-        }
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) sc[gi] = mfma(KF::op(t.k[gi], s, ksh, mg), qop[s], sc[gi]);
         if (!full) {
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi)
+          for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (t0 + 16 * gi + 4 * j + i >= U.t_end) sc[gi][i] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float mx = -INFINITY;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          mx = fmaxf(mx, fmaxf(fmaxf(sc[gi][0], sc[gi][1]), fmaxf(sc[gi][2], sc[gi][3])));
+        mx = max_over_rows(mx);
         // Lazy rescale: the softmax is invariant to the reference m, so m_run
         // only moves when some head's max exceeds it by more than kSlack
         // (then p <= 2^kSlack, safe in f16) - the accumulators are rescaled
@@ -549,32 +583,34 @@ decode_kernel(const DecodeArgs a) {
           for (int e = 0; e < E; ++e) acc[e] *= alpha;
           m_run = m_new;
         }
-        float p[8];
+        float ps = 0.0f;
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
+        for (int pp = 0; pp < NG / 2; ++pp) {
+          float p[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[4 * gi + i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_run);
-        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l_run += ps;
-        f16x8 pop;
+          for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pop[i] = f16(p[i]);
-
-        if constexpr (VF::kQuant) {
-          uint32_t q[8][VF::ND];
-          f16x2 dd[4];
+            for (int i = 0; i < 4; ++i)
+              p[4 * h2 + i] = __builtin_amdgcn_exp2f(sc[2 * pp + h2][i] - m_run);
+          ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          f16x8 pop;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) VF::realign(t.v[i], vl.sh, q[i]);
+          for (int i = 0; i < 8; ++i) pop[i] = f16(p[i]);
+          if constexpr (VF::kQuant) {
+            uint32_t q[8][VF::ND];
+            f16x2 dd[4];
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) dd[pp] = f16x2{t.v[2 * pp].d, t.v[2 * pp + 1].d};
+            for (int i = 0; i < 8; ++i) VF::realign(t.v[pp][i], vl.sh, q[i]);
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op_q(q, dd, e, mg), pop, acc[e]);
-        } else {
+            for (int qq = 0; qq < 4; ++qq) dd[qq] = f16x2{t.v[pp][2 * qq].d, t.v[pp][2 * qq + 1].d};
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op(t.v, e), pop, acc[e]);
+            for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op_q(q, dd, e, mg), pop, acc[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = mfma(VF::op(t.v[pp], e), pop, acc[e]);
+          }
         }
+        l_run += sum_over_rows(ps);
       };
 
       // ---- wave w streams tiles w, w+4, ... with one tile prefetched ------

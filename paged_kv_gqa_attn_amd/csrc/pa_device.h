@@ -76,17 +76,21 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
 }
+// Cache policy of the K/V loads. The non-temporal hint is off: a quantised
+// row shares 128-byte lines with the neighbouring kv head, read by another
+// workgroup on the same XCD, and streaming those lines out of L2 costs a refetch.
+constexpr int kNonTemporal = 0;
 __device__ __forceinline__ u32x4 buf_u32x4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
 }
 __device__ __forceinline__ u32x2 buf_u32x2(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal);
 }
 __device__ __forceinline__ uint32_t buf_u32(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
 }
 __device__ __forceinline__ uint16_t buf_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kNonTemporal);
 }
 
 // (x & mask) | magic in one v_and_or_b32: gfx9 VOP3 takes no literal, so the
