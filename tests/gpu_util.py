@@ -77,3 +77,50 @@ def check_parity(case, out, heads=None):
         worst = max(worst, e)
         assert e <= tol, f"b={b} g={g}: max row error {e:.3e} > {tol}"
     return worst
+
+
+class BlockSubset:
+    """Host copy of selected blocks of a device pool, serving the oracle's row
+    reads by byte offset (the oracle computes the offsets itself). Reading a
+    row of a block that was not copied raises."""
+
+    def __init__(self, pool_dev, block_ids):
+        self.shape = tuple(pool_dev.shape)          # [nblocks, bs, Hkv, rb]
+        ids = sorted(set(int(i) for i in block_ids))
+        self.index = {b: k for k, b in enumerate(ids)}
+        sel = torch.tensor(ids, dtype=torch.int64, device=pool_dev.device)
+        self.data = pool_dev.index_select(0, sel).cpu().numpy()
+
+    def read_rows(self, offsets, rbytes):
+        nb, bs, hkv, rb = self.shape
+        assert rb == rbytes
+        offsets = np.asarray(offsets, dtype=np.int64)
+        if offsets.size and (offsets % rb).any():
+            raise ValueError("unaligned row offset")
+        row = offsets // rb
+        blk = row // (bs * hkv)
+        within = row % (bs * hkv)
+        k = np.array([self.index[int(b)] for b in blk], dtype=np.int64)
+        flat = self.data.reshape(len(self.index), bs * hkv, rb)
+        return flat[k, within]
+
+
+def sampled_parity(case_dev, out, items):
+    """Oracle check of selected (b, g) groups of a device-resident case; the
+    pool bytes the oracle reads are host copies of just those sequences'
+    blocks."""
+    import types
+    tab = case_dev.table.cpu()
+    blocks = set()
+    for b, _ in items:
+        n = -(-case_dev.seq_lens[b] // case_dev.block_size)
+        blocks |= set(tab[b, :n].tolist())
+    host = types.SimpleNamespace(**{k: getattr(case_dev, k) for k in (
+        "B", "Hq", "Hkv", "D", "block_size", "nblocks", "max_blocks", "k_fmt", "v_fmt",
+        "seq_lens", "scale", "seed")})
+    host.q = case_dev.q.cpu()
+    host.table = tab
+    host.seq_len = case_dev.seq_len.cpu()
+    host.k_pool = BlockSubset(case_dev.k_pool, blocks)
+    host.v_pool = BlockSubset(case_dev.v_pool, blocks)
+    return check_parity(host, out, heads=items)

@@ -1,0 +1,173 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+include/paged_attn.h declares, and its host logic (planner, argument
+validation, error reporting, row sizes) behaves as documented. No kernel is
+launched: every call here returns before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+LIB = os.path.join(ROOT, "paged_kv_gqa_attn_amd", "libpaged_attn.so")
+
+
+def _ensure_built():
+    """Build the library if nothing is built yet (without importing the
+    package, whose import needs the library)."""
+    if not os.path.exists(LIB):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_pa_build", os.path.join(ROOT, "paged_kv_gqa_attn_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+
+
+_ensure_built()
+import paged_kv_gqa_attn_amd as pa  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_][a-z_0-9]*)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ["paged_attn_plan", "paged_attn_decode", "paged_attn_merge", "paged_attn_step",
+                 "paged_kv_gather", "paged_attn_status", "kv_pool_alloc", "kv_pool_release",
+                 "kv_pool_create", "kv_pool_destroy", "kv_pool_reset", "pa_last_error"]:
+        assert must in names, must
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    L = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(L, n)
+
+
+def test_binding_names_match_the_c_abi():
+    for n in declared_functions():
+        if n.startswith("kv_pool_"):
+            continue                       # wrapped by the KvPool class
+        assert hasattr(pa, n), n
+
+
+def test_row_bytes():
+    assert pa.pa_row_bytes(pa.PA_F16, 256) == 512
+    assert pa.pa_row_bytes(pa.PA_Q8_0, 256) == 272
+    assert pa.pa_row_bytes(pa.PA_Q4_0, 256) == 144
+    assert pa.pa_row_bytes(pa.PA_Q4_0, 128) == 72
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_row_bytes(pa.PA_Q4_0, 100)
+    assert e.value.code == pa.PA_ERR_INVALID and "pa_row_bytes" in str(e.value)
+
+
+def _shape(**kw):
+    base = dict(B=8, Hq=24, Hkv=4, D=256, block_size=16, nblocks=100000, max_blocks=8192,
+                k_type="q4_0", v_type="q4_0")
+    base.update(kw)
+    return pa.shape_of(**base)
+
+
+def test_plan_automatic_partitions_for_long_context():
+    p = pa.paged_attn_plan(_shape(), 131072, total_tokens=8 * 131072, num_cus=256)
+    assert p.psize % 32 == 0 and p.psize >= 1024
+    assert p.p_max == -(-131072 // p.psize)
+    assert p.direct == 0
+    assert p.ws_bytes == 256 + 8 * 24 * p.p_max * (256 + 2) * 4
+    assert 1 <= p.grid <= 256 * 8
+    assert abs(p.scale - 1 / 16) < 1e-7
+
+
+def test_plan_partial_traffic_floor_and_direct_mode():
+    # a short batch: the partial-traffic floor forces one partition -> direct
+    p = pa.paged_attn_plan(_shape(B=1), 200, num_cus=256)
+    assert p.direct == 1 and p.p_max == 1 and p.ws_bytes == 256
+    assert p.psize >= 200
+    # the floor keeps partials under ~4% of the K/V bytes of a partition
+    p = pa.paged_attn_plan(_shape(), 32768, total_tokens=8 * 32768, num_cus=256)
+    part = 24 * (256 + 2) * 4 * 2
+    kv = p.psize * 4 * (144 + 144)
+    assert part / kv <= 0.04 + 1e-9
+
+
+def test_plan_forced_partitions_and_tokens():
+    p = pa.paged_attn_plan(_shape(), 1000, num_cus=256, force_partitions=1)
+    assert p.direct == 1 and p.psize >= 1000
+    p = pa.paged_attn_plan(_shape(), 1000, num_cus=256, force_partitions=7)
+    assert p.p_max <= 7 and p.psize % 32 == 0 and p.p_max == -(-1000 // p.psize)
+    p = pa.paged_attn_plan(_shape(), 1000, num_cus=256, partition_tokens=100)
+    assert p.psize == 128 and p.p_max == 8
+    p = pa.paged_attn_plan(_shape(), 0, num_cus=256)
+    assert p.direct == 1
+
+
+def test_plan_ragged_grid_follows_total_tokens():
+    lens = [131072] + [8192] * 7
+    p1 = pa.paged_attn_plan(_shape(), max(lens), total_tokens=sum(lens), num_cus=256)
+    p2 = pa.paged_attn_plan(_shape(), max(lens), total_tokens=0, num_cus=256)
+    assert p1.grid <= p2.grid
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(Hq=25), pa.PA_ERR_INVALID, "multiple of Hkv"),
+    (dict(D=64), pa.PA_ERR_UNSUPPORTED, "D=64"),
+    (dict(block_size=24), pa.PA_ERR_INVALID, "power of two"),
+    (dict(block_size=8), pa.PA_ERR_UNSUPPORTED, "block_size"),
+    (dict(Hq=68, Hkv=4), pa.PA_ERR_UNSUPPORTED, "query heads per K/V head"),
+    (dict(B=0), pa.PA_ERR_INVALID, ">= 1"),
+    (dict(B=2000), pa.PA_ERR_UNSUPPORTED, "B=2000"),
+    (dict(k_type=7), pa.PA_ERR_INVALID, "type"),
+])
+def test_plan_refusals_name_the_entry_point(kw, code, word):
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_plan(_shape(**kw), 100, num_cus=256)
+    assert e.value.code == code
+    assert "paged_attn_plan" in str(e.value) and word in str(e.value)
+
+
+def test_plan_rejects_seq_len_beyond_table():
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_plan(_shape(max_blocks=10), 161, num_cus=256)
+    assert e.value.code == pa.PA_ERR_INVALID
+
+
+def test_decode_argument_checks_before_any_launch():
+    plan = pa.paged_attn_plan(_shape(), 4096, num_cus=256)
+    fake = 0x1000            # never dereferenced: every call below is refused first
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_decode(plan, fake, fake, fake, fake, fake, fake, out=fake, stream=0,
+                             ws_bytes=int(plan.ws_bytes) - 1)
+    assert e.value.code == pa.PA_ERR_INVALID and "workspace" in str(e.value)
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_decode(plan, None, fake, fake, fake, fake, fake, out=fake, stream=0,
+                             ws_bytes=int(plan.ws_bytes))
+    assert "paged_attn_decode" in str(e.value)
+    bad = pa.PaPlan()
+    bad.shape = _shape()
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_merge(bad, fake, fake, fake, stream=0, ws_bytes=1 << 20)
+    assert "not produced by paged_attn_plan" in str(e.value)
+    with pytest.raises(pa.PaError):
+        pa.paged_kv_gather(plan, fake, 2, fake, 0, 0, 1, fake, stream=0)
+    with pytest.raises(pa.PaError):
+        pa.paged_kv_gather(plan, fake, 0, fake, 8, 0, 1, fake, stream=0)
+    with pytest.raises(pa.PaError):
+        pa.paged_kv_gather(plan, fake, 0, fake, 0, 8192 * 16, 1, fake, stream=0)
+
+
+def test_direct_plan_merge_is_a_no_op():
+    plan = pa.paged_attn_plan(_shape(B=1), 100, num_cus=256)
+    assert plan.direct == 1
+    pa.paged_attn_merge(plan, 0x1000, 0x1000, 0x1000, stream=0, ws_bytes=256)
