@@ -244,11 +244,11 @@ def make_case(seq_lens: Sequence[int], *, Hq: int = 24, Hkv: int = 4, D: int = 2
               nblocks: Optional[int] = None, max_blocks: Optional[int] = None,
               table_mode: str = "shuffled", junk: str = "nan", seed: int = 0,
               device="cpu", split_block: int = 0, scale: Optional[float] = None,
-              value_std: float = 1.0, chunk_tokens: int = 1 << 16) -> Case:
+              value_std: float = 1.0, q_std: float = 1.0, chunk_tokens: int = 1 << 16) -> Case:
     """Build one seeded decode-step case.
 
-    q ~ N(0,1) fp32; live K and V values ~ N(0, value_std^2) then encoded in
-    k_fmt / v_fmt. The pool defaults to 1.25x the used blocks (rounded up);
+    q ~ N(0, q_std^2) fp32; live K and V values ~ N(0, value_std^2) then
+    encoded in k_fmt / v_fmt. The pool defaults to 1.25x the used blocks (rounded up);
     every unused block and every dead slot of a partly filled block holds junk.
     """
     seq_lens = [int(L) for L in seq_lens]
@@ -266,7 +266,7 @@ def make_case(seq_lens: Sequence[int], *, Hq: int = 24, Hkv: int = 4, D: int = 2
     dev = torch.device(device)
     gen_dev = torch.Generator(device=dev).manual_seed(seed + 1)
     table = make_table(seq_lens, bs, nblocks, max_blocks, table_mode, gen_cpu, split_block)
-    q = torch.randn((B, Hq, D), generator=gen_dev, device=dev, dtype=torch.float32)
+    q = torch.randn((B, Hq, D), generator=gen_dev, device=dev, dtype=torch.float32) * q_std
 
     def build_pool(fmt: str, salt: int) -> torch.Tensor:
         rb = row_bytes(fmt, D)

@@ -207,3 +207,37 @@ def test_red_control_wrong_table_fails_parity():
     out, _ = run(g, plan_for(case, force_partitions=1), table=tab)
     ref = oracle.decode_case(case)
     assert float(rel_err_rows(out.cpu().double().numpy(), ref).max()) > 1e-2
+
+
+@pytest.mark.parametrize("pair,std", [(("q4_0", "q4_0"), 400.0), (("q4_0", "f16"), 400.0),
+                                      (("f16", "q4_0"), 400.0), (("q8_0", "q8_0"), 5000.0),
+                                      (("q8_0", "q4_0"), 5000.0)])
+def test_large_block_scales_use_the_exact_conversion(pair, std):
+    """Block scales |d| >= 64 (live rows) cannot use the fma-form conversion
+    (-1024*d is not a finite f16); the kernel must recompute with the exact
+    form and still match the oracle. q shrinks as K grows so the logits stay
+    O(1), as in real attention (with f16 operands, logit error grows with
+    |q|*|k|)."""
+    case = _case([300, 77, 1000], k_fmt=pair[0], v_fmt=pair[1], seed=41, value_std=std,
+                 q_std=min(1.0, 4.0 / std))
+    g = case.to(DEV)
+    for force in (0, 1, 3):
+        out, _ = run(g, plan_for(case, force_partitions=force))
+        check_parity(case, out)
+
+
+def test_mixed_scales_within_one_sequence():
+    """Large-scale rows only in part of the context: the waves that meet them
+    recompute, the others keep the fast form."""
+    case = _case([2000, 500], k_fmt="q4_0", v_fmt="q4_0", seed=43)
+    big = synth.make_case([2000, 500], k_fmt="q4_0", v_fmt="q4_0", seed=43, value_std=500.0,
+                          nblocks=case.nblocks)
+    case.q *= 0.002   # logits stay O(1) on the large rows (f16 operands: logit error ~ |q||k|)
+    # splice the large-scale rows of blocks 10..20 of sequence 0 into the pool
+    ids = case.table[0, 10:20].long()
+    case.k_pool[ids] = big.k_pool[big.table[0, 10:20].long()]
+    case.v_pool[ids] = big.v_pool[big.table[0, 10:20].long()]
+    g = case.to(DEV)
+    for force in (0, 1, 4):
+        out, _ = run(g, plan_for(case, force_partitions=force))
+        check_parity(case, out)
