@@ -114,7 +114,14 @@ typedef struct pa_plan {
   int32_t grid;         /* workgroups launched by paged_attn_decode */
   int32_t num_cus;      /* compute units the plan was sized for */
   int32_t direct;       /* 1: p_max == 1, decode writes out, merge is a no-op */
-  int32_t reserved;
+  int32_t path;         /* decode kernel: 2 = LDS-staged (K/V blocks DMA'd into
+                           LDS, one workgroup per 4 kv heads; needs Hkv % 4 == 0,
+                           B <= 256, no F16 side at D=256 and 16-byte aligned
+                           pools, else path 1 runs), 1 = register-streaming.
+                           paged_attn_plan picks 2 where the shape allows it; a
+                           caller may set 1 to force the register kernel. The
+                           two kernels differ only in the order of fp32
+                           accumulation. */
   uint64_t ws_bytes;    /* workspace bytes paged_attn_decode/merge need */
 } pa_plan;
 
@@ -157,9 +164,13 @@ int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t tota
  *   [4, 256)    reserved
  *   partials    only when plan->direct == 0, at offset 256:
  *               float o [B][Hq][p_max][D]  normalised output of each partition
- *               float ml[B][Hq][p_max][2]  (m, l): m = max over the partition of
- *                                          the base-2 logit log2(e)*scale*q.k,
- *                                          l = sum of 2^(logit - m)
+ *               float ml[B][Hq][p_max][2]  (m, l): m is a reference value of
+ *                                          the base-2 logits x = log2(e)*scale*q.k
+ *                                          of the partition with
+ *                                          m <= max x <= m + 8 (the kernel moves
+ *                                          its reference only when a logit
+ *                                          exceeds it by more than 8),
+ *                                          l = sum of 2^(x - m)
  *               Partition p of sequence b covers tokens [p*psize,
  *               min(seq_len, (p+1)*psize)); only p < ceil(seq_len/psize) is
  *               written or read. A partition that met a bad block id holds

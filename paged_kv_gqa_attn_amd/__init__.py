@@ -38,14 +38,14 @@ class PaPlan(ctypes.Structure):
     _fields_ = [("shape", PaShape), ("scale", ctypes.c_float), ("psize", ctypes.c_int32),
                 ("p_max", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("direct", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("direct", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("ws_bytes", ctypes.c_uint64)]
 
     def __repr__(self):
         s = self.shape
         return (f"PaPlan(B={s.B}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D}, bs={s.block_size}, "
                 f"psize={self.psize}, p_max={self.p_max}, grid={self.grid}, "
-                f"direct={self.direct}, ws_bytes={self.ws_bytes})")
+                f"direct={self.direct}, path={self.path}, ws_bytes={self.ws_bytes})")
 
 
 class PaError(RuntimeError):

@@ -58,13 +58,21 @@ int32_t check_shape(const pa_shape* s, const char* who) {
   return PA_OK;
 }
 
+// The LDS-staged kernel takes the shape: quads of kv heads, the batch prefix
+// fits its LDS budget, and one step of both sides fits a ring slot.
+bool lds_path_ok(const pa_shape& s) {
+  return s.Hkv % 4 == 0 && s.B <= kLdsMaxB && lds_groups(s.k_type, s.v_type, s.D) > 0;
+}
+
 int32_t check_plan(const pa_plan* p, const char* who) {
   if (!p) return fail(PA_ERR_INVALID, "%s: null plan", who);
   int32_t rc = check_shape(&p->shape, who);
   if (rc) return rc;
   if (p->psize < kTileTokens || p->psize % kTileTokens || p->p_max < 1 || p->grid < 1 ||
-      !(p->scale == p->scale) || p->direct != (p->p_max == 1))
+      !(p->scale == p->scale) || p->direct != (p->p_max == 1) || (p->path != 1 && p->path != 2))
     return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_plan", who);
+  if (p->path == 2 && !lds_path_ok(p->shape))
+    return fail(PA_ERR_UNSUPPORTED, "%s: plan path 2 (LDS-staged kernel) does not take this shape", who);
   return PA_OK;
 }
 
@@ -131,22 +139,33 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
 
   const int64_t L = max_seq_len;
   const int64_t rbk = pa_row_bytes(s.k_type, s.D), rbv = pa_row_bytes(s.v_type, s.D);
+  const bool lds = lds_path_ok(s);
+  // units per (sequence, partition): one per kv head (register kernel) or per
+  // quad of kv heads (LDS-staged kernel)
+  const int64_t per_bp = lds ? s.Hkv / 4 : s.Hkv;
+  const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {
     psize = round_up(partition_tokens, kTileTokens);
   } else if (force_partitions >= 1) {
     psize = round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
+  } else if (lds) {
+    // Occupancy-aware partitioning (lucebox PR #555, Summary). The LDS-staged
+    // kernel runs two workgroups per compute unit and streams at full rate
+    // only when every unit slot is busy, so the batch is cut into about
+    // 2*num_cus equal units (at least 256 tokens each, so a unit's start-up
+    // stays small against its stream). The partial results this adds are
+    // (D+2)*4 bytes per query head per partition, written once and read once.
+    const int64_t units_target = int64_t(num_cus) * 2;
+    psize = std::max<int64_t>(256, round_up(std::max<int64_t>(1, ceil_div(tok * per_bp, units_target)),
+                                            kTileTokens));
   } else {
-    // Occupancy-aware partitioning (lucebox PR #555, Summary): aim for about
-    // four workgroups per compute unit over the whole batch, but never split
+    // Register kernel: about four workgroups per compute unit, but never split
     // so finely that partial results (written and read once more by the merge)
     // exceed ~4% of the K/V bytes of a partition.
-    const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
     const int64_t units_target = int64_t(num_cus) * 4;
-    // the decode kernel's tile: 64 tokens when K and V are both Q4_0, else 32
-    const int64_t tile = (s.k_type == PA_Q4_0 && s.v_type == PA_Q4_0) ? 64 : kTileTokens;
-    const int64_t per_unit = tile * kWavesPerUnit;
-    const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * s.Hkv, units_target)), per_unit);
+    const int64_t per_unit = int64_t(kTileTokens) * kWavesPerUnit;
+    const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * per_bp, units_target)), per_unit);
     const double part_bytes = double(s.Hq) * (s.D + 2) * 4.0 * 2.0;
     const double kv_per_token = double(s.Hkv) * double(rbk + rbv);
     const int64_t floor_tok = round_up(int64_t(std::ceil(part_bytes / (0.04 * kv_per_token))), per_unit);
@@ -158,8 +177,8 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
   const bool direct = p_max == 1;
   int64_t bp_upper = int64_t(s.B) * p_max;
   if (total_tokens > 0) bp_upper = std::min(bp_upper, ceil_div(total_tokens, psize) + s.B);
-  const int64_t units = std::max<int64_t>(1, bp_upper * s.Hkv);
-  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * 8);
+  const int64_t units = std::max<int64_t>(1, bp_upper * per_bp);
+  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * (lds ? 2 : 8));
 
   std::memset(plan, 0, sizeof *plan);
   plan->shape = s;
@@ -170,6 +189,7 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
   plan->grid = int32_t(grid);
   plan->num_cus = num_cus;
   plan->direct = direct ? 1 : 0;
+  plan->path = lds ? 2 : 1;
   plan->ws_bytes = ws_bytes_for(s, int(p_max), direct);
   clear_error();
   return PA_OK;
@@ -208,7 +228,10 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   a.k_type = s.k_type; a.v_type = s.v_type;
   a.direct = plan->direct;
   a.qscale = float(double(plan->scale) * 1.4426950408889634);   // scale * log2(e)
-  hipError_t e = launch_decode(a, static_cast<hipStream_t>(stream));
+  // the LDS-staged kernel's DMA chunks are 16-byte aligned only on aligned pools
+  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) == 0;
+  hipError_t e = plan->path == 2 && aligned ? launch_decode_lds(a, static_cast<hipStream_t>(stream))
+                                            : launch_decode_regs(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   clear_error();
   return PA_OK;

@@ -1,0 +1,376 @@
+// Paged GQA decode attention: the LDS-staged partition kernel.
+//
+// Computes what the register-streaming kernel computes (lucebox PR #555,
+// Summary: for each live (sequence, K/V head, context partition) the r query
+// heads of the group attend over the partition's tokens and write (m, l, o)
+// partials, or the final output in direct mode), organised around how the
+// paged pool sits in HBM:
+//   * One block of the pool holds block_size token slots of all Hkv heads,
+//     so the 16-slot groups of 4 consecutive kv heads are one contiguous run
+//     of 16 * 4 * row_bytes bytes when Hkv == 4 (16 runs of 4 rows otherwise).
+//     A workgroup (4 wave64s) takes a unit (sequence b, partition p, kv-head
+//     quad hg) and wave w serves kv head g = 4*hg + w with its r query heads,
+//     so the four waves consume together exactly what one coalesced stream
+//     of the block brings in.
+//   * K/V bytes move HBM -> LDS with buffer_load_dwordx4 ... lds: every lane
+//     fetches one 16-byte chunk and an instruction lands 1 KB of contiguous
+//     pool bytes (or of 4-row runs) in LDS, without passing through VGPRs.
+//     The block table is resolved once per 16-slot group from an LDS copy of
+//     the partition's block ids; the group address is 64-bit (mlxcel issue
+//     #2153, Proposed Solution).
+//   * A step stages G groups (16*G tokens) of K and V for the four heads; a
+//     ring of two step slots keeps the next step's DMA in flight while the
+//     current one is computed. One barrier per step separates "my DMA of
+//     step s has landed" (s_waitcnt vmcnt(0) by every wave) from "slot s-1
+//     is free" (every wave finished computing it).
+//   * Each wave reads its head's rows from LDS into the same MFMA operand
+//     layouts the register kernel builds from HBM (decode_common.h), then
+//     runs the same scores / exp2 online softmax / PV sequence: 16x16x32
+//     MFMAs for 32-token steps, 16x16x16 for the PV of 16-token steps.
+//   * No cross-wave combine: a wave owns all tokens of its head group, so it
+//     writes its partial (or output) rows directly.
+#include <algorithm>
+
+#include "decode_common.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNidS = 512;     // block ids staged per segment of a partition
+
+template <int KT, int VT, int D>
+struct LdsLayout {
+  static constexpr int RBK = row_bytes_of(KT, D), RBV = row_bytes_of(VT, D);
+  static constexpr int SPK = 4 * RBK, SPV = 4 * RBV;   // one slot's rows of 4 heads
+  static constexpr int CPK = SPK / 16, CPV = SPV / 16; // 16-byte chunks per slot
+  static constexpr int NIK = lds_dma_per_group(KT, D), NIV = lds_dma_per_group(VT, D);
+  static constexpr int G = lds_groups(KT, VT, D);
+  static constexpr int VOFF = G * NIK * 1024;          // V groups follow the K groups
+  static constexpr int SLOT = lds_slot_bytes(KT, VT, D, G);
+  static_assert(SPK % 16 == 0 && SPV % 16 == 0, "4-row runs are whole 16-byte chunks");
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// The workgroup's dynamic LDS (declared at file scope so that the DMA
+// destination below is known to be an LDS address).
+extern __shared__ __align__(16) unsigned char g_lds[];
+
+// One 1 KB DMA instruction: lane l fetches chunk 64*sub + l of a 16-slot
+// group whose slots are CP chunks long and `stride` bytes apart in the pool,
+// starting `head_off` bytes into each slot, and lands it at LDS byte
+// dst + 16*l; chunks past the group read as 0.
+template <int CP>
+__device__ __forceinline__ void dma_chunk(rsrc_t R, uint32_t dst, int sub, int lane, uint32_t stride,
+                                          uint32_t head_off, uint32_t oob) {
+  const int c = 64 * sub + lane;
+  const int slot = c / CP, within = c - slot * CP;
+  const uint32_t voff = c < 16 * CP ? uint32_t(slot) * stride + head_off + 16u * within : oob;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, 0);
+}
+
+template <int KT, int VT, int D>
+__global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArgs a) {
+  using KF = KFmt<KT, D>;
+  using VF = VFmt<VT, D>;
+  using LY = LdsLayout<KT, VT, D>;
+  constexpr int S = D / 32;      // score MFMA steps
+  constexpr int E = D / 16;      // PV d-tiles
+  constexpr int G = LY::G;       // 16-row groups per step
+  constexpr int T = 16 * G;      // tokens per step
+  constexpr int NP = 2 * G;      // V row pairs per lane (4 rows per group)
+
+  unsigned char* const smem = g_lds;
+  unsigned char* ring = smem;
+  int32_t* unit_start = reinterpret_cast<int32_t*>(smem + a.ring_bytes);
+  int32_t* lens = unit_start + (a.B + 1);
+  int32_t* ids = unit_start + (((2 * a.B + 1) + 3) & ~3);
+  float* qs = reinterpret_cast<float*>(ring);          // q staging at unit start
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int m = lane & 15;
+  const int j = lane >> 4;
+
+  live_partition_prefix<kThreads>(a, lens, unit_start, reinterpret_cast<int*>(ring));
+  const int n_bp = __builtin_amdgcn_readfirstlane(unit_start[a.B]);
+  const int HG = a.Hkv / 4;
+  const int n_units = n_bp * HG;
+  const int Gd = gridDim.x;
+
+  // In direct mode no merge follows: an empty sequence's rows are zeroed here.
+  if (a.direct) {
+    for (int b = blockIdx.x; b < a.B; b += Gd) {
+      if (lens[b] != 0) continue;
+      float* o = a.out + int64_t(b) * a.Hq * D;
+      for (int i = tid; i < a.Hq * D; i += kThreads) o[i] = 0.0f;
+    }
+  }
+
+  const int logical = xcd_logical(blockIdx.x, Gd);
+  const uint32_t kstride = uint32_t(a.Hkv) * LY::RBK;  // pool bytes between token slots
+  const uint32_t vstride = uint32_t(a.Hkv) * LY::RBV;
+  const uint32_t ksh = KF::shift(j);
+  const auto vl = VF::lane(m, 0u);
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int seg_tokens = kNidS << a.bs_shift;
+
+  for (int u = logical; u < n_units; u += Gd) {
+    // ---- locate the unit -----------------------------------------------------
+    const int bp = u / HG;
+    const int hg = u - bp * HG;
+    const int b = sequence_of(unit_start, a.B, bp);
+    const int p = bp - __builtin_amdgcn_readfirstlane(unit_start[b]);
+    const int t_begin = p * a.psize;
+    const int t_end = min(__builtin_amdgcn_readfirstlane(lens[b]), t_begin + a.psize);
+    const int g = 4 * hg + wave;                        // this wave's kv head
+    const uint32_t khead = uint32_t(4 * hg) * LY::RBK;  // first head's offset in a slot
+    const uint32_t vhead = uint32_t(4 * hg) * LY::RBV;
+
+    // ---- stage the 4r query rows of the quad (scaled by scale*log2 e) -------
+    __syncthreads();                        // the previous unit is done with the ring
+    {
+      const float* qg = a.q + (int64_t(b) * a.Hq + int64_t(4 * hg) * a.r) * D;
+      for (int i = tid; i < a.r * D; i += kThreads) {
+        float4 v = reinterpret_cast<const float4*>(qg)[i];
+        v.x *= a.qscale; v.y *= a.qscale; v.z *= a.qscale; v.w *= a.qscale;
+        reinterpret_cast<float4*>(qs)[i] = v;
+      }
+    }
+    __syncthreads();
+    // Q operand: column n = lane%16 holds head g*r+n (zero when n >= r)
+    f16x8 qop[S];
+    {
+      const int n = m < a.r ? m : a.r - 1;
+      const float keep = m < a.r ? 1.0f : 0.0f;
+      const float* qw = qs + (wave * a.r + n) * D;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qop[s][i] = f16(qw[KF::dslot(j, s, i)] * keep);
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
+
+    for (int seg_t0 = t_begin; seg_t0 < t_end; seg_t0 += seg_tokens) {
+      const int seg_t1 = min(t_end, seg_t0 + seg_tokens);
+      const int jb0 = seg_t0 >> a.bs_shift;
+      const int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // q staging, ids[] and the ring are free
+      int badl = 0;
+      for (int i = tid; i < nb; i += kThreads) {
+        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
+      }
+      bad |= __syncthreads_or(badl);         // also publishes ids[]
+      const int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
+
+      // ---- DMA of step s into ring slot s&1 (each wave its share) ----------
+      auto issue = [&](int s) __attribute__((always_inline)) {
+        const uint32_t slot = uint32_t(s & 1) * LY::SLOT;   // ring starts at LDS byte 0
+        const int t0 = seg_t0 + s * T;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          const int tg = t0 + 16 * gi;
+          const bool live = tg < seg_t1;
+          const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+          const int slot0 = live ? (tg & bs_mask) : 0;
+          const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
+                                      live ? 16u * kstride : 0u);
+          const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
+                                      live ? 16u * vstride : 0u);
+#pragma unroll
+          for (int sub = 0; sub < LY::NIK; ++sub)
+            if ((gi * LY::NIK + sub) % 4 == wave)
+              dma_chunk<LY::CPK>(kr, slot + (gi * LY::NIK + sub) * 1024, sub, lane, kstride, khead,
+                                 16u * kstride);
+#pragma unroll
+          for (int sub = 0; sub < LY::NIV; ++sub)
+            if ((G * LY::NIK + gi * LY::NIV + sub) % 4 == wave)
+              dma_chunk<LY::CPV>(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, sub, lane, vstride,
+                                 vhead, 16u * vstride);
+        }
+      };
+
+      // ---- compute step s from LDS: scores, online softmax (exp2), PV -------
+      auto compute = [&](int s) __attribute__((always_inline)) {
+        const unsigned char* slot = ring + (s & 1) * LY::SLOT;
+        const int t0 = seg_t0 + s * T;
+        const bool full = t0 + T <= t_end;
+        typename KF::Raw kr[G];
+        typename VF::Raw vr[2 * NP];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+          KF::load_lds(kr[gi], slot + gi * LY::NIK * 1024 + m * LY::SPK + wave * LY::RBK + KF::lane_off(j));
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            VF::load_lds(vr[4 * gi + i],
+                         slot + LY::VOFF + gi * LY::NIV * 1024 + (4 * j + i) * LY::SPV + wave * LY::RBV, vl);
+        if (!full) {
+          // zero V rows past the end so 0 * junk never reaches the PV MFMA
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + 16 * gi + 4 * j + i >= t_end) VF::kill(vr[4 * gi + i]);
+        }
+        f32x4 sc[G];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) sc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) sc[gi] = mfma(KF::op(kr[gi], s2, ksh, mg), qop[s2], sc[gi]);
+        if (!full) {
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + 16 * gi + 4 * j + i >= t_end) sc[gi][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+          mx = fmaxf(mx, fmaxf(fmaxf(sc[gi][0], sc[gi][1]), fmaxf(sc[gi][2], sc[gi][3])));
+        mx = max_over_rows(mx);
+        // Lazy rescale: the reference m only moves when some head's max exceeds
+        // it by more than kSlack (then p <= 2^kSlack, safe in f16); the
+        // lucebox page skips the rescale when the max is unchanged.
+        if (__any(mx > m_run + kSlack)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] *= alpha;
+          m_run = m_new;
+        }
+        float pr[2 * NP];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[4 * gi + i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_run);
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2 * NP; i += 4) ps += (pr[i] + pr[i + 1]) + (pr[i + 2] + pr[i + 3]);
+        typename OpVec<NP>::type pop;
+#pragma unroll
+        for (int i = 0; i < 2 * NP; ++i) pop[i] = f16(pr[i]);
+        auto pv = [&](typename OpVec<NP>::type av, f32x4 c) __attribute__((always_inline)) {
+          if constexpr (NP == 4) return mfma(av, pop, c);
+          else return mfma16(av, pop, c);
+        };
+        if constexpr (VF::kQuant) {
+          uint32_t q[2 * NP][VF::ND];
+          f16x2 dd[NP];
+#pragma unroll
+          for (int i = 0; i < 2 * NP; ++i) VF::realign(vr[i], vl.sh, q[i]);
+#pragma unroll
+          for (int qq = 0; qq < NP; ++qq) dd[qq] = f16x2{vr[2 * qq].d, vr[2 * qq + 1].d};
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op_q<NP>(q, dd, e, mg), acc[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op<NP>(vr, e), acc[e]);
+        }
+        l_run += sum_over_rows(ps);
+      };
+
+      // ---- the ring: DMA of step s+1 in flight while step s is computed ----
+      issue(0);
+      for (int s = 0; s < nsteps; ++s) {
+        // every wave's DMA of step s has landed, and every wave is done with
+        // step s-1 (whose slot the next issue overwrites)
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + 1 < nsteps) issue(s + 1);
+        compute(s);
+      }
+    }
+
+    // ---- partial (or final) rows of the wave's r heads --------------------
+    const int n = m;
+    if (bad && tid == 0) atomicOr(a.status, 1u);
+    if (n < a.r) {
+      const int h = g * a.r + n;
+      const float inv = 1.0f / l_run;
+      float* dst;
+      if (a.direct) {
+        dst = a.out + (int64_t(b) * a.Hq + h) * D;
+      } else {
+        const int64_t row = (int64_t(b) * a.Hq + h) * a.p_max + p;
+        dst = a.part_o + row * D;
+        if (j == 0) {
+          a.part_ml[2 * row] = bad ? __builtin_nanf("") : m_run;
+          a.part_ml[2 * row + 1] = l_run;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = bad ? __builtin_nanf("") : acc[e][i] * inv;
+    }
+  }
+}
+
+// LDS bytes of a launch: the ring (or the q staging of 4r rows, if larger),
+// then unit_start[B+1] | lens[B] | pad | ids[kNidS+1] (a segment of kNidS
+// blocks' worth of tokens that starts inside a block touches kNidS+1 blocks).
+template <int KT, int VT, int D>
+size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
+  using LY = LdsLayout<KT, VT, D>;
+  const size_t ring = std::max<size_t>(2 * LY::SLOT, size_t(16) * a.r * D);
+  *ring_bytes = int((ring + 15) & ~size_t(15));
+  return size_t(*ring_bytes) + 4 * size_t(((2 * a.B + 1) + 3) & ~3) + 4 * size_t((kNidS + 1 + 3) & ~3);
+}
+
+template <int KT, int VT, int D>
+hipError_t launch_typed(const DecodeArgs& a0, hipStream_t stream) {
+  if constexpr (lds_groups(KT, VT, D) == 0) {
+    return hipErrorInvalidValue;
+  } else {
+    DecodeArgs a = a0;
+    const size_t lds = lds_bytes<KT, VT, D>(a, &a.ring_bytes);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_lds_kernel<KT, VT, D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 81920);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((decode_lds_kernel<KT, VT, D>), dim3(a.grid), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  switch (a.k_type * 3 + a.v_type) {
+    case 0: return launch_typed<kF16, kF16, D>(a, s);
+    case 1: return launch_typed<kF16, kQ8_0, D>(a, s);
+    case 2: return launch_typed<kF16, kQ4_0, D>(a, s);
+    case 3: return launch_typed<kQ8_0, kF16, D>(a, s);
+    case 4: return launch_typed<kQ8_0, kQ8_0, D>(a, s);
+    case 5: return launch_typed<kQ8_0, kQ4_0, D>(a, s);
+    case 6: return launch_typed<kQ4_0, kF16, D>(a, s);
+    case 7: return launch_typed<kQ4_0, kQ8_0, D>(a, s);
+    case 8: return launch_typed<kQ4_0, kQ4_0, D>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_lds(const DecodeArgs& a, hipStream_t stream) {
+  if (a.Hkv % 4 || a.B > kLdsMaxB) return hipErrorInvalidValue;
+  if (a.D == 256) return launch_d<256>(a, stream);
+  if (a.D == 128) return launch_d<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

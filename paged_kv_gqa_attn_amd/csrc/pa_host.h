@@ -31,9 +31,33 @@ struct DecodeArgs {
   int32_t k_type, v_type;
   int32_t direct;
   float qscale;            // scale * log2(e)
+  int32_t ring_bytes;      // LDS-staged kernel: bytes of the K/V ring (set by its launcher)
 };
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Decode kernels: register streaming (any supported shape) and LDS staged
+// (the shapes lds_groups() admits, Hkv % 4 == 0, B <= kLdsMaxB, pools
+// 16-byte aligned).
+hipError_t launch_decode_regs(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_lds(const DecodeArgs& a, hipStream_t stream);
+
+// Geometry of the LDS-staged kernel, shared by the planner and the kernel.
+// One step stages, for the four kv heads of a workgroup, G groups of 16
+// token slots of K and of V (one 16-byte DMA chunk per lane, 1 KB per
+// instruction) into one of two ring slots of at most kLdsSlotMax bytes.
+constexpr int kLdsSlotMax = 36864;
+constexpr int kLdsMaxB = 256;
+constexpr int lds_row_bytes(int type, int D) {
+  return type == PA_F16 ? 2 * D : (type == PA_Q8_0 ? 34 * (D / 32) : 18 * (D / 32));
+}
+// 1 KB DMA instructions that stage 16 slots x 4 heads of one side.
+constexpr int lds_dma_per_group(int type, int D) { return (16 * 4 * lds_row_bytes(type, D) + 1023) / 1024; }
+constexpr int lds_slot_bytes(int kt, int vt, int D, int G) {
+  return G * 1024 * (lds_dma_per_group(kt, D) + lds_dma_per_group(vt, D));
+}
+// 16-slot groups per step (2, else 1), or 0 when one group does not fit.
+constexpr int lds_groups(int kt, int vt, int D) {
+  return lds_slot_bytes(kt, vt, D, 2) <= kLdsSlotMax ? 2 : (lds_slot_bytes(kt, vt, D, 1) <= kLdsSlotMax ? 1 : 0);
+}
 
 struct MergeArgs {
   const float* part_o;

@@ -24,10 +24,28 @@ def shape_for(case):
                        case.max_blocks, case.k_fmt, case.v_fmt)
 
 
-def plan_for(case, **kw):
+def lds_path_ok(case):
+    """Whether the LDS-staged decode kernel (plan path 2) takes the case's shape:
+    quads of kv heads, B <= 256, and one 16-slot group of K and V of four heads
+    in a 36 KB ring slot (so no F16 side at D=256)."""
+    rb = {"f16": 2 * case.D, "q8_0": 34 * case.D // 32, "q4_0": 18 * case.D // 32}
+    per_group = sum(-(-16 * 4 * rb[f] // 1024) for f in (case.k_fmt, case.v_fmt)) * 1024
+    return case.Hkv % 4 == 0 and case.B <= 256 and per_group <= 36864
+
+
+def plan_for(case, path=None, **kw):
+    """paged_attn_plan for the case; path=1/2 forces the decode kernel (a case
+    the LDS-staged kernel does not take is skipped for path 2)."""
+    import pytest
     pa = pa_mod()
     kw.setdefault("total_tokens", sum(case.seq_lens))
-    return pa.paged_attn_plan(shape_for(case), max(max(case.seq_lens), 0), **kw)
+    plan = pa.paged_attn_plan(shape_for(case), max(max(case.seq_lens), 0), **kw)
+    assert plan.path == (2 if lds_path_ok(case) else 1)
+    if path is not None:
+        if path == 2 and not lds_path_ok(case):
+            pytest.skip("the LDS-staged kernel does not take this shape")
+        plan.path = path
+    return plan
 
 
 def run(case_dev, plan, table="case", ws=None, canary=0):

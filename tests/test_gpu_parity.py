@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 PAIRS = [(k, v) for k in synth.FORMATS for v in synth.FORMATS]
+PATHS = [1, 2]      # decode kernel: register-streaming, LDS-staged
 
 
 def _case(lens, **kw):
@@ -34,9 +35,10 @@ def test_tiny_f16_workload_all_partitionings():
         assert pa_mod().paged_attn_status(ws) == 0
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("D", [256, 128])
 @pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
-def test_nine_type_pairs(pair, D):
+def test_nine_type_pairs(pair, D, path):
     k_fmt, v_fmt = pair
     Hq, Hkv = (24, 4) if D == 256 else (32, 8)
     lens = [200, 1, 16, 17, 33, 0, 95]
@@ -44,18 +46,19 @@ def test_nine_type_pairs(pair, D):
                  seed=7 + D + 3 * synth.FORMATS.index(k_fmt) + synth.FORMATS.index(v_fmt))
     g = case.to(DEV)
     for force in (1, 3):
-        out, _ = run(g, plan_for(case, force_partitions=force))
+        out, _ = run(g, plan_for(case, path=path, force_partitions=force))
         check_parity(case, out)
         assert np.all(out[5].cpu().numpy() == 0.0), "empty sequence must give a zero row"
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("L", [1, 15, 16, 17, 31, 32, 33, 64, 65, 200, 511, 1000])
 @pytest.mark.parametrize("bs", [16, 32])
-def test_block_boundaries(L, bs):
+def test_block_boundaries(L, bs, path):
     case = _case([L, L + 1], block_size=bs, k_fmt="q4_0", v_fmt="q8_0", seed=L * 3 + bs)
     g = case.to(DEV)
     for force in (0, 1, 2):
-        out, _ = run(g, plan_for(case, force_partitions=force))
+        out, _ = run(g, plan_for(case, path=path, force_partitions=force))
         check_parity(case, out)
 
 
@@ -91,16 +94,17 @@ def test_gather_bit_exact_paged_and_contiguous():
             assert torch.equal(dst.cpu(), flat[rows])
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("pair", [("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "q4_0")])
-def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
+def test_paged_equals_contiguous_bitwise_and_deterministic(pair, path):
     case = _case([700, 333, 1, 64], k_fmt=pair[0], v_fmt=pair[1], seed=11)
     cc = synth.contiguous_copy(case)
     g, gc = case.to(DEV), cc.to(DEV)
     for force in (0, 1, 3):
-        plan = plan_for(case, force_partitions=force)
+        plan = plan_for(case, path=path, force_partitions=force)
         out_p, _ = run(g, plan)
         out_p2, _ = run(g, plan)
-        plan_c = plan_for(cc, force_partitions=force)
+        plan_c = plan_for(cc, path=path, force_partitions=force)
         assert plan_c.psize == plan.psize
         out_c, _ = run(gc, plan_c, table=None)
         assert torch.equal(out_p, out_p2), "repeated runs differ"
@@ -108,9 +112,10 @@ def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
         check_parity(case, out_p)
 
 
-def test_bad_block_id_sets_status_and_nans_only_that_sequence():
+@pytest.mark.parametrize("pair", [("f16", "q4_0"), ("q4_0", "q8_0")])
+def test_bad_block_id_sets_status_and_nans_only_that_sequence(pair):
     pa = pa_mod()
-    case = _case([100, 64, 40], k_fmt="f16", v_fmt="q4_0", seed=13)
+    case = _case([100, 64, 40], k_fmt=pair[0], v_fmt=pair[1], seed=13)
     g = case.to(DEV)
     for force in (1, 0, 3):
         plan = plan_for(case, force_partitions=force)
@@ -148,9 +153,10 @@ def pa_run_with_seq_len(g, plan, sl):
     return out, ws
 
 
+@pytest.mark.parametrize("pair", [("q4_0", "f16"), ("q8_0", "q4_0")])
 @pytest.mark.parametrize("junk", ["nan", "big", "random"])
-def test_junk_in_dead_slots_never_leaks(junk):
-    case = _case([33, 17, 1, 250], k_fmt="q4_0", v_fmt="f16", seed=19, junk=junk)
+def test_junk_in_dead_slots_never_leaks(junk, pair):
+    case = _case([33, 17, 1, 250], k_fmt=pair[0], v_fmt=pair[1], seed=19, junk=junk)
     g = case.to(DEV)
     for force in (0, 1, 2):
         out, _ = run(g, plan_for(case, force_partitions=force))
@@ -185,11 +191,12 @@ def test_merge_kernel_on_oracle_partials():
     assert np.all(out[1].cpu().numpy() == 0.0)
 
 
-def test_workspace_canary_untouched():
+@pytest.mark.parametrize("path", PATHS)
+def test_workspace_canary_untouched(path):
     case = _case([1000, 517, 3], k_fmt="q4_0", v_fmt="q4_0", seed=29)
     g = case.to(DEV)
     for force in (0, 1, 5):
-        plan = plan_for(case, force_partitions=force)
+        plan = plan_for(case, path=path, force_partitions=force)
         out, ws = run(g, plan, canary=4096)
         tail = ws[int(plan.ws_bytes):].cpu()
         assert torch.all(tail == 0xA5), "decode or merge wrote past plan.ws_bytes"
@@ -209,26 +216,25 @@ def test_red_control_wrong_table_fails_parity():
     assert float(rel_err_rows(out.cpu().double().numpy(), ref).max()) > 1e-2
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("pair,std", [(("q4_0", "q4_0"), 400.0), (("q4_0", "f16"), 400.0),
                                       (("f16", "q4_0"), 400.0), (("q8_0", "q8_0"), 5000.0),
                                       (("q8_0", "q4_0"), 5000.0)])
-def test_large_block_scales_use_the_exact_conversion(pair, std):
-    """Block scales |d| >= 64 (live rows) cannot use the fma-form conversion
-    (-1024*d is not a finite f16); the kernel must recompute with the exact
-    form and still match the oracle. q shrinks as K grows so the logits stay
-    O(1), as in real attention (with f16 operands, logit error grows with
-    |q|*|k|)."""
+def test_large_block_scales(pair, std, path):
+    """Block scales far from O(1) (|d| in the hundreds to thousands, values up
+    to ~1e4): the dequantisation must stay exact up to its one f16 rounding.
+    q shrinks as K grows so the logits stay O(1), as in real attention (with
+    f16 operands, logit error grows with |q|*|k|)."""
     case = _case([300, 77, 1000], k_fmt=pair[0], v_fmt=pair[1], seed=41, value_std=std,
                  q_std=min(1.0, 4.0 / std))
     g = case.to(DEV)
     for force in (0, 1, 3):
-        out, _ = run(g, plan_for(case, force_partitions=force))
+        out, _ = run(g, plan_for(case, path=path, force_partitions=force))
         check_parity(case, out)
 
 
 def test_mixed_scales_within_one_sequence():
-    """Large-scale rows only in part of the context: the waves that meet them
-    recompute, the others keep the fast form."""
+    """Large-scale rows only in part of the context, next to O(1) rows."""
     case = _case([2000, 500], k_fmt="q4_0", v_fmt="q4_0", seed=43)
     big = synth.make_case([2000, 500], k_fmt="q4_0", v_fmt="q4_0", seed=43, value_std=500.0,
                           nblocks=case.nblocks)

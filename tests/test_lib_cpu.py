@@ -91,15 +91,58 @@ def test_plan_automatic_partitions_for_long_context():
 
 
 def test_plan_partial_traffic_floor_and_direct_mode():
-    # a short batch: the partial-traffic floor forces one partition -> direct
+    # a short batch: one partition covers it -> direct
     p = pa.paged_attn_plan(_shape(B=1), 200, num_cus=256)
     assert p.direct == 1 and p.p_max == 1 and p.ws_bytes == 256
     assert p.psize >= 200
-    # the floor keeps partials under ~4% of the K/V bytes of a partition
-    p = pa.paged_attn_plan(_shape(), 32768, total_tokens=8 * 32768, num_cus=256)
-    part = 24 * (256 + 2) * 4 * 2
-    kv = p.psize * 4 * (144 + 144)
+    # register kernel (Hkv not a multiple of 4): the floor keeps partials
+    # under ~4% of the K/V bytes of a partition
+    p = pa.paged_attn_plan(_shape(Hq=12, Hkv=2), 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.path == 1
+    part = 12 * (256 + 2) * 4 * 2
+    kv = p.psize * 2 * (144 + 144)
     assert part / kv <= 0.04 + 1e-9
+
+
+def test_plan_lds_path_fills_two_workgroups_per_cu():
+    for L in (32768, 131072):
+        p = pa.paged_attn_plan(_shape(), L, total_tokens=8 * L, num_cus=256)
+        assert p.path == 2 and p.grid == 512
+        units = 8 * -(-L // p.psize)           # one unit per (sequence, partition) at Hkv = 4
+        assert 480 <= units <= 512
+    lens = [131072] + [8192] * 7
+    p = pa.paged_attn_plan(_shape(), max(lens), total_tokens=sum(lens), num_cus=256)
+    units = sum(-(-L // p.psize) for L in lens)
+    assert p.path == 2 and units <= 512 and p.psize >= 256
+
+
+@pytest.mark.parametrize("kw,path", [
+    (dict(), 2),                                   # Q4_0/Q4_0, D=256, Hkv=4
+    (dict(k_type="q8_0", v_type="q8_0"), 2),
+    (dict(k_type="f16", v_type="f16"), 1),         # a 16-slot group of 4 F16 rows of D=256 is too big
+    (dict(k_type="f16", v_type="q4_0"), 1),
+    (dict(k_type="f16", v_type="f16", D=128, Hq=32, Hkv=8), 2),
+    (dict(Hq=12, Hkv=2), 1),                       # no quad of kv heads
+    (dict(Hq=24, Hkv=8), 2),
+    (dict(B=300), 1),                              # batch prefix beyond the LDS budget
+])
+def test_plan_picks_the_decode_kernel(kw, path):
+    p = pa.paged_attn_plan(_shape(**kw), 4096, num_cus=256)
+    assert p.path == path
+
+
+def test_plan_path_two_refused_where_the_shape_does_not_fit():
+    p = pa.paged_attn_plan(_shape(k_type="f16", v_type="f16"), 4096, num_cus=256)
+    p.path = 2
+    fake = 0x1000
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_decode(p, fake, fake, fake, fake, fake, fake, out=fake, stream=0,
+                             ws_bytes=int(p.ws_bytes))
+    assert e.value.code == pa.PA_ERR_UNSUPPORTED and "path 2" in str(e.value)
+    p.path = 3
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_merge(p, fake, fake, fake, stream=0, ws_bytes=int(p.ws_bytes))
+    assert e.value.code == pa.PA_ERR_INVALID
 
 
 def test_plan_forced_partitions_and_tokens():
