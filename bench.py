@@ -52,12 +52,16 @@ WORKLOADS = {
     "slab_f16": ("slab_f16", 8, 65536, "F16 D=128 Hq=32 Hkv=8 bs=32 B=8 L=65536, pool past 2^32 elements"),
 }
 DEFAULT = "uniform_q4_0_128k_b8"
-DECODE_SRC = os.path.join(ROOT, "paged_kv_gqa_attn_amd", "csrc", "decode.hip")
+
+
+DECODE_KERNELS = ("decode_kernel", "decode_lds_kernel")
 
 
 def source_hash() -> str:
+    """Hash of the decode kernels' sources: counter summaries taken on other
+    sources are not used for `traffic`."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "pa_device.h", "pa_host.h"):
+    for name in ("decode.hip", "decode_lds.hip", "decode_common.h", "pa_device.h", "pa_host.h"):
         with open(os.path.join(ROOT, "paged_kv_gqa_attn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -225,7 +229,8 @@ def run_bench(args):
             "B": c0.B, "Hq": c0.Hq, "Hkv": c0.Hkv, "D": c0.D, "block_size": c0.block_size,
             "k_type": c0.k_fmt, "v_type": c0.v_fmt, "seq_lens": sorted(set(c0.seq_lens)),
             "live_tokens": sum(c0.seq_lens), "psize": plan.psize, "p_max": plan.p_max,
-            "grid": plan.grid, "pool_copies": len(cases),
+            "grid": plan.grid, "decode_kernel": DECODE_KERNELS[plan.path - 1],
+            "pool_copies": len(cases),
             "step_us_median_events": round(med * 1e3, 2),
             "decode_us_mean": round(dec_avg * 1e3, 2),
             "merge_us_mean": round(sum(mrg_ms) / len(mrg_ms) * 1e3, 2),
@@ -264,12 +269,19 @@ def summarize_stats(d, label, cmd):
         raise SystemExit(f"no kernel_stats.csv under {d}")
     lines = [f"# rocprofv3 kernel statistics: {label}", f"# command: {cmd}",
              f"# source_hash = {source_hash()}",
+             "# library kernels (the rest is the benchmark's input generation in torch)",
              "# name | calls | total_ns | average_ns | min_ns | max_ns | percent"]
+    other_calls, other_ns = 0, 0
     for r in rows:
         nm = r.get("Name", r.get("KernelName", "?"))
+        if "pa::" not in nm:
+            other_calls += int(r.get("Calls", "0") or 0)
+            other_ns += int(float(r.get("TotalDurationNs", "0") or 0))
+            continue
         lines.append(" | ".join([nm[:110], r.get("Calls", ""), r.get("TotalDurationNs", ""),
                                  r.get("AverageNs", ""), r.get("MinNs", ""), r.get("MaxNs", ""),
                                  r.get("Percentage", "")]))
+    lines.append(f"# other kernels: {other_calls} calls, {other_ns} ns in total")
     out = os.path.join(ROOT, "profiles", f"decode_{label}_stats.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -291,9 +303,9 @@ def summarize_pmc(d, label, cmd, calib_bytes):
                 per[(nm, did)][cn] += val
     if not per:
         raise SystemExit(f"no counter_collection.csv under {d}")
-    dec = [v for (nm, _), v in per.items() if "decode_kernel" in nm]
-    cpy = [v for (nm, _), v in per.items() if "decode_kernel" not in nm and "merge" not in nm
-           and "gather" not in nm]
+    dec = [v for (nm, _), v in per.items() if any(k in nm for k in DECODE_KERNELS)]
+    cpy = [v for (nm, _), v in per.items() if not any(k in nm for k in DECODE_KERNELS)
+           and "merge" not in nm and "gather" not in nm]
     lines = [f"# rocprofv3 counters: {label}", f"# command: {cmd}", f"source_hash = {source_hash()}"]
     result = {}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):

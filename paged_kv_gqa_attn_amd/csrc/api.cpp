@@ -153,12 +153,15 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
     // Occupancy-aware partitioning (lucebox PR #555, Summary). The LDS-staged
     // kernel runs two workgroups per compute unit and streams at full rate
     // only when every unit slot is busy, so the batch is cut into about
-    // 2*num_cus equal units (at least 256 tokens each, so a unit's start-up
-    // stays small against its stream). The partial results this adds are
-    // (D+2)*4 bytes per query head per partition, written once and read once.
+    // 2*num_cus equal units (at least 64 tokens each: two steps of the ring).
+    // The partial results this adds are (D+2)*4 bytes per query head per
+    // partition, written once and read once.
+    // Sequences of at most 256 tokens stay in one partition: splitting them
+    // saves less decode time than the merge launch costs.
     const int64_t units_target = int64_t(num_cus) * 2;
-    psize = std::max<int64_t>(256, round_up(std::max<int64_t>(1, ceil_div(tok * per_bp, units_target)),
-                                            kTileTokens));
+    psize = std::max<int64_t>(64, round_up(std::max<int64_t>(1, ceil_div(tok * per_bp, units_target)),
+                                           kTileTokens));
+    if (L <= 256) psize = L;
   } else {
     // Register kernel: about four workgroups per compute unit, but never split
     // so finely that partial results (written and read once more by the merge)

@@ -113,7 +113,7 @@ def test_plan_lds_path_fills_two_workgroups_per_cu():
     lens = [131072] + [8192] * 7
     p = pa.paged_attn_plan(_shape(), max(lens), total_tokens=sum(lens), num_cus=256)
     units = sum(-(-L // p.psize) for L in lens)
-    assert p.path == 2 and units <= 512 and p.psize >= 256
+    assert p.path == 2 and units <= 512 and p.psize >= 64
 
 
 @pytest.mark.parametrize("kw,path", [
