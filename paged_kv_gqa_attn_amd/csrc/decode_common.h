@@ -58,6 +58,50 @@ __device__ __forceinline__ f16x2 nib_pair_to_f16(uint32_t w_shifted, f16x2 d2, u
   return (bitcast<f16x2>(v) - f16x2{1032.0f16, 1032.0f16}) * d2;
 }
 
+// Nibble value times scale, offset left out: n*d from x = 1024 + n (the
+// magic-number f16). Two forms of the same single rounding of n*d:
+//   fma form:   fma(x, d, -1024*d) - the product and the subtraction are exact
+//               inside the FMA; needs -1024*d finite, i.e. |d| < 64;
+//   exact form: (x - 1024) * d - the subtraction is exact.
+// The format offset (-8 for Q4_0) is added back once per block by a
+// correction term, so both forms give bit-identical results.
+template <bool FMA>
+__device__ __forceinline__ f16x2 nd_pair(uint32_t w_shifted, f16x2 d2, f16x2 c2, uint32_t mg) {
+  const f16x2 x = bitcast<f16x2>(and_or(w_shifted, 0x000F000Fu, mg));
+  if constexpr (FMA) return __builtin_elementwise_fma(x, d2, c2);
+  else return (x - f16x2{1024.0f16, 1024.0f16}) * d2;
+}
+// The same in place for both nibbles of bytes 0 and 2 of w (no shift): the low
+// nibble gives n*d, the high nibble, taken under the mask 0x00F000F0, reads as
+// 1024 + 16n and gives 16*n*d - the "x16 frame", undone by the consumer (q/16
+// for K, 1/16 on the output columns for V). fma form only: |d| < 64 keeps
+// -1024*d finite and 16*15*|d| inside the f16 range.
+__device__ __forceinline__ f16x2 nd_lo(uint32_t w, f16x2 d2, f16x2 c2, uint32_t mg) {
+  return __builtin_elementwise_fma(bitcast<f16x2>(and_or(w, 0x000F000Fu, mg)), d2, c2);
+}
+__device__ __forceinline__ f16x2 nd_hi16(uint32_t w, f16x2 d2, f16x2 c2, uint32_t mg) {
+  return __builtin_elementwise_fma(bitcast<f16x2>(and_or(w, 0x00F000F0u, mg)), d2, c2);
+}
+// Power-of-two shift k >= 0 that brings |d| below 64 (d * 2^-k keeps -1024*d
+// finite for the fma form), from the f16 exponent field: 64 has field 21.
+__device__ __forceinline__ int scale_shift(f16 d) {
+  const int e = int((bitcast<uint16_t>(d) & 0x7FFFu) >> 10);
+  return e > 20 ? e - 20 : 0;
+}
+// 2^-k as an f16 pair (0 <= k <= 11; exact).
+__device__ __forceinline__ f16x2 pow2_neg_f16x2(int k) {
+  const uint32_t h = uint32_t(15 - k) << 10;
+  return bitcast<f16x2>(h | (h << 16));
+}
+// Largest k of the wave, given each lane's k (usually all zero; the loop over
+// thresholds only runs when some lane needs a shift).
+__device__ __forceinline__ int wave_max_shift(int k) {
+  if (!__any(k > 0)) return 0;
+  for (int t = 11; t > 1; --t)
+    if (__any(k >= t)) return t;
+  return 1;
+}
+
 __device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
@@ -179,6 +223,20 @@ template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
   using B = KQuantBase<kQ4_0, D>;
   using typename B::Raw;
   static constexpr int NBL = D / 128;
+  __device__ static f16 dscale(const Raw& r, int blk, uint32_t sh) { return B::half_at(r, 18 * blk, sh); }
+  // op without the -8 offset and with the high nibbles in the x16 frame (see
+  // nd_hi16): slots 0, 1, 4, 5 hold n*d', slots 2, 3, 6, 7 hold 16*n*d', for
+  // the same elements as op; d2[blk] = (d', d') the lane's block scale
+  // (|d'| < 64, possibly pre-scaled by a power of two), c2[blk] = -1024*d'.
+  __device__ static f16x8 op_n16(const Raw& r, int s, uint32_t sh, uint32_t mg, const f16x2* d2,
+                                 const f16x2* c2) {
+    const int blk = s / 4, c = s % 4;
+    const uint32_t w = B::dw(r, 18 * blk + 2 + 4 * c, sh);
+    const uint32_t w8 = w >> 8;
+    return pack8(nd_lo(w, d2[blk], c2[blk], mg), nd_hi16(w, d2[blk], c2[blk], mg),
+                 nd_lo(w8, d2[blk], c2[blk], mg), nd_hi16(w8, d2[blk], c2[blk], mg));
+  }
+  __host__ __device__ static bool hi_slot(int i) { return (i & 2) != 0; }
   // step s: block s/4, nibble bytes 4c..4c+3 (c = s%4) -> elements
   // 4c, 4c+2, 16+4c, 18+4c, 4c+1, 4c+3, 17+4c, 19+4c.
   __device__ static f16x8 op(const Raw& r, int s, uint32_t sh, uint32_t mg) {
@@ -320,6 +378,24 @@ template <int D> struct VFmt<kQ8_0, D> : VQuantBase<kQ8_0, D> {
 
 template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
   using B = VQuantBase<kQ4_0, D>;
+  // op_q without the -8 offset and with the high-nibble columns (e >= QB) in
+  // the x16 frame (see nd_hi16); dd[p] = scales with |d'| < 64, cc[p] = -1024*dd[p].
+  template <int NP>
+  __device__ static typename OpVec<NP>::type op_n16(const uint32_t (*q)[B::ND], const f16x2* dd,
+                                                    const f16x2* cc, int e, uint32_t mg) {
+    const bool hi = e >= B::QB;
+    const int byte = hi ? e - B::QB : e;
+    const int k = byte % 4, i = byte / 4;
+    const uint32_t sel = uint32_t(k) | (0x0Cu << 8) | (uint32_t(4 + k) << 16) | (0x0Cu << 24);
+    f16x2 o[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t x = perm_bytes(q[2 * p + 1][i], q[2 * p][i], sel);
+      o[p] = hi ? nd_hi16(x, dd[p], cc[p], mg) : nd_lo(x, dd[p], cc[p], mg);
+    }
+    return OpVec<NP>::pack(o);
+  }
+  __host__ __device__ static bool hi_col(int e) { return e >= B::QB; }
   // e < QB: low nibble of quant byte e; e >= QB: high nibble of byte e-QB.
   __host__ __device__ static int dv(int m, int e) {
     const int qidx = m * B::QB;

@@ -30,6 +30,7 @@
 //   * No cross-wave combine: a wave owns all tokens of its head group, so it
 //     writes its partial (or output) rows directly.
 #include <algorithm>
+#include <type_traits>
 
 #include "decode_common.h"
 
@@ -48,7 +49,18 @@ struct LdsLayout {
   static constexpr int G = lds_groups(KT, VT, D);
   static constexpr int VOFF = G * NIK * 1024;          // V groups follow the K groups
   static constexpr int SLOT = lds_slot_bytes(KT, VT, D, G);
+  static constexpr int R = lds_ring_slots(KT, VT, D);   // ring slots
+  static constexpr int NI = G * (NIK + NIV);           // DMA instructions per step
+  static constexpr int NIW = (NI + 3) / 4;             // at most this many per wave
   static_assert(SPK % 16 == 0 && SPV % 16 == 0, "4-row runs are whole 16-byte chunks");
+};
+
+// x16-frame slots / columns of the Q4_0 conversions (none for other formats).
+template <int KT, int D> struct KFmtHi {
+  __host__ __device__ static constexpr bool hi(int i) { return KT == kQ4_0 && (i & 2) != 0; }
+};
+template <int VT, int D> struct VFmtHi {
+  __host__ __device__ static constexpr bool hi(int e) { return VT == kQ4_0 && e >= (D / 16) / 2; }
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -57,17 +69,56 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // destination below is known to be an LDS address).
 extern __shared__ __align__(16) unsigned char g_lds[];
 
-// One 1 KB DMA instruction: lane l fetches chunk 64*sub + l of a 16-slot
-// group whose slots are CP chunks long and `stride` bytes apart in the pool,
-// starting `head_off` bytes into each slot, and lands it at LDS byte
-// dst + 16*l; chunks past the group read as 0.
-template <int CP>
-__device__ __forceinline__ void dma_chunk(rsrc_t R, uint32_t dst, int sub, int lane, uint32_t stride,
-                                          uint32_t head_off, uint32_t oob) {
+// LDS placement of the four head rows of a slot. Within slot t, head w's row
+// is stored at row position (w + rot(t)) mod 4, so that the 64 lanes of a
+// wave, which read the same head from 16 slots (K) or 4 slots (V) at once,
+// spread over the LDS banks (a plain copy puts 16 K rows 576 bytes apart on
+// the same few banks). Only rows made of whole 16-byte chunks can be moved
+// this way (row_bytes % 16 == 0); other rows keep rot = 0.
+template <int RB> struct RowRot {
+  static constexpr bool on = RB % 16 == 0;
+  __device__ static int k(int t) { return on ? (t >> 2) & 3 : 0; }          // K: 16 slots
+  __device__ static int v(int t) { return on ? ((t >> 2) & 1) << 1 : 0; }   // V: 4 slots
+};
+
+// Pool offset of the chunk lane l fetches in the 1 KB DMA instruction `sub`
+// of a 16-slot group: LDS chunk 64*sub + l of a group whose slots are CP
+// chunks (four rows of RB bytes) long in LDS and `stride` bytes apart in the
+// pool, starting `head_off` bytes into each pool slot, rows placed by `rot`;
+// chunks past the group get `oob` (reads as 0).
+template <int CP, int RB>
+__device__ __forceinline__ uint32_t chunk_voff(int sub, int lane, uint32_t stride, uint32_t head_off,
+                                               uint32_t oob, int (*rot)(int)) {
   const int c = 64 * sub + lane;
-  const int slot = c / CP, within = c - slot * CP;
-  const uint32_t voff = c < 16 * CP ? uint32_t(slot) * stride + head_off + 16u * within : oob;
+  const int slot = c / CP;
+  int within = c - slot * CP;
+  if constexpr (RowRot<RB>::on) {
+    constexpr int CPR = RB / 16;                       // chunks per row
+    const int hp = within / CPR;                       // row position in LDS
+    within += (((hp - rot(slot)) & 3) - hp) * CPR;     // the pool row stored there
+  }
+  return c < 16 * CP ? uint32_t(slot) * stride + head_off + 16u * within : oob;
+}
+
+// One DMA instruction: every lane fetches 16 bytes at its offset and the
+// wave lands them as 1 KB at LDS byte dst + 16*lane.
+__device__ __forceinline__ void dma16(rsrc_t R, uint32_t dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n wave-uniform, at most 15; larger n waits for more
+// than needed, which is safe) followed by the workgroup barrier. The asm
+// memory clobber keeps every LDS read of the step after the barrier.
+__device__ __forceinline__ void wait_dma_then_barrier(int n) {
+#define PA_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")\n\ts_barrier" ::: "memory"); break;
+  switch (n < 15 ? n : 15) {
+    PA_WAIT_CASE(0) PA_WAIT_CASE(1) PA_WAIT_CASE(2) PA_WAIT_CASE(3) PA_WAIT_CASE(4)
+    PA_WAIT_CASE(5) PA_WAIT_CASE(6) PA_WAIT_CASE(7) PA_WAIT_CASE(8) PA_WAIT_CASE(9)
+    PA_WAIT_CASE(10) PA_WAIT_CASE(11) PA_WAIT_CASE(12) PA_WAIT_CASE(13) PA_WAIT_CASE(14)
+    default: asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory"); break;
+  }
+#undef PA_WAIT_CASE
 }
 
 template <int KT, int VT, int D>
@@ -80,6 +131,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   constexpr int G = LY::G;       // 16-row groups per step
   constexpr int T = 16 * G;      // tokens per step
   constexpr int NP = 2 * G;      // V row pairs per lane (4 rows per group)
+  constexpr bool kKFold = KT == kQ4_0;   // Q4_0 offsets folded into corrections
+  constexpr bool kVFold = VT == kQ4_0;
+  constexpr int KF_NBL = kKFold ? D / 128 : 1;   // ggml blocks per K lane window
 
   unsigned char* const smem = g_lds;
   unsigned char* ring = smem;
@@ -110,6 +164,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   }
 
   const int logical = xcd_logical(blockIdx.x, Gd);
+  const int cw = (LY::NI - wave + 3) / 4;              // DMA instructions this wave issues per step
+  // LDS offsets (within a group) of the rows this lane reads: K row m, V rows
+  // 4j+i, of the wave's head, at their rotated row positions
+  const int k_row = m * LY::SPK + ((wave + RowRot<LY::RBK>::k(m)) & 3) * LY::RBK + int(KF::lane_off(j));
+  int v_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v_row[i] = (4 * j + i) * LY::SPV + ((wave + RowRot<LY::RBV>::v(4 * j + i)) & 3) * LY::RBV;
   const uint32_t kstride = uint32_t(a.Hkv) * LY::RBK;  // pool bytes between token slots
   const uint32_t vstride = uint32_t(a.Hkv) * LY::RBV;
   const uint32_t ksh = KF::shift(j);
@@ -129,6 +191,19 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     const int g = 4 * hg + wave;                        // this wave's kv head
     const uint32_t khead = uint32_t(4 * hg) * LY::RBK;  // first head's offset in a slot
     const uint32_t vhead = uint32_t(4 * hg) * LY::RBV;
+    // this lane's pool offset in each DMA instruction q = wave + 4i of a step
+    // (the same for every step: only the group base changes)
+    uint32_t dvoff[LY::NIW];
+#pragma unroll
+    for (int i = 0; i < LY::NIW; ++i) {
+      const int q = wave + 4 * i;
+      if (q < G * LY::NIK)
+        dvoff[i] = chunk_voff<LY::CPK, LY::RBK>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
+                                                 RowRot<LY::RBK>::k);
+      else
+        dvoff[i] = chunk_voff<LY::CPV, LY::RBV>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
+                                                 16u * vstride, RowRot<LY::RBV>::v);
+    }
 
     // ---- stage the 4r query rows of the quad (scaled by scale*log2 e) -------
     __syncthreads();                        // the previous unit is done with the ring
@@ -150,13 +225,33 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 #pragma unroll
       for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qop[s][i] = f16(qw[KF::dslot(j, s, i)] * keep);
+        for (int i = 0; i < 8; ++i) {
+          // Q4_0: the high-nibble slots meet K values in the x16 frame
+          const float hs = (kKFold && KFmtHi<KT, D>::hi(i)) ? 0.0625f : 1.0f;
+          qop[s][i] = f16(qw[KF::dslot(j, s, i)] * keep * hs);
+        }
+    }
+
+    // Q4_0 K: B operand of the per-block offset correction. Column n = head,
+    // lane j: for each of the lane's ggml blocks bl, -8 * (sum of the q values
+    // its slots carry for that block), in fp32 (a 16x16x4 f32 MFMA per block).
+    float kcorr[KF_NBL];
+#pragma unroll
+    for (int bl = 0; bl < KF_NBL; ++bl) {
+      float qsum = 0.0f;
+#pragma unroll
+      for (int s2 = 4 * bl; s2 < 4 * bl + 4; ++s2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qsum += float(qop[s2][i]) * (KFmtHi<KT, D>::hi(i) ? 16.0f : 1.0f);
+      kcorr[bl] = -8.0f * qsum;
     }
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 vcorr = f32x4{0.f, 0.f, 0.f, 0.f};   // Q4_0 V: sum_t d_t p_t per row block
+    int vshift = 0;                            // Q4_0 V: acc holds the sums times 2^-vshift
     int bad = 0;
 
     for (int seg_t0 = t_begin; seg_t0 < t_end; seg_t0 += seg_tokens) {
@@ -175,7 +270,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 
       // ---- DMA of step s into ring slot s&1 (each wave its share) ----------
       auto issue = [&](int s) __attribute__((always_inline)) {
-        const uint32_t slot = uint32_t(s & 1) * LY::SLOT;   // ring starts at LDS byte 0
+        const uint32_t slot = uint32_t(s % LY::R) * LY::SLOT;   // ring starts at LDS byte 0
         const int t0 = seg_t0 + s * T;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -188,34 +283,32 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
                                       live ? 16u * vstride : 0u);
 #pragma unroll
-          for (int sub = 0; sub < LY::NIK; ++sub)
-            if ((gi * LY::NIK + sub) % 4 == wave)
-              dma_chunk<LY::CPK>(kr, slot + (gi * LY::NIK + sub) * 1024, sub, lane, kstride, khead,
-                                 16u * kstride);
+          for (int sub = 0; sub < LY::NIK; ++sub) {
+            const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
+            if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+          }
 #pragma unroll
-          for (int sub = 0; sub < LY::NIV; ++sub)
-            if ((G * LY::NIK + gi * LY::NIV + sub) % 4 == wave)
-              dma_chunk<LY::CPV>(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, sub, lane, vstride,
-                                 vhead, 16u * vstride);
+          for (int sub = 0; sub < LY::NIV; ++sub) {
+            const int q = G * LY::NIK + gi * LY::NIV + sub;
+            if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+          }
         }
       };
 
       // ---- compute step s from LDS: scores, online softmax (exp2), PV -------
       auto compute = [&](int s) __attribute__((always_inline)) {
-        const unsigned char* slot = ring + (s & 1) * LY::SLOT;
+        const unsigned char* slot = ring + (s % LY::R) * LY::SLOT;
         const int t0 = seg_t0 + s * T;
         const bool full = t0 + T <= t_end;
         typename KF::Raw kr[G];
         typename VF::Raw vr[2 * NP];
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi)
-          KF::load_lds(kr[gi], slot + gi * LY::NIK * 1024 + m * LY::SPK + wave * LY::RBK + KF::lane_off(j));
+        for (int gi = 0; gi < G; ++gi) KF::load_lds(kr[gi], slot + gi * LY::NIK * 1024 + k_row);
 #pragma unroll
         for (int gi = 0; gi < G; ++gi)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            VF::load_lds(vr[4 * gi + i],
-                         slot + LY::VOFF + gi * LY::NIV * 1024 + (4 * j + i) * LY::SPV + wave * LY::RBV, vl);
+            VF::load_lds(vr[4 * gi + i], slot + LY::VOFF + gi * LY::NIV * 1024 + v_row[i], vl);
         if (!full) {
           // zero V rows past the end so 0 * junk never reaches the PV MFMA
 #pragma unroll
@@ -224,13 +317,68 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
             for (int i = 0; i < 4; ++i)
               if (t0 + 16 * gi + 4 * j + i >= t_end) VF::kill(vr[4 * gi + i]);
         }
+        // The fma form of the Q4_0 conversion needs |d| < 64 (-1024*d finite):
+        // a step whose live scales exceed that is converted with d * 2^-k (exact
+        // scaling) and the results are scaled back by 2^k in fp32, so every
+        // step runs the same code.
+        // (the largest |d| of the lane as f16 bits; the shift is only worked
+        // out when some lane's reaches 64)
+        int kk = 0, kv = 0;
+        if constexpr (kKFold) {
+          uint32_t kb = 0;
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) {
+            const bool live_row = t0 + 16 * gi + m < t_end;   // dead K rows are masked below
+#pragma unroll
+            for (int bl = 0; bl < KF_NBL; ++bl)
+              kb = max(kb, live_row ? uint32_t(bitcast<uint16_t>(KF::dscale(kr[gi], bl, ksh))) & 0x7FFFu : 0u);
+          }
+          if (__any(kb >= 0x5400u)) kk = wave_max_shift(scale_shift(bitcast<f16>(uint16_t(kb))));
+        }
+        if constexpr (kVFold) {
+          uint32_t vb = 0;
+#pragma unroll
+          for (int i = 0; i < 2 * NP; ++i) vb = max(vb, uint32_t(bitcast<uint16_t>(vr[i].d)) & 0x7FFFu);
+          if (__any(vb >= 0x5400u)) kv = wave_max_shift(scale_shift(bitcast<f16>(uint16_t(vb))));
+        }
+
         f32x4 sc[G];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) sc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // ---- scores ------------------------------------------------------
+        if constexpr (kKFold) {
+          // n*d operands; the -8 offset is added per block by a 16x16x4 f32
+          // MFMA of the block scales (A: row m, k = the lane's j) against kcorr
+          const f16x2 sk = pow2_neg_f16x2(kk);
 #pragma unroll
-        for (int s2 = 0; s2 < S; ++s2)
+          for (int gi = 0; gi < G; ++gi) {
+            f16x2 d2[KF_NBL], c2[KF_NBL];
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) sc[gi] = mfma(KF::op(kr[gi], s2, ksh, mg), qop[s2], sc[gi]);
+            for (int bl = 0; bl < KF_NBL; ++bl) {
+              d2[bl] = splat2(KF::dscale(kr[gi], bl, ksh)) * sk;
+              c2[bl] = d2[bl] * f16x2{-1024.0f16, -1024.0f16};
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2)
+              sc[gi] = mfma(KF::op_n16(kr[gi], s2, ksh, mg, d2, c2), qop[s2], sc[gi]);
+          }
+          if (kk) {
+            const float up = __builtin_ldexpf(1.0f, kk);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) sc[gi] *= up;
+          }
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int bl = 0; bl < KF_NBL; ++bl)
+              sc[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(float(KF::dscale(kr[gi], bl, ksh)), kcorr[bl],
+                                                            sc[gi], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) sc[gi] = mfma(KF::op(kr[gi], s2, ksh, mg), qop[s2], sc[gi]);
+        }
         if (!full) {
 #pragma unroll
           for (int gi = 0; gi < G; ++gi)
@@ -238,20 +386,22 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
             for (int i = 0; i < 4; ++i)
               if (t0 + 16 * gi + 4 * j + i >= t_end) sc[gi][i] = -INFINITY;
         }
+        // ---- online softmax ------------------------------------------------
         float mx = -INFINITY;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi)
           mx = fmaxf(mx, fmaxf(fmaxf(sc[gi][0], sc[gi][1]), fmaxf(sc[gi][2], sc[gi][3])));
         mx = max_over_rows(mx);
-        // Lazy rescale: the reference m only moves when some head's max exceeds
-        // it by more than kSlack (then p <= 2^kSlack, safe in f16); the
-        // lucebox page skips the rescale when the max is unchanged.
+        // Lazy rescale: the reference m only moves when some head's max
+        // exceeds it by more than kSlack (then p <= 2^kSlack, safe in f16);
+        // the lucebox page skips the rescale when the max is unchanged.
         if (__any(mx > m_run + kSlack)) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           l_run *= alpha;
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[e] *= alpha;
+          vcorr *= alpha;
           m_run = m_new;
         }
         float pr[2 * NP];
@@ -269,6 +419,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           if constexpr (NP == 4) return mfma(av, pop, c);
           else return mfma16(av, pop, c);
         };
+        // ---- PV ------------------------------------------------------------
         if constexpr (VF::kQuant) {
           uint32_t q[2 * NP][VF::ND];
           f16x2 dd[NP];
@@ -276,8 +427,31 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           for (int i = 0; i < 2 * NP; ++i) VF::realign(vr[i], vl.sh, q[i]);
 #pragma unroll
           for (int qq = 0; qq < NP; ++qq) dd[qq] = f16x2{vr[2 * qq].d, vr[2 * qq + 1].d};
+          if constexpr (kVFold) {
+            // n*d' operands with d' = d * 2^-kv; acc holds the true sums times
+            // 2^-vshift, so a change of shift rescales it once (exact). The sum
+            // of d_t p_t (per row block and head) carries the -8 offset, added
+            // once at the end of the unit.
+            if (kv != vshift) {
+              const float f = __builtin_ldexpf(1.0f, vshift - kv);
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op_q<NP>(q, dd, e, mg), acc[e]);
+              for (int e = 0; e < E; ++e) acc[e] *= f;
+              vshift = kv;
+            }
+            const f16x2 sv = pow2_neg_f16x2(kv);
+            f16x2 ds[NP], cc[NP];
+#pragma unroll
+            for (int qq = 0; qq < NP; ++qq) {
+              ds[qq] = dd[qq] * sv;
+              cc[qq] = ds[qq] * f16x2{-1024.0f16, -1024.0f16};
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op_n16<NP>(q, ds, cc, e, mg), acc[e]);
+            vcorr = pv(OpVec<NP>::pack(dd), vcorr);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op_q<NP>(q, dd, e, mg), acc[e]);
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[e] = pv(VF::template op<NP>(vr, e), acc[e]);
@@ -285,14 +459,27 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
         l_run += sum_over_rows(ps);
       };
 
-      // ---- the ring: DMA of step s+1 in flight while step s is computed ----
-      issue(0);
+      // ---- the ring: steps s+1 .. s+R-2 in flight while step s is computed -
+      for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);
       for (int s = 0; s < nsteps; ++s) {
-        // every wave's DMA of step s has landed, and every wave is done with
-        // step s-1 (whose slot the next issue overwrites)
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 1 < nsteps) issue(s + 1);
+        // every wave's DMA of step s has landed (this wave may still have the
+        // DMA of the later steps outstanding: cw instructions each), and every
+        // wave is done with step s-1, whose slot the next issue overwrites
+        const int later = min(LY::R - 2, nsteps - 1 - s);
+        wait_dma_then_barrier(later * cw);
+        if (s + LY::R - 1 < nsteps) issue(s + LY::R - 1);
         compute(s);
+      }
+    }
+
+    // ---- Q4_0 V: add the -8 offset of every accumulated value -------------
+    if constexpr (kVFold) {
+      const float f = __builtin_ldexpf(1.0f, vshift);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float fe = VFmtHi<VT, D>::hi(e) ? f * 0.0625f : f;   // undo the x16 frame
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[e][i] = acc[e][i] * fe - 8.0f * vcorr[i];
       }
     }
 
@@ -327,7 +514,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 template <int KT, int VT, int D>
 size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
   using LY = LdsLayout<KT, VT, D>;
-  const size_t ring = std::max<size_t>(2 * LY::SLOT, size_t(16) * a.r * D);
+  const size_t ring = std::max<size_t>(size_t(LY::R) * LY::SLOT, size_t(16) * a.r * D);
   *ring_bytes = int((ring + 15) & ~size_t(15));
   return size_t(*ring_bytes) + 4 * size_t(((2 * a.B + 1) + 3) & ~3) + 4 * size_t((kNidS + 1 + 3) & ~3);
 }

@@ -43,8 +43,12 @@ hipError_t launch_decode_lds(const DecodeArgs& a, hipStream_t stream);
 // Geometry of the LDS-staged kernel, shared by the planner and the kernel.
 // One step stages, for the four kv heads of a workgroup, G groups of 16
 // token slots of K and of V (one 16-byte DMA chunk per lane, 1 KB per
-// instruction) into one of two ring slots of at most kLdsSlotMax bytes.
-constexpr int kLdsSlotMax = 36864;
+// instruction) into one slot of a ring of R slots that shares kLdsRingBytes
+// of LDS (two workgroups per compute unit); R-1 steps are in flight while one
+// is computed.
+constexpr int kLdsRingBytes = 73728;
+constexpr int kLdsPreferGroups = 2;
+constexpr int kLdsMaxSlots = 4;
 constexpr int kLdsMaxB = 256;
 constexpr int lds_row_bytes(int type, int D) {
   return type == PA_F16 ? 2 * D : (type == PA_Q8_0 ? 34 * (D / 32) : 18 * (D / 32));
@@ -54,9 +58,18 @@ constexpr int lds_dma_per_group(int type, int D) { return (16 * 4 * lds_row_byte
 constexpr int lds_slot_bytes(int kt, int vt, int D, int G) {
   return G * 1024 * (lds_dma_per_group(kt, D) + lds_dma_per_group(vt, D));
 }
-// 16-slot groups per step (2, else 1), or 0 when one group does not fit.
+// 16-slot groups per step (kLdsPreferGroups, else 1), or 0 when not even a
+// two-slot ring of one group fits.
 constexpr int lds_groups(int kt, int vt, int D) {
-  return lds_slot_bytes(kt, vt, D, 2) <= kLdsSlotMax ? 2 : (lds_slot_bytes(kt, vt, D, 1) <= kLdsSlotMax ? 1 : 0);
+  return 2 * lds_slot_bytes(kt, vt, D, kLdsPreferGroups) <= kLdsRingBytes ? kLdsPreferGroups
+         : (2 * lds_slot_bytes(kt, vt, D, 1) <= kLdsRingBytes ? 1 : 0);
+}
+constexpr int lds_ring_slots(int kt, int vt, int D) {
+  return lds_groups(kt, vt, D) == 0
+             ? 0
+             : (kLdsRingBytes / lds_slot_bytes(kt, vt, D, lds_groups(kt, vt, D)) > kLdsMaxSlots
+                    ? kLdsMaxSlots
+                    : kLdsRingBytes / lds_slot_bytes(kt, vt, D, lds_groups(kt, vt, D)));
 }
 
 struct MergeArgs {
