@@ -101,9 +101,13 @@ __device__ __forceinline__ uint32_t chunk_voff(int sub, int lane, uint32_t strid
 }
 
 // One DMA instruction: every lane fetches 16 bytes at its offset and the
-// wave lands them as 1 KB at LDS byte dst + 16*lane.
+// wave lands them as 1 KB at LDS byte dst + 16*lane. Every pool line is read
+// exactly once here (a workgroup owns whole blocks of its head quad), so the
+// loads carry the non-temporal hint: it raised the streaming rate of this
+// pattern from ~5.9 to ~6.7 TB/s when measured on its own.
+constexpr int kDmaNonTemporal = 2;
 __device__ __forceinline__ void dma16(rsrc_t R, uint32_t dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, kDmaNonTemporal);
 }
 
 // s_waitcnt vmcnt(n) (n wave-uniform, at most 15; larger n waits for more
@@ -419,6 +423,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           if constexpr (NP == 4) return mfma(av, pop, c);
           else return mfma16(av, pop, c);
         };
+        __builtin_amdgcn_s_setprio(1);
         // ---- PV ------------------------------------------------------------
         if constexpr (VF::kQuant) {
           uint32_t q[2 * NP][VF::ND];
@@ -467,6 +472,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
         // wave is done with step s-1, whose slot the next issue overwrites
         const int later = min(LY::R - 2, nsteps - 1 - s);
         wait_dma_then_barrier(later * cw);
+        // Issue priority: the DMA and the score / softmax chain (short,
+        // latency bound) go ahead of the other workgroup's wave on this SIMD,
+        // whose VALU-heavy PV part then fills the gaps (measured 3-8% faster).
+        __builtin_amdgcn_s_setprio(3);
         if (s + LY::R - 1 < nsteps) issue(s + LY::R - 1);
         compute(s);
       }
