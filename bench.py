@@ -81,7 +81,7 @@ def algorithmic_bytes(case, plan):
     seq = 4 * case.B
     if plan.direct:
         return kv + table + seq + q + out, 0
-    parts = sum(-(-L // plan.psize) for L in case.seq_lens) * case.Hq * (case.D + 2) * 4
+    parts = sum(-(-L // plan.psize) for L in case.seq_lens) * case.Hq * (2 * case.D + 8)
     return kv + table + seq + q + parts, parts + seq + out
 
 
@@ -178,29 +178,32 @@ def run_bench(args):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def step(c, evs=None):
-        if evs is not None:
-            evs[0].record(stream)
+    def step(c, ev_start=None, ev_end=None):
+        if ev_start is not None:
+            ev_start.record(stream)
         pa.paged_attn_decode(plan, c.q, c.k_pool, c.v_pool, c.table, c.seq_len, ws, out, stream=sptr)
-        if evs is not None:
-            evs[1].record(stream)
+        if ev_end is not None:
+            ev_end.record(stream)
         pa.paged_attn_merge(plan, ws, c.seq_len, out, stream=sptr)
-        if evs is not None:
-            evs[2].record(stream)
 
     for i in range(args.warmup):
         step(cases[i % len(cases)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Two timing events per step, around the decode launch: an event record
+    # costs the stream a few µs, so the merge is timed from the decode's end
+    # event to the next step's start event (one more event closes the loop).
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(cases[i % len(cases)], evs[i])
+        step(cases[i % len(cases)], ev_start[i], ev_end[i])
+    ev_start[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    mrg_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    dec_ms = [ev_start[i].elapsed_time(ev_end[i]) for i in range(args.steps)]
+    mrg_ms = [ev_end[i].elapsed_time(ev_start[i + 1]) for i in range(args.steps)]
+    step_ms = [ev_start[i].elapsed_time(ev_start[i + 1]) for i in range(args.steps)]
     if pa.paged_attn_status(ws) != 0:
         raise SystemExit("bench: device status word set (bad table or seq_len)")
 

@@ -163,8 +163,13 @@ int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t tota
  *               first decode; paged_attn_status reads and clears it
  *   [4, 256)    reserved
  *   partials    only when plan->direct == 0, at offset 256:
- *               float o [B][Hq][p_max][D]  normalised output of each partition
- *               float ml[B][Hq][p_max][2]  (m, l): m is a reference value of
+ *               uint16 o[B][Hq][p_max][D]  normalised output of each partition
+ *                                          as IEEE binary16, rounded to nearest
+ *                                          even (lucebox PR #555, Summary:
+ *                                          normalised f16 partials; |o| never
+ *                                          exceeds the largest |V| value)
+ *               float ml[B][Hq][p_max][2]  at offset 256 + 2*B*Hq*p_max*D:
+ *                                          (m, l): m is a reference value of
  *                                          the base-2 logits x = log2(e)*scale*q.k
  *                                          of the partition with
  *                                          m <= max x <= m + 8 (the kernel moves

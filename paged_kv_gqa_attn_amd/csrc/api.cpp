@@ -78,7 +78,7 @@ int32_t check_plan(const pa_plan* p, const char* who) {
 
 uint64_t ws_bytes_for(const pa_shape& s, int p_max, bool direct) {
   uint64_t bytes = 256;
-  if (!direct) bytes += uint64_t(s.B) * s.Hq * p_max * uint64_t(s.D + 2) * 4u;
+  if (!direct) bytes += uint64_t(s.B) * s.Hq * p_max * (2u * uint64_t(s.D) + 8u);
   return (bytes + 255) & ~uint64_t(255);
 }
 
@@ -154,8 +154,8 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
     // kernel runs two workgroups per compute unit and streams at full rate
     // only when every unit slot is busy, so the batch is cut into about
     // 2*num_cus equal units (at least 64 tokens each: two steps of the ring).
-    // The partial results this adds are (D+2)*4 bytes per query head per
-    // partition, written once and read once.
+    // The partial results this adds are 2D+8 bytes per query head per
+    // partition (binary16 o, fp32 m and l), written once and read once.
     // Sequences of at most 256 tokens stay in one partition: splitting them
     // saves less decode time than the merge launch costs.
     const int64_t units_target = int64_t(num_cus) * 2;
@@ -169,7 +169,7 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
     const int64_t units_target = int64_t(num_cus) * 4;
     const int64_t per_unit = int64_t(kTileTokens) * kWavesPerUnit;
     const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * per_bp, units_target)), per_unit);
-    const double part_bytes = double(s.Hq) * (s.D + 2) * 4.0 * 2.0;
+    const double part_bytes = double(s.Hq) * (2.0 * s.D + 8.0) * 2.0;
     const double kv_per_token = double(s.Hkv) * double(rbk + rbv);
     const int64_t floor_tok = round_up(int64_t(std::ceil(part_bytes / (0.04 * kv_per_token))), per_unit);
     psize = std::max(bal, floor_tok);
@@ -220,8 +220,8 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   a.seq_len = seq_len;
   a.out = out;
   a.status = static_cast<uint32_t*>(ws);
-  a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 256);
-  a.part_ml = a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D;
+  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+  a.part_ml = reinterpret_cast<float*>(a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D);
   a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.r = s.Hq / s.Hkv;
   a.nblocks = s.nblocks; a.max_blocks = s.max_blocks; a.block_size = s.block_size;
   a.bs_shift = ilog2_exact(s.block_size);
@@ -252,8 +252,8 @@ extern "C" int32_t paged_attn_merge(const pa_plan* plan, const void* ws, uint64_
                 (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
   const pa_shape& s = plan->shape;
   MergeArgs a{};
-  a.part_o = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + 256);
-  a.part_ml = a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D;
+  a.part_o = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(ws) + 256);
+  a.part_ml = reinterpret_cast<const float*>(a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D);
   a.seq_len = seq_len;
   a.out = out;
   a.B = s.B; a.Hq = s.Hq; a.D = s.D; a.psize = plan->psize; a.p_max = plan->p_max;

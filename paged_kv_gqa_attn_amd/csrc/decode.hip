@@ -340,31 +340,36 @@ decode_kernel(const DecodeArgs a) {
         cwt[w] = __builtin_amdgcn_exp2f(mw[w] - M);
         l += lw[w] * cwt[w];
       }
-      const float inv = 1.0f / l;
+      const float inv = bad ? __builtin_nanf("") : 1.0f / l;
       const int h = U.g * a.r + n;
       if (bad && lane == 0) atomicOr(a.status, 1u);
+      // combined, normalised value of d-tile column e, row i of this lane
+      auto value = [&](int e, int i) {
+        const int d = VF::dv(4 * j + i, e);
+        float v = acc[e][i] * c0;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) v += comb[w * comb_stride + n * D + d] * cwt[w];
+        return v * inv;
+      };
       if (n < a.r) {
-        float* dst;
         if (a.direct) {
-          dst = a.out + (int64_t(U.b) * a.Hq + h) * D;
+          float* dst = a.out + (int64_t(U.b) * a.Hq + h) * D;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = value(e, i);
         } else {
           const int64_t row = (int64_t(U.b) * a.Hq + h) * a.p_max + U.p;
-          dst = a.part_o + row * D;
+          f16* dst = reinterpret_cast<f16*>(a.part_o) + row * D;
           if (j == 0) {
             a.part_ml[2 * row] = bad ? __builtin_nanf("") : M;
             a.part_ml[2 * row + 1] = l;
           }
+#pragma unroll
+          for (int e = 0; e < E; e += 2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store_f16_pair(dst, VF::dv(4 * j + i, e), value(e, i), value(e + 1, i));
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = VF::dv(4 * j + i, e);
-            float v = acc[e][i] * c0;
-#pragma unroll
-            for (int w = 0; w < 3; ++w) v += comb[w * comb_stride + n * D + d] * cwt[w];
-            dst[d] = bad ? __builtin_nanf("") : v * inv;
-          }
       }
     }
     __syncthreads();

@@ -261,6 +261,15 @@ template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
 // with the scalar offset i*stride); `load_lds` reads one row staged in LDS
 // (`row` = its first byte) at the same in-row offsets.
 // ===========================================================================
+// Partial rows are stored as binary16 (lucebox PR #555, Summary: normalised
+// f16 partials), rounded to nearest even. For every V format below, d-tile
+// columns e and e+1 (e even) of a lane sit at adjacent head-dimension
+// positions dv(m, e) and dv(m, e) + 1, with dv(m, e) even, so a pair is one
+// aligned 4-byte store.
+__device__ __forceinline__ void store_f16_pair(f16* row, int d, float x0, float x1) {
+  *reinterpret_cast<f16x2*>(row + d) = f16x2{f16(x0), f16(x1)};
+}
+
 template <int VT, int D> struct VFmt;
 
 template <int D> struct VFmt<kF16, D> {

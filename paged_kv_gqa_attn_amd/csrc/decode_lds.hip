@@ -19,10 +19,11 @@
 //     the partition's block ids; the group address is 64-bit (mlxcel issue
 //     #2153, Proposed Solution).
 //   * A step stages G groups (16*G tokens) of K and V for the four heads; a
-//     ring of two step slots keeps the next step's DMA in flight while the
-//     current one is computed. One barrier per step separates "my DMA of
-//     step s has landed" (s_waitcnt vmcnt(0) by every wave) from "slot s-1
-//     is free" (every wave finished computing it).
+//     ring of R step slots keeps the DMA of the next R-1 steps in flight
+//     while the current one is computed. One barrier per step separates "my
+//     DMA of step s has landed" (every wave waits until only its DMA of the
+//     later steps is outstanding) from "the slot of step s-1 is free" (every
+//     wave finished computing it).
 //   * Each wave reads its head's rows from LDS into the same MFMA operand
 //     layouts the register kernel builds from HBM (decode_common.h), then
 //     runs the same scores / exp2 online softmax / PV sequence: 16x16x32
@@ -497,22 +498,26 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     if (bad && tid == 0) atomicOr(a.status, 1u);
     if (n < a.r) {
       const int h = g * a.r + n;
-      const float inv = 1.0f / l_run;
-      float* dst;
+      const float inv = bad ? __builtin_nanf("") : 1.0f / l_run;
       if (a.direct) {
-        dst = a.out + (int64_t(b) * a.Hq + h) * D;
+        float* dst = a.out + (int64_t(b) * a.Hq + h) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = acc[e][i] * inv;
       } else {
         const int64_t row = (int64_t(b) * a.Hq + h) * a.p_max + p;
-        dst = a.part_o + row * D;
+        f16* dst = reinterpret_cast<f16*>(a.part_o) + row * D;
         if (j == 0) {
           a.part_ml[2 * row] = bad ? __builtin_nanf("") : m_run;
           a.part_ml[2 * row + 1] = l_run;
         }
+#pragma unroll
+        for (int e = 0; e < E; e += 2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            store_f16_pair(dst, VF::dv(4 * j + i, e), acc[e][i] * inv, acc[e + 1][i] * inv);
       }
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = bad ? __builtin_nanf("") : acc[e][i] * inv;
     }
   }
 }

@@ -3,13 +3,16 @@
 // For each (sequence b, query head h) over its live partitions
 // p < ceil(seq_len[b]/psize), with per-partition base-2 reference m_p, sum
 // l_p and normalised output o_p (lucebox PR #555, Summary: partials stored
-// normalised, stable split-softmax merge; llama.cpp PR #13 HRX, Changes:
-// per-block normalisation scale):
+// normalised in f16, stable split-softmax merge; llama.cpp PR #13 HRX,
+// Changes: per-block normalisation scale):
 //     M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p
 // The merge reads every partial byte once, so it is spread wide: a workgroup
-// takes one (b, h) and 64 output columns; its 256 threads are 16 column
-// quads x 16 partition classes (p mod 16), each thread accumulating float4
-// columns over its partitions, and the 16 classes are summed through LDS.
+// takes one (b, h) and 64 output columns; its 256 threads are 8 column octets
+// x 32 partition classes (p mod 32). A thread reads 8 binary16 columns (16
+// bytes) of each of its partitions and accumulates w_p o_p in fp32; the 32
+// classes are then summed through LDS in a fixed order. The first kPre
+// partitions of every class are loaded before the max is reduced, so their
+// latency overlaps the reduction.
 // Loop bounds are the runtime partition count (llama.cpp PR #13, the
 // SGPR-exhaustion fix: a constant-folded bound fully unrolled the reduction).
 #include "pa_device.h"
@@ -19,13 +22,19 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 64;                 // output columns per workgroup
-constexpr int kQuads = kCols / 4;         // float4 column quads
-constexpr int kClasses = kThreads / kQuads;
+constexpr int kCols = 64;                   // output columns per workgroup
+constexpr int kOcts = kCols / 8;            // 16-byte loads of 8 binary16 columns
+constexpr int kClasses = kThreads / kOcts;  // partition classes
+constexpr int kPre = 2;                     // partitions per class loaded ahead of the max
+
+__device__ __forceinline__ void axpy8(float* acc, float w, const f16x8& v) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] += w * float(v[k]);
+}
 
 __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   __shared__ float red[kThreads];
-  __shared__ float4 part[kClasses][kQuads];
+  __shared__ float part[kClasses][kCols + 1];
   __shared__ float wpart[kClasses];
   const int tid = threadIdx.x;
   const int chunks = a.D / kCols;
@@ -41,7 +50,16 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
     return;
   }
   const float* ml = a.part_ml + int64_t(bh) * a.p_max * 2;
-  const float* o = a.part_o + int64_t(bh) * a.p_max * a.D + col0;
+  const int q = tid % kOcts, c = tid / kOcts;
+  const f16* o = reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * a.D + col0 + 8 * q;
+
+  // the first kPre partitions of this thread's class, loaded ahead
+  f16x8 pre[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int p = c + u * kClasses;
+    pre[u] = p < P ? *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D) : f16x8{};
+  }
 
   // pass 1: M = max_p m_p; a NaN m (a partition that met a bad block id)
   // turns into a NaN max through the comparison below
@@ -63,49 +81,49 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   }
   const float M = red[0];
 
-  // pass 2: thread (quad q, class c) sums w_p o_p[4q..4q+3] over p = c mod kClasses
-  const int q = tid % kQuads, c = tid / kQuads;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // pass 2: thread (octet q, class c) sums w_p o_p[8q..8q+7] over p = c mod kClasses
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
-  int p = c;
-  for (; p + 3 * kClasses < P; p += 4 * kClasses) {
-    float w[4];
-    float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pu = p + u * kClasses;
-      w[u] = __builtin_amdgcn_exp2f(ml[2 * pu] - M) * ml[2 * pu + 1];
-      v[u] = reinterpret_cast<const float4*>(o + int64_t(pu) * a.D)[q];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wsum += w[u];
-      acc.x += w[u] * v[u].x; acc.y += w[u] * v[u].y; acc.z += w[u] * v[u].z; acc.w += w[u] * v[u].w;
+  for (int u = 0; u < kPre; ++u) {
+    const int p = c + u * kClasses;
+    if (p < P) {
+      const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+      wsum += w;
+      axpy8(acc, w, pre[u]);
     }
   }
-  for (; p < P; p += kClasses) {
+  int p = c + kPre * kClasses;
+  for (; p + kClasses < P; p += 2 * kClasses) {
+    const f16x8 v0 = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
+    const f16x8 v1 = *reinterpret_cast<const f16x8*>(o + int64_t(p + kClasses) * a.D);
+    const float w0 = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+    const float w1 = __builtin_amdgcn_exp2f(ml[2 * (p + kClasses)] - M) * ml[2 * (p + kClasses) + 1];
+    wsum += w0;
+    axpy8(acc, w0, v0);
+    wsum += w1;
+    axpy8(acc, w1, v1);
+  }
+  if (p < P) {
+    const f16x8 v = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
     const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
-    const float4 v = reinterpret_cast<const float4*>(o + int64_t(p) * a.D)[q];
     wsum += w;
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    axpy8(acc, w, v);
   }
-  part[c][q] = acc;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) part[c][8 * q + k] = acc[k];
   if (q == 0) wpart[c] = wsum;
   __syncthreads();
 
   // pass 3: sum the classes in a fixed order and normalise
-  if (tid < kQuads) {
-    float4 s = part[0][tid];
+  if (tid < kCols) {
+    float s = part[0][tid];
     float W = wpart[0];
     for (int k = 1; k < kClasses; ++k) {
-      const float4 t = part[k][tid];
-      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+      s += part[k][tid];
       W += wpart[k];
     }
-    const float inv = 1.0f / W;
-    float4 r = make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
-    if (M != M) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
-    reinterpret_cast<float4*>(dst)[tid] = r;
+    dst[tid] = M != M ? __builtin_nanf("") : s / W;
   }
 }
 

@@ -21,7 +21,7 @@ struct DecodeArgs {
   const int32_t* table;    // nullptr = contiguous layout
   const int32_t* seq_len;
   float* out;              // direct mode
-  float* part_o;           // [B][Hq][p_max][D]
+  uint16_t* part_o;        // [B][Hq][p_max][D] binary16 bits
   float* part_ml;          // [B][Hq][p_max][2]
   uint32_t* status;
   int32_t B, Hq, Hkv, D, r;
@@ -73,7 +73,7 @@ constexpr int lds_ring_slots(int kt, int vt, int D) {
 }
 
 struct MergeArgs {
-  const float* part_o;
+  const uint16_t* part_o;  // binary16 bits
   const float* part_ml;
   const int32_t* seq_len;
   float* out;

@@ -163,32 +163,78 @@ def test_junk_in_dead_slots_never_leaks(junk, pair):
         check_parity(case, out)
 
 
+def _oracle_partials(case, psize):
+    kp, vp = case.k_pool.numpy().reshape(-1), case.v_pool.numpy().reshape(-1)
+    return oracle.partials(case.q, kp, vp, case.table, case.seq_len, Hkv=case.Hkv, D=case.D,
+                           block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
+                           nblocks=case.nblocks, max_blocks=case.max_blocks, psize=psize,
+                           scale=case.scale)
+
+
+def _ws_partials(ws, B, Hq, P, D):
+    """(o [B,Hq,P,D] from binary16, ml [B,Hq,P,2] fp32) read from a workspace
+    in the documented layout."""
+    raw = ws.detach().cpu()
+    n_o = B * Hq * P * D
+    o = raw[256:256 + 2 * n_o].view(torch.float16).reshape(B, Hq, P, D)
+    ml = raw[256 + 2 * n_o:256 + 2 * n_o + 8 * B * Hq * P].view(torch.float32).reshape(B, Hq, P, 2)
+    return o.double().numpy(), ml.double().numpy()
+
+
 def test_merge_kernel_on_oracle_partials():
-    """Write the oracle's own partials into the documented workspace layout and
-    check the GPU merge against the oracle merge."""
+    """Write the oracle's own partials, o rounded to binary16, into the
+    documented workspace layout and check the GPU merge against the oracle
+    merge of the same values; and against the unrounded partials within what
+    binary16 rounding of o can move the result (2^-11 of the largest |o_p|)."""
     pa = pa_mod()
     case = _case([300, 0, 97, 31], k_fmt="f16", v_fmt="q8_0", seed=23, Hq=8, Hkv=2)
     plan = plan_for(case, partition_tokens=64)
-    kp, vp = case.k_pool.numpy().reshape(-1), case.v_pool.numpy().reshape(-1)
-    m, l, o, n = oracle.partials(case.q, kp, vp, case.table, case.seq_len, Hkv=case.Hkv, D=case.D,
-                                 block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
-                                 nblocks=case.nblocks, max_blocks=case.max_blocks,
-                                 psize=plan.psize, scale=case.scale)
+    m, l, o, n = _oracle_partials(case, plan.psize)
     B, Hq, P, D = o.shape
     assert P == plan.p_max
+    o16 = o.astype(np.float16)
+    ml = np.stack([m, l], axis=-1).astype(np.float32)
     ws = pa.workspace(plan, "cpu")
-    body = ws[256:256 + B * Hq * P * (D + 2) * 4].view(torch.float32)
-    body[: B * Hq * P * D] = torch.from_numpy(o.reshape(-1)).float()
-    ml = np.stack([m, l], axis=-1).reshape(-1)
-    body[B * Hq * P * D:] = torch.from_numpy(ml).float()
+    n_o = B * Hq * P * D
+    ws[256:256 + 2 * n_o] = torch.from_numpy(o16.reshape(-1)).view(torch.uint8)
+    ws[256 + 2 * n_o:256 + 2 * n_o + 8 * B * Hq * P] = torch.from_numpy(ml.reshape(-1)).view(torch.uint8)
     wsd = ws.to(DEV)
     out = torch.full((B, Hq, D), float("nan"), device=DEV)
     pa.paged_attn_merge(plan, wsd, case.seq_len.to(DEV), out)
     torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    ref16 = oracle.merge(m, l, o16.astype(np.float64), n)
+    assert float(rel_err_rows(got, ref16).max()) <= 1e-5
     ref = oracle.merge(m, l, o, n)
-    err = rel_err_rows(out.cpu().double().numpy(), ref)
-    assert float(err.max()) <= 1e-5
-    assert np.all(out[1].cpu().numpy() == 0.0)
+    bound = 2.0 ** -11 * np.abs(o).max(axis=(2, 3)) + 1e-6 * np.abs(ref).max(axis=-1) + 1e-7
+    assert np.all(np.abs(got - ref).max(axis=-1) <= bound)
+    assert np.all(got[1] == 0.0)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("pair", [("q4_0", "q8_0"), ("f16", "q4_0")])
+def test_decode_partials_match_the_oracle_split_form(pair, path):
+    """The partials a decode kernel leaves in the workspace (binary16 o, fp32
+    m and l, documented layout) against the oracle's split form with the same
+    partition size: o to the format tolerance, m a reference value within 8
+    (log2 units) below the partition's largest logit, and l * 2^m equal to the
+    oracle's sum to the tolerance."""
+    case = _case([300, 0, 97, 130], k_fmt=pair[0], v_fmt=pair[1], seed=31)
+    plan = plan_for(case, path=path, partition_tokens=64)
+    out, ws = run(case.to(DEV), plan)
+    m_r, l_r, o_r, n = _oracle_partials(case, plan.psize)
+    B, Hq, P, D = o_r.shape
+    assert P == plan.p_max
+    o, ml = _ws_partials(ws, B, Hq, P, D)
+    tol = tol_for(case)
+    for b in range(B):
+        for p in range(int(n[b])):
+            assert float(rel_err_rows(o[b, :, p], o_r[b, :, p]).max()) <= tol
+            m_g, l_g = ml[b, :, p, 0], ml[b, :, p, 1]
+            assert np.all(m_g <= m_r[b, :, p] + 1e-2) and np.all(m_r[b, :, p] <= m_g + 8 + 1e-2)
+            rel = np.abs(l_g * np.exp2(m_g - m_r[b, :, p]) / l_r[b, :, p] - 1.0)
+            assert float(rel.max()) <= tol
+    check_parity(case, out)
 
 
 @pytest.mark.parametrize("path", PATHS)

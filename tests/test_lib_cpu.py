@@ -85,7 +85,8 @@ def test_plan_automatic_partitions_for_long_context():
     assert p.psize % 32 == 0 and p.psize >= 1024
     assert p.p_max == -(-131072 // p.psize)
     assert p.direct == 0
-    assert p.ws_bytes == 256 + 8 * 24 * p.p_max * (256 + 2) * 4
+    # binary16 o rows, then fp32 (m, l) pairs
+    assert p.ws_bytes == 256 + 8 * 24 * p.p_max * (2 * 256 + 8)
     assert 1 <= p.grid <= 256 * 8
     assert abs(p.scale - 1 / 16) < 1e-7
 
@@ -99,7 +100,7 @@ def test_plan_partial_traffic_floor_and_direct_mode():
     # under ~4% of the K/V bytes of a partition
     p = pa.paged_attn_plan(_shape(Hq=12, Hkv=2), 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.path == 1
-    part = 12 * (256 + 2) * 4 * 2
+    part = 12 * (2 * 256 + 8) * 2
     kv = p.psize * 2 * (144 + 144)
     assert part / kv <= 0.04 + 1e-9
 
