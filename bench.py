@@ -20,6 +20,7 @@ object (the fp64 oracle timed on a bounded sample on the host cores).
   python bench.py [--steps K] [--warmup W] [--workload NAME]
   python bench.py --summarize-stats DIR --label NAME   (rocprofv3 --stats CSV -> profiles/)
   python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
+  python bench.py --metadata     (paging-metadata update and copy-on-write timings)
 """
 from __future__ import annotations
 
@@ -263,7 +264,7 @@ def _csvs(d, suffix):
     return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
 
 
-def summarize_stats(d, label, cmd):
+def summarize_stats(d, label, cmd, stem=None):
     rows = []
     for path in _csvs(d, "kernel_stats.csv"):
         with open(path) as f:
@@ -285,7 +286,7 @@ def summarize_stats(d, label, cmd):
                                  r.get("AverageNs", ""), r.get("MinNs", ""), r.get("MaxNs", ""),
                                  r.get("Percentage", "")]))
     lines.append(f"# other kernels: {other_calls} calls, {other_ns} ns in total")
-    out = os.path.join(ROOT, "profiles", f"decode_{label}_stats.txt")
+    out = os.path.join(ROOT, "profiles", f"{stem or 'decode_' + label}_stats.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
@@ -352,6 +353,88 @@ def pmc_pass(args):
     run_bench(args)
 
 
+def run_metadata(args):
+    """Paging-metadata maintenance (lucebox PR #555, Summary: 4 bytes per fresh
+    block instead of the whole table; Roadmap item 6: copy-on-write). Prints
+    one JSON line:
+      * table: paged_table_update of one fresh block per sequence plus its
+        seq_len (the per-step upload at B=8, 16-token blocks, 128K-token
+        tables), against copying the whole live table and seq_len from pinned
+        host memory every step;
+      * cow: paged_kv_copy_blocks of 64 1 MB blocks (256 slots x 8 heads of
+        F16 D=256 rows) per call, rotating over a pool 5x the MALL, HBM bytes
+        read + written per second.
+    """
+    import torch
+    import paged_kv_gqa_attn_amd as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    B, MB, K = 8, 8192, max(args.steps, 20)
+
+    def timed(fn, reps):
+        for _ in range(5):
+            fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / reps, e0.elapsed_time(e1) * 1e3 / reps
+
+    table = torch.zeros((B, MB), dtype=torch.int32, device=dev)
+    seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    host_table = torch.zeros((B, MB), dtype=torch.int32).pin_memory()
+    host_seq = torch.zeros(B, dtype=torch.int32).pin_memory()
+
+    def update(i):
+        j = i % MB
+        pa.paged_table_update(table, seq_len, [(b, j, b * MB + j) for b in range(B)] +
+                              [(b, -1, 16 * (j + 1)) for b in range(B)], stream=stream)
+
+    def full_upload(i):
+        table.copy_(host_table, non_blocking=True)
+        seq_len.copy_(host_seq, non_blocking=True)
+
+    upd_wall, upd_gpu = timed(update, K)
+    full_wall, full_gpu = timed(full_upload, K)
+
+    # 1.25 GiB pool (5x the MALL); each call copies 64 blocks from the lower
+    # half to the upper half, rotating so that no call finds its blocks cached
+    nb, bsz = 1280, 256 * 8 * 512
+    pool = torch.zeros((nb, 256, 8, 512), dtype=torch.uint8, device=dev)
+    half = nb // 2
+
+    def cow(i):
+        base = (64 * i) % half
+        src = [(base + k) % half for k in range(64)]
+        dst = [half + (base + 320 + k) % half for k in range(64)]
+        pa.paged_kv_copy_blocks(pool, src, dst, stream=stream)
+
+    cow_wall, cow_gpu = timed(cow, K)
+    cow_bytes = 2 * 64 * bsz
+    line = {
+        "metric": "paging metadata: per-step table update and copy-on-write block copy",
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "data": "synthetic",
+        "table": {"B": B, "max_blocks": MB, "update_entries": 2 * B,
+                  "update_bytes": 2 * B * 12, "update_us_gpu": round(upd_gpu, 2),
+                  "update_us_wall": round(upd_wall, 2),
+                  "full_table_bytes": (B * MB + B) * 4, "full_upload_us_gpu": round(full_gpu, 2),
+                  "full_upload_us_wall": round(full_wall, 2)},
+        "cow": {"pairs": 64, "block_bytes": bsz, "us_gpu": round(cow_gpu, 2),
+                "GB_s": round(cow_bytes / (cow_gpu * 1e-6) / 1e9, 1),
+                "frac_of_8TBs": round(cow_bytes / (cow_gpu * 1e-6) / 1e9 / PEAK_GBS, 3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,9 +451,12 @@ def main():
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--label", default=DEFAULT)
     ap.add_argument("--cmd", default="")
+    ap.add_argument("--stem", default=None, help="profiles/ file stem (default decode_LABEL)")
+    ap.add_argument("--metadata", action="store_true",
+                    help="measure the paging-metadata entry points instead of the decode step")
     args = ap.parse_args()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.label, args.cmd)
+        summarize_stats(args.summarize_stats, args.label, args.cmd, args.stem)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.label, args.cmd, args.calib_bytes)
@@ -381,6 +467,9 @@ def main():
         sys.exit(2)
     if args.pmc_pass:
         pmc_pass(args)
+        return
+    if args.metadata:
+        run_metadata(args)
         return
     run_bench(args)
 

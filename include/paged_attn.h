@@ -249,6 +249,44 @@ int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
 int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
 
 /*
+ * paged_table_update - write a few entries of the device-resident block table
+ * and seq_len (lucebox PR #555, Summary: the paging metadata stays resident on
+ * the device next to the pool, and a decode step uploads 4 bytes per fresh
+ * 16-token block instead of the whole live table).
+ *   table       device int32 [B][max_blocks]; seq_len device int32 [B]
+ *   updates     HOST int32 [n][3] triples (b, slot, value): slot >= 0 sets
+ *               table[b][slot] = value, slot == -1 sets seq_len[b] = value.
+ *               Read before the call returns (they travel in the kernel
+ *               arguments), so the array may be reused at once.
+ *   n           >= 0 (0 is a no-op); any number, launched 256 per kernel
+ * Stream-ordered; allocates nothing. PA_ERR_INVALID (nothing launched) for
+ * b outside [0, B), slot outside [-1, max_blocks) or two triples naming the
+ * same entry. Values are not checked here: decode checks every block id it
+ * reads and clamps seq_len (status bits).
+ */
+int32_t paged_table_update(int32_t* table, int32_t* seq_len, int32_t B, int32_t max_blocks,
+                           const int32_t* updates, int32_t n, void* stream);
+
+/*
+ * paged_kv_copy_blocks - copy whole blocks inside one pool: the device half
+ * of copy-on-write (lucebox PR #555, Roadmap item 6: shared prefix blocks
+ * with reference counting and copy-on-write). After kv_pool_cow hands an
+ * allocation a private id for a shared block, copy the shared block there
+ * (in the K pool and in the V pool) before writing into it.
+ *   pool          device memory, 16-byte aligned: nblocks blocks of
+ *                 block_bytes = block_size*Hkv*row_bytes bytes (a multiple
+ *                 of 16)
+ *   src_ids, dst_ids  HOST int32 [n]: block src_ids[i] is copied to
+ *                 dst_ids[i]; read before the call returns
+ * Stream-ordered; allocates nothing. PA_ERR_INVALID (nothing launched) for
+ * ids outside [0, nblocks), a block that is both a source and a destination,
+ * or a destination named twice.
+ */
+int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_t nblocks,
+                             const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                             void* stream);
+
+/*
  * Fixed-block allocator over the block ids [0, nblocks) of a caller-owned
  * pool (lucebox PR #555, Summary and Validation: exact fixed-block allocator,
  * transactional allocation, stale-handle detection, immediate release, pool
@@ -256,9 +294,15 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  *
  * An allocation is a list of block ids, in the order they were handed out,
  * named by a 64-bit handle (slot index and generation; 0 is never a valid
- * handle). Blocks go back to the pool the moment their allocation is
- * released. Any use of a handle that was released, released twice or issued
+ * handle). Any use of a handle that was released, released twice or issued
  * before a reset returns PA_ERR_STALE_HANDLE and changes nothing.
+ *
+ * Prefix sharing (lucebox PR #555, Roadmap item 6: shared prefix blocks with
+ * reference counting and copy-on-write): every block counts the allocations
+ * that hold it. kv_pool_fork starts an allocation with another's first
+ * blocks; a block goes back to the pool the moment the last allocation
+ * holding it is released; kv_pool_cow gives an allocation a private block in
+ * place of a shared one before it writes there.
  */
 typedef struct kv_pool kv_pool;
 
@@ -286,6 +330,23 @@ int32_t kv_pool_count(const kv_pool* pool, uint64_t handle);
 /* Copy up to cap ids of an allocation, in order, to ids_out; returns the
  * number held (may exceed cap) or a negative code. */
 int32_t kv_pool_blocks(const kv_pool* pool, uint64_t handle, int32_t* ids_out, int32_t cap);
+
+/* Open a new allocation (*handle) holding the first n_shared blocks of the
+ * live allocation src (0 <= n_shared <= its block count); each of those blocks
+ * gains a reference. Grow it with kv_pool_alloc as usual. */
+int32_t kv_pool_fork(kv_pool* pool, uint64_t src, int32_t n_shared, uint64_t* handle);
+
+/* Make block `index` of an allocation private before writing into it. If no
+ * other allocation holds it: *id_out = that id, *copy_from = -1 (write in
+ * place). Otherwise a free block replaces it in this allocation (the shared
+ * block loses a reference): *id_out = the new id, *copy_from = the shared id,
+ * whose bytes the caller copies over with paged_kv_copy_blocks. With no free
+ * block returns PA_ERR_CAPACITY and changes nothing. */
+int32_t kv_pool_cow(kv_pool* pool, uint64_t handle, int32_t index, int32_t* id_out,
+                    int32_t* copy_from);
+
+/* Allocations holding block id (0 = free) or a negative code. */
+int32_t kv_pool_refcount(const kv_pool* pool, int32_t id);
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,11 @@ def _load():
         "kv_pool_free_count": (i32, [vp]),
         "kv_pool_count": (i32, [vp, u64]),
         "kv_pool_blocks": (i32, [vp, u64, P(i32), i32]),
+        "kv_pool_fork": (i32, [vp, u64, i32, P(u64)]),
+        "kv_pool_cow": (i32, [vp, u64, i32, P(i32), P(i32)]),
+        "kv_pool_refcount": (i32, [vp, i32]),
+        "paged_table_update": (i32, [vp, vp, i32, i32, P(i32), i32, vp]),
+        "paged_kv_copy_blocks": (i32, [vp, u64, i32, P(i32), P(i32), i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -175,6 +180,32 @@ def paged_attn_status(ws, stream=None) -> int:
     return flags.value
 
 
+def _i32_array(values):
+    flat = [int(v) for v in values]
+    return (ctypes.c_int32 * max(len(flat), 1))(*flat), len(flat)
+
+
+def paged_table_update(table, seq_len, updates, stream=None) -> None:
+    """Write (b, slot, value) triples into the device table [B, max_blocks]
+    (slot >= 0) or seq_len [B] (slot == -1); the triples are host values."""
+    B, max_blocks = table.shape
+    flat, n3 = _i32_array(v for t in updates for v in t)
+    _check(lib.paged_table_update(_ptr(table), _ptr(seq_len), B, max_blocks, flat, n3 // 3,
+                                  _stream(stream)))
+
+
+def paged_kv_copy_blocks(pool, src_ids, dst_ids, stream=None) -> None:
+    """Copy whole blocks src_ids[i] -> dst_ids[i] inside a device pool
+    [nblocks, block_size, Hkv, row_bytes] (host id lists)."""
+    nblocks = pool.shape[0]
+    block_bytes = pool[0].numel() * pool.element_size() if nblocks else 0
+    src, n = _i32_array(src_ids)
+    dst, m = _i32_array(dst_ids)
+    if n != m:
+        raise ValueError("src_ids and dst_ids differ in length")
+    _check(lib.paged_kv_copy_blocks(_ptr(pool), block_bytes, nblocks, src, dst, n, _stream(stream)))
+
+
 def workspace(plan: PaPlan, device="cuda", extra: int = 0):
     """A zero-filled uint8 workspace tensor of plan.ws_bytes (+ extra) bytes."""
     import torch
@@ -217,6 +248,22 @@ class KvPool:
 
     def count(self, handle: int) -> int:
         return _check(lib.kv_pool_count(self._h, handle))
+
+    def fork(self, src: int, n_shared: int) -> int:
+        """A new allocation holding the first n_shared blocks of src."""
+        h = ctypes.c_uint64(0)
+        _check(lib.kv_pool_fork(self._h, src, n_shared, ctypes.byref(h)))
+        return h.value
+
+    def cow(self, handle: int, index: int):
+        """Make block `index` private: returns (id, copy_from), copy_from = -1
+        when no copy is needed."""
+        i, c = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib.kv_pool_cow(self._h, handle, index, ctypes.byref(i), ctypes.byref(c)))
+        return i.value, c.value
+
+    def refcount(self, block_id: int) -> int:
+        return _check(lib.kv_pool_refcount(self._h, block_id))
 
     def blocks(self, handle: int):
         n = _check(lib.kv_pool_blocks(self._h, handle, None, 0))

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -313,6 +314,78 @@ extern "C" int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags) {
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
   *flags = v;
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_table_update(int32_t* table, int32_t* seq_len, int32_t B, int32_t max_blocks,
+                                      const int32_t* updates, int32_t n, void* stream) {
+  const char* who = "paged_table_update";
+  if (n < 0 || B < 1 || max_blocks < 1)
+    return fail(PA_ERR_INVALID, "%s: n < 0, B < 1 or max_blocks < 1", who);
+  if (n == 0) { clear_error(); return PA_OK; }
+  if (!table || !seq_len || !updates) return fail(PA_ERR_INVALID, "%s: null table, seq_len or updates", who);
+  // every entry named once: sort the flat targets (seq_len[b] as -1 - b)
+  std::vector<int64_t> targets(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = updates[3 * i], slot = updates[3 * i + 1];
+    if (b < 0 || b >= B || slot < -1 || slot >= max_blocks)
+      return fail(PA_ERR_INVALID, "%s: update %d names (b=%d, slot=%d) outside B=%d, max_blocks=%d", who, i,
+                  b, slot, B, max_blocks);
+    targets[size_t(i)] = slot < 0 ? -1 - int64_t(b) : int64_t(b) * max_blocks + slot;
+  }
+  std::sort(targets.begin(), targets.end());
+  if (std::adjacent_find(targets.begin(), targets.end()) != targets.end())
+    return fail(PA_ERR_INVALID, "%s: two updates name the same entry", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < n; i0 += kTableUpdates) {
+    TableUpdateArgs a;
+    a.table = table;
+    a.seq_len = seq_len;
+    a.max_blocks = max_blocks;
+    a.n = std::min(kTableUpdates, n - i0);
+    std::memcpy(a.upd, updates + 3 * int64_t(i0), sizeof(int32_t) * 3 * size_t(a.n));
+    hipError_t e = launch_table_update(a, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  }
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_t nblocks,
+                                        const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                                        void* stream) {
+  const char* who = "paged_kv_copy_blocks";
+  if (n < 0 || nblocks < 0) return fail(PA_ERR_INVALID, "%s: n < 0 or nblocks < 0", who);
+  if (n == 0) { clear_error(); return PA_OK; }
+  if (!pool || !src_ids || !dst_ids) return fail(PA_ERR_INVALID, "%s: null pool, src_ids or dst_ids", who);
+  if (block_bytes == 0 || block_bytes % 16 || (reinterpret_cast<uintptr_t>(pool) & 15))
+    return fail(PA_ERR_INVALID, "%s: block_bytes must be a positive multiple of 16 and the pool 16-byte aligned",
+                who);
+  std::vector<int32_t> srcs(src_ids, src_ids + n), dsts(dst_ids, dst_ids + n);
+  for (int32_t i = 0; i < n; ++i)
+    if (srcs[size_t(i)] < 0 || srcs[size_t(i)] >= nblocks || dsts[size_t(i)] < 0 || dsts[size_t(i)] >= nblocks)
+      return fail(PA_ERR_INVALID, "%s: pair %d (%d -> %d) outside [0, %d)", who, i, srcs[size_t(i)],
+                  dsts[size_t(i)], nblocks);
+  std::sort(srcs.begin(), srcs.end());
+  std::vector<int32_t> sorted_dst = dsts;
+  std::sort(sorted_dst.begin(), sorted_dst.end());
+  if (std::adjacent_find(sorted_dst.begin(), sorted_dst.end()) != sorted_dst.end())
+    return fail(PA_ERR_INVALID, "%s: a destination block is named twice", who);
+  for (int32_t d : sorted_dst)
+    if (std::binary_search(srcs.begin(), srcs.end(), d))
+      return fail(PA_ERR_INVALID, "%s: block %d is both a source and a destination", who, d);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < n; i0 += kCopyPairs) {
+    CopyBlocksArgs a;
+    a.pool = static_cast<uint8_t*>(pool);
+    a.block_bytes = block_bytes;
+    a.n = std::min(kCopyPairs, n - i0);
+    std::memcpy(a.src, src_ids + i0, sizeof(int32_t) * size_t(a.n));
+    std::memcpy(a.dst, dst_ids + i0, sizeof(int32_t) * size_t(a.n));
+    hipError_t e = launch_copy_blocks(a, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  }
   clear_error();
   return PA_OK;
 }

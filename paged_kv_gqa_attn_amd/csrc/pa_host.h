@@ -72,6 +72,30 @@ constexpr int lds_ring_slots(int kt, int vt, int D) {
                     : kLdsRingBytes / lds_slot_bytes(kt, vt, D, lds_groups(kt, vt, D)));
 }
 
+// Whole-block copies inside one pool (copy-on-write); up to kCopyPairs pairs
+// per launch travel in the kernel arguments.
+constexpr int kCopyPairs = 64;
+struct CopyBlocksArgs {
+  uint8_t* pool;
+  uint64_t block_bytes;    // multiple of 16; pool 16-byte aligned
+  int32_t n;
+  int32_t src[kCopyPairs];
+  int32_t dst[kCopyPairs];
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
+// Block-table / seq_len scatter; up to kTableUpdates (b, slot, value) triples
+// per launch travel in the kernel arguments (slot < 0: seq_len[b] = value).
+constexpr int kTableUpdates = 256;
+struct TableUpdateArgs {
+  int32_t* table;
+  int32_t* seq_len;
+  int32_t max_blocks;
+  int32_t n;
+  int32_t upd[3 * kTableUpdates];
+};
+hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t stream);
+
 struct MergeArgs {
   const uint16_t* part_o;  // binary16 bits
   const float* part_ml;

@@ -41,7 +41,9 @@ def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for must in ["paged_attn_plan", "paged_attn_decode", "paged_attn_merge", "paged_attn_step",
                  "paged_kv_gather", "paged_attn_status", "kv_pool_alloc", "kv_pool_release",
-                 "kv_pool_create", "kv_pool_destroy", "kv_pool_reset", "pa_last_error"]:
+                 "kv_pool_create", "kv_pool_destroy", "kv_pool_reset", "pa_last_error",
+                 "kv_pool_fork", "kv_pool_cow", "kv_pool_refcount", "paged_table_update",
+                 "paged_kv_copy_blocks"]:
         assert must in names, must
 
 
@@ -215,3 +217,46 @@ def test_direct_plan_merge_is_a_no_op():
     plan = pa.paged_attn_plan(_shape(B=1), 100, num_cus=256)
     assert plan.direct == 1
     pa.paged_attn_merge(plan, 0x1000, 0x1000, 0x1000, stream=0, ws_bytes=256)
+
+
+def _i32(vals):
+    arr = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+    return arr
+
+
+def test_table_update_refusals_before_any_launch():
+    """paged_table_update validates every triple on the host and launches
+    nothing when one is out of range or two name the same entry (lucebox PR
+    #555, Summary: the resident table is updated entry by entry)."""
+    fake = 0x1000
+    cases = [
+        ([2, 0, 7], "outside"),             # b = 2 >= B
+        ([0, 4, 7], "outside"),             # slot = max_blocks
+        ([0, -2, 7], "outside"),            # slot < -1
+        ([0, 1, 7, 0, 1, 8], "same entry"),
+        ([1, -1, 3, 1, -1, 4], "same entry"),
+    ]
+    for flat, word in cases:
+        rc = pa.lib.paged_table_update(fake, fake, 2, 4, _i32(flat), len(flat) // 3, 0)
+        assert rc == pa.PA_ERR_INVALID and word in pa.pa_last_error()
+        assert "paged_table_update" in pa.pa_last_error()
+    assert pa.lib.paged_table_update(fake, fake, 2, 4, None, 0, 0) == pa.PA_OK      # nothing to do
+    assert pa.lib.paged_table_update(None, fake, 2, 4, _i32([0, 0, 1]), 1, 0) == pa.PA_ERR_INVALID
+
+
+def test_copy_blocks_refusals_before_any_launch():
+    fake = 0x1000
+    cases = [
+        ([0], [4], 4, 64, "outside"),         # dst >= nblocks
+        ([-1], [2], 4, 64, "outside"),
+        ([0, 1], [2, 2], 4, 64, "named twice"),
+        ([0, 2], [2, 3], 4, 64, "both a source and a destination"),
+        ([0], [1], 4, 40, "multiple of 16"),
+    ]
+    for src, dst, nb, bb, word in cases:
+        rc = pa.lib.paged_kv_copy_blocks(fake, bb, nb, _i32(src), _i32(dst), len(src), 0)
+        assert rc == pa.PA_ERR_INVALID and word in pa.pa_last_error(), (src, dst, pa.pa_last_error())
+        assert "paged_kv_copy_blocks" in pa.pa_last_error()
+    rc = pa.lib.paged_kv_copy_blocks(fake + 8, 64, 4, _i32([0]), _i32([1]), 1, 0)
+    assert rc == pa.PA_ERR_INVALID and "aligned" in pa.pa_last_error()
+    assert pa.lib.paged_kv_copy_blocks(fake, 64, 4, None, None, 0, 0) == pa.PA_OK
