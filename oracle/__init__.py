@@ -49,7 +49,7 @@ import numpy as np
 LOG2E = 1.0 / math.log(2.0)
 
 __all__ = ["row_bytes", "dequant_rows", "row_offsets", "gather_rows", "attend",
-           "decode", "decode_heads", "partials", "merge", "LOG2E"]
+           "decode", "decode_heads", "partials", "merge", "chunk", "LOG2E"]
 
 
 def row_bytes(fmt: str, D: int) -> int:
@@ -205,6 +205,48 @@ def decode_case(case, heads: Optional[Sequence[tuple]] = None, table="case"):
     if heads is None:
         return decode(case.q, kp, vp, tab, case.seq_len, **kw)
     return decode_heads(case.q, kp, vp, tab, case.seq_len, items=heads, **kw)
+
+
+def chunk(q, k_pool, v_pool, table, seq_len, *, Hkv: int, D: int, block_size: int,
+          k_fmt: str, v_fmt: str, nblocks: int, max_blocks: int,
+          scale: Optional[float] = None) -> np.ndarray:
+    """Multi-token query over the paged pool with causal masking inside the
+    chunk (llama.cpp PR #13 HRX, Roadmap item 3: multi-token queries over the
+    preceding paged K/V, causal attention within the chunk; TensorFold PR
+    #1418, What: paged prompt-chunk attention equal to the contiguous one).
+
+    q is [B, Tq, Hq, D]; seq_len[b] = L counts the chunk's own tokens, which
+    are the last Tq of the sequence, so chunk token t sits at position
+    L - Tq + t and attends to the keys at positions 0 .. L - Tq + t. A
+    sequence with L = 0 gives zero rows; 0 < L < Tq raises. Returns float64
+    [B, Tq, Hq, D].
+    """
+    qn = _np(q).astype(np.float64)
+    B, Tq, Hq, _ = qn.shape
+    r = Hq // Hkv
+    seq_len = _np(seq_len).astype(np.int64)
+    tab = None if table is None else _np(table)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kb, vb = row_bytes(k_fmt, D), row_bytes(v_fmt, D)
+    kw = dict(block_size=block_size, Hkv=Hkv, nblocks=nblocks, max_blocks=max_blocks)
+    out = np.zeros((B, Tq, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_len[b])
+        if L == 0:
+            continue
+        if L < Tq or L > max_blocks * block_size:
+            raise ValueError(f"seq_len[{b}]={L} outside [Tq, max_blocks*block_size]")
+        for g in range(Hkv):
+            K = dequant_rows(gather_rows(k_pool, row_offsets(tab, b, g, L, rbytes=kb, **kw), kb),
+                             k_fmt, D)
+            V = dequant_rows(gather_rows(v_pool, row_offsets(tab, b, g, L, rbytes=vb, **kw), vb),
+                             v_fmt, D)
+            for t in range(Tq):
+                n = L - Tq + t + 1                 # keys 0 .. L - Tq + t
+                out[b, t, g * r:(g + 1) * r] = attend(qn[b, t, g * r:(g + 1) * r], K[:n], V[:n],
+                                                      scale)
+    return out
 
 
 def partials(q, k_pool, v_pool, table, seq_len, *, Hkv: int, D: int, block_size: int,
