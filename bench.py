@@ -21,6 +21,7 @@ object (the fp64 oracle timed on a bounded sample on the host cores).
   python bench.py --summarize-stats DIR --label NAME   (rocprofv3 --stats CSV -> profiles/)
   python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
   python bench.py --metadata     (paging-metadata update and copy-on-write timings)
+  python bench.py --chunk NAME   (multi-token query attention, see CHUNKS)
 """
 from __future__ import annotations
 
@@ -353,6 +354,92 @@ def pmc_pass(args):
     run_bench(args)
 
 
+# name -> (synth workload, B, L, Tq, description)
+CHUNKS = {
+    "verify_q4_0_32k_b8_t8": ("uniform_q4_0", 8, 32768, 8, "verify window Q4_0 B=8 L=32768 Tq=8"),
+    "prefill_q4_0_8k_t512": ("uniform_q4_0", 1, 8192, 512, "prefill chunk Q4_0 B=1 L=8192 Tq=512"),
+}
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 MFMA, public figure
+
+
+def run_chunk(args):
+    """Multi-token query (chunk) attention over the paged pool: one call of
+    paged_attn_chunk (chunk kernel + merge) per step. Prints one JSON line with
+    the step time, the algorithmic HBM bytes and the useful MFMA work (4*D
+    flops per (query row, visible key)), each against its MI355X peak."""
+    import torch
+    import synth
+    import paged_kv_gqa_attn_amd as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl, B, L, Tq, desc = CHUNKS[args.chunk]
+    # pool copies rotated so that a step's K/V is not served from the MALL
+    # (at most 16: a short prefill chunk's pool is small and stays hot anyway)
+    cases = []
+    need = 4 * MALL_BYTES
+    while need > 0 and len(cases) < 16:
+        c = synth.workload(wl, B=B, L=L, seed=args.seed + 17 * len(cases), device=dev, junk="zero")
+        cases.append(c)
+        need -= c.k_pool.numel() + c.v_pool.numel()
+    c0 = cases[0]
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    qs = [torch.randn((B, Tq, c0.Hq, c0.D), generator=g, device=dev) for _ in cases]
+    shape = pa.shape_of(c0.B, c0.Hq, c0.Hkv, c0.D, c0.block_size, c0.nblocks, c0.max_blocks,
+                        c0.k_fmt, c0.v_fmt)
+    plan = pa.paged_attn_chunk_plan(shape, Tq, L, total_tokens=B * L)
+    ws = pa.workspace(plan, dev)
+    out = torch.empty((B, Tq, c0.Hq, c0.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = cases[i % len(cases)]
+        pa.paged_attn_chunk(plan, qs[i % len(cases)], c.k_pool, c.v_pool, c.table, c.seq_len, ws, out,
+                            stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    gpu_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    if pa.paged_attn_status(ws) != 0:
+        raise SystemExit("bench: device status word set")
+
+    rb = synth.row_bytes(c0.k_fmt, c0.D) + synth.row_bytes(c0.v_fmt, c0.D)
+    kv = B * L * c0.Hkv * rb
+    rows = B * Tq * c0.Hq
+    parts = 0 if plan.direct else rows * (-(-L // plan.psize)) * (2 * c0.D + 8) * 2
+    nbytes = kv + B * (-(-L // c0.block_size)) * 4 + 2 * rows * c0.D * 4 + parts
+    keys = B * c0.Hq * sum(L - Tq + t + 1 for t in range(Tq))
+    flops = 4.0 * c0.D * keys
+    gbs = nbytes / (wall_us * 1e-6) / 1e9
+    tfs = flops / (wall_us * 1e-6) / 1e12
+    hbm_frac, mfma_frac = gbs / PEAK_GBS, tfs / PEAK_F16_TFLOPS
+    bound = "hbm" if hbm_frac >= mfma_frac else "mfma"
+    line = {
+        "metric": "paged chunk attention step (chunk kernel + merge)",
+        "value": round(wall_us, 2), "unit": "us", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": desc, "name": args.chunk, "B": B, "L": L, "Tq": Tq, "Hq": c0.Hq,
+                   "Hkv": c0.Hkv, "D": c0.D, "k_type": c0.k_fmt, "v_type": c0.v_fmt,
+                   "psize": plan.psize, "p_max": plan.p_max, "grid": plan.grid,
+                   "pool_copies": len(cases), "gpu_us_events": round(gpu_us, 2)},
+        "roofline": {"bound": bound,
+                     "hbm": {"achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                             "frac": round(hbm_frac, 4), "bytes": nbytes},
+                     "mfma": {"achieved": round(tfs, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(mfma_frac, 4), "flops": flops}},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_metadata(args):
     """Paging-metadata maintenance (lucebox PR #555, Summary: 4 bytes per fresh
     block instead of the whole table; Roadmap item 6: copy-on-write). Prints
@@ -452,6 +539,8 @@ def main():
     ap.add_argument("--label", default=DEFAULT)
     ap.add_argument("--cmd", default="")
     ap.add_argument("--stem", default=None, help="profiles/ file stem (default decode_LABEL)")
+    ap.add_argument("--chunk", default=None, choices=sorted(CHUNKS),
+                    help="measure paged_attn_chunk on this workload instead of the decode step")
     ap.add_argument("--metadata", action="store_true",
                     help="measure the paging-metadata entry points instead of the decode step")
     args = ap.parse_args()
@@ -470,6 +559,9 @@ def main():
         return
     if args.metadata:
         run_metadata(args)
+        return
+    if args.chunk:
+        run_chunk(args)
         return
     run_bench(args)
 

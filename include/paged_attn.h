@@ -249,6 +249,48 @@ int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
 int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
 
 /*
+ * Multi-token queries over the paged pool: chunked prefill and verify windows
+ * (llama.cpp PR #13 HRX, Roadmap item 3: multi-token queries over the
+ * preceding paged K/V with causal attention inside the chunk; TensorFold PR
+ * #1418, What: paged prompt-chunk attention equal to the contiguous one).
+ *
+ * q and out are fp32 [B][Tq][Hq][D]. seq_len[b] = L counts the chunk's own
+ * tokens, whose K/V rows are already in the pool as the last Tq of the
+ * sequence: chunk token t sits at position L - Tq + t and attends to the keys
+ * at positions 0 .. L - Tq + t of kv head h / (Hq/Hkv). A sequence with L = 0
+ * gives zero rows; 0 < L < Tq also gives zero rows and sets
+ * PA_STATUS_BAD_SEQ_LEN. The key range is cut into partitions whose
+ * partials (the decode layout with Tq*Hq rows per sequence) are reduced by
+ * the same stable split-softmax merge; one partition writes out directly.
+ */
+typedef struct pa_chunk_plan {
+  pa_shape shape;
+  int32_t tq;           /* query tokens per sequence (1 .. 4096) */
+  float scale;          /* softmax scale applied to q.k */
+  int32_t psize;        /* keys per partition (multiple of 32) */
+  int32_t p_max;        /* partitions of the longest admissible sequence */
+  int32_t max_seq_len;
+  int32_t grid;         /* workgroups (one wave64 each) */
+  int32_t num_cus;
+  int32_t direct;       /* 1: one partition, no merge */
+  uint64_t ws_bytes;    /* workspace: status word + partials
+                           (256 + B*Tq*Hq*p_max*(2D+8) bytes when direct == 0) */
+} pa_chunk_plan;
+
+/* Plan a chunk launch; arguments as for paged_attn_plan plus tq (the number
+ * of query tokens per sequence). total_tokens = 0 assumes B*max_seq_len. */
+int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int32_t max_seq_len,
+                              int64_t total_tokens, int32_t num_cus, int32_t force_partitions,
+                              int32_t partition_tokens, float scale, pa_chunk_plan* plan);
+
+/* One chunk step: the chunk kernel, then the merge when direct == 0
+ * (stream-ordered, allocates nothing). Argument rules as for
+ * paged_attn_decode; q, out: fp32 [B][Tq][Hq][D]. */
+int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table, const int32_t* seq_len,
+                         void* ws, uint64_t ws_bytes, float* out, void* stream);
+
+/*
  * paged_table_update - write a few entries of the device-resident block table
  * and seq_len (lucebox PR #555, Summary: the paging metadata stays resident on
  * the device next to the pool, and a decode step uploads 4 bytes per fresh

@@ -48,6 +48,20 @@ class PaPlan(ctypes.Structure):
                 f"direct={self.direct}, path={self.path}, ws_bytes={self.ws_bytes})")
 
 
+class PaChunkPlan(ctypes.Structure):
+    _fields_ = [("shape", PaShape), ("tq", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("psize", ctypes.c_int32), ("p_max", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("direct", ctypes.c_int32),
+                ("ws_bytes", ctypes.c_uint64)]
+
+    def __repr__(self):
+        s = self.shape
+        return (f"PaChunkPlan(B={s.B}, Tq={self.tq}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D}, "
+                f"psize={self.psize}, p_max={self.p_max}, grid={self.grid}, direct={self.direct}, "
+                f"ws_bytes={self.ws_bytes})")
+
+
 class PaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"[{code}] {msg}")
@@ -87,6 +101,9 @@ def _load():
         "kv_pool_cow": (i32, [vp, u64, i32, P(i32), P(i32)]),
         "kv_pool_refcount": (i32, [vp, i32]),
         "paged_table_update": (i32, [vp, vp, i32, i32, P(i32), i32, vp]),
+        "paged_attn_chunk_plan": (i32, [P(PaShape), i32, i32, i64, i32, i32, i32, ctypes.c_float,
+                                        P(PaChunkPlan)]),
+        "paged_attn_chunk": (i32, [P(PaChunkPlan), vp, vp, vp, vp, vp, vp, u64, vp, vp]),
         "paged_kv_copy_blocks": (i32, [vp, u64, i32, P(i32), P(i32), i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -178,6 +195,24 @@ def paged_attn_status(ws, stream=None) -> int:
     flags = ctypes.c_uint32(0)
     _check(lib.paged_attn_status(_ptr(ws), _stream(stream), ctypes.byref(flags)))
     return flags.value
+
+
+def paged_attn_chunk_plan(shape: PaShape, tq: int, max_seq_len: int, total_tokens: int = 0,
+                          num_cus: int = 0, force_partitions: int = 0, partition_tokens: int = 0,
+                          scale: float = 0.0) -> PaChunkPlan:
+    plan = PaChunkPlan()
+    _check(lib.paged_attn_chunk_plan(ctypes.byref(shape), tq, max_seq_len, total_tokens, num_cus,
+                                     force_partitions, partition_tokens, scale, ctypes.byref(plan)))
+    return plan
+
+
+def paged_attn_chunk(plan: PaChunkPlan, q, k_pool, v_pool, block_table, seq_len, ws, out,
+                     stream=None, ws_bytes: Optional[int] = None) -> None:
+    """Chunk attention (q, out: fp32 [B, Tq, Hq, D]), merge included."""
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib.paged_attn_chunk(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_table), _ptr(seq_len), _ptr(ws), nb, _ptr(out),
+                                _stream(stream)))
 
 
 def _i32_array(values):

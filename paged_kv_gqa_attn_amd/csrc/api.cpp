@@ -25,6 +25,7 @@ constexpr int kMaxB = 1024;
 constexpr int kMaxR = 16;
 constexpr int kTileTokens = 32;
 constexpr int kWavesPerUnit = 4;
+constexpr int kMaxChunk = 4096;   // query tokens per sequence in one chunk call
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -385,6 +386,142 @@ extern "C" int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_
     std::memcpy(a.dst, dst_ids + i0, sizeof(int32_t) * size_t(a.n));
     hipError_t e = launch_copy_blocks(a, st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  }
+  clear_error();
+  return PA_OK;
+}
+
+namespace {
+uint64_t chunk_ws_bytes(const pa_shape& s, int tq, int p_max, bool direct) {
+  uint64_t bytes = 256;
+  if (!direct) bytes += uint64_t(s.B) * uint64_t(tq) * s.Hq * p_max * (2u * uint64_t(s.D) + 8u);
+  return (bytes + 255) & ~uint64_t(255);
+}
+
+int32_t check_chunk_plan(const pa_chunk_plan* p, const char* who) {
+  if (!p) return fail(PA_ERR_INVALID, "%s: null plan", who);
+  int32_t rc = check_shape(&p->shape, who);
+  if (rc) return rc;
+  if (p->tq < 1 || p->tq > kMaxChunk || p->psize < kTileTokens || p->psize % kTileTokens ||
+      p->p_max < 1 || p->grid < 1 || !(p->scale == p->scale) || p->direct != (p->p_max == 1))
+    return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_chunk_plan", who);
+  return PA_OK;
+}
+}  // namespace
+
+extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int32_t max_seq_len,
+                                         int64_t total_tokens, int32_t num_cus, int32_t force_partitions,
+                                         int32_t partition_tokens, float scale, pa_chunk_plan* plan) {
+  const char* who = "paged_attn_chunk_plan";
+  if (!plan) return fail(PA_ERR_INVALID, "%s: null plan", who);
+  int32_t rc = check_shape(shape, who);
+  if (rc) return rc;
+  const pa_shape& s = *shape;
+  if (tq < 1 || tq > kMaxChunk) return fail(PA_ERR_INVALID, "%s: tq %d outside [1, %d]", who, tq, kMaxChunk);
+  const int64_t cap = int64_t(s.max_blocks) * s.block_size;
+  if (max_seq_len < 0 || max_seq_len > cap)
+    return fail(PA_ERR_INVALID, "%s: max_seq_len %d outside [0, max_blocks*block_size=%lld]", who,
+                max_seq_len, (long long)cap);
+  if (total_tokens < 0 || force_partitions < 0 || partition_tokens < 0)
+    return fail(PA_ERR_INVALID, "%s: negative total_tokens/force_partitions/partition_tokens", who);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(PA_ERR_HIP, "%s: could not query the device's compute-unit count", who);
+  }
+  if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
+  const int64_t L = max_seq_len;
+  const int64_t r = s.Hq / s.Hkv;
+  const int64_t qt = (int64_t(tq) * r + 15) / 16;           // 16-row query tiles per kv head
+  const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
+  int64_t psize;
+  if (partition_tokens > 0) {
+    psize = round_up(partition_tokens, kTileTokens);
+  } else if (force_partitions >= 1) {
+    psize = round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
+  } else {
+    // Occupancy-aware partitioning (lucebox PR #555, Summary), counting one
+    // wave per unit and eight waves per compute unit; never so fine that the
+    // partials (2D+8 bytes per query row, written and read once) exceed a
+    // quarter of the K/V bytes a partition streams.
+    const int64_t units_target = int64_t(num_cus) * 8;
+    const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * s.Hkv * qt, units_target)), kTileTokens);
+    const int64_t rbk = pa_row_bytes(s.k_type, s.D), rbv = pa_row_bytes(s.v_type, s.D);
+    const double part = double(tq) * s.Hq * (2.0 * s.D + 8.0) * 2.0;
+    const int64_t floor_tok = round_up(int64_t(std::ceil(part / (0.25 * double(s.Hkv) * double(rbk + rbv)))),
+                                       kTileTokens);
+    psize = std::max<int64_t>(std::max(bal, floor_tok), 128);
+  }
+  if (psize >= L) psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
+  if (psize > INT32_MAX - kTileTokens) return fail(PA_ERR_INVALID, "%s: partition size overflows", who);
+  const int64_t p_max = std::max<int64_t>(1, ceil_div(L, psize));
+  const bool direct = p_max == 1;
+  const int64_t units = std::max<int64_t>(1, int64_t(s.B) * p_max * s.Hkv * qt);
+  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * 8);
+  const uint64_t ws = chunk_ws_bytes(s, tq, int(p_max), direct);
+  std::memset(plan, 0, sizeof *plan);
+  plan->shape = s;
+  plan->tq = tq;
+  plan->scale = scale == 0.0f ? float(1.0 / std::sqrt(double(s.D))) : scale;
+  plan->psize = int32_t(psize);
+  plan->p_max = int32_t(p_max);
+  plan->max_seq_len = max_seq_len;
+  plan->grid = int32_t(grid);
+  plan->num_cus = num_cus;
+  plan->direct = direct ? 1 : 0;
+  plan->ws_bytes = ws;
+  clear_error();
+  return PA_OK;
+}
+
+extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_table, const int32_t* seq_len,
+                                    void* ws, uint64_t ws_bytes, float* out, void* stream) {
+  const char* who = "paged_attn_chunk";
+  int32_t rc = check_chunk_plan(plan, who);
+  if (rc) return rc;
+  if (!q || !k_pool || !v_pool || !seq_len || !ws || !out)
+    return fail(PA_ERR_INVALID, "%s: null q, k_pool, v_pool, seq_len, ws or out", who);
+  if (ws_bytes < plan->ws_bytes)
+    return fail(PA_ERR_INVALID, "%s: workspace of %llu bytes, plan needs %llu", who,
+                (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
+  const pa_shape& s = plan->shape;
+  const uint64_t rows = uint64_t(s.B) * uint64_t(plan->tq) * s.Hq;
+  ChunkArgs a{};
+  a.q = q;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.table = block_table;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.status = static_cast<uint32_t*>(ws);
+  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+  a.part_ml = reinterpret_cast<float*>(a.part_o + rows * plan->p_max * s.D);
+  a.B = s.B; a.Tq = plan->tq; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.r = s.Hq / s.Hkv;
+  a.nblocks = s.nblocks; a.max_blocks = s.max_blocks;
+  a.bs_shift = ilog2_exact(s.block_size);
+  a.psize = plan->psize; a.p_max = plan->p_max; a.grid = plan->grid;
+  a.cap_tokens = int32_t(std::min<int64_t>(int64_t(s.max_blocks) * s.block_size,
+                                           int64_t(plan->p_max) * plan->psize));
+  a.k_type = s.k_type; a.v_type = s.v_type;
+  a.direct = plan->direct;
+  a.qscale = float(double(plan->scale) * 1.4426950408889634);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_chunk(a, st);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  if (!plan->direct) {
+    MergeArgs mg{};
+    mg.part_o = a.part_o;
+    mg.part_ml = a.part_ml;
+    mg.seq_len = seq_len;
+    mg.out = out;
+    mg.B = s.B; mg.Hq = plan->tq * s.Hq; mg.D = s.D; mg.psize = plan->psize; mg.p_max = plan->p_max;
+    mg.cap_tokens = a.cap_tokens;
+    mg.min_len = plan->tq;
+    e = launch_merge(mg, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: merge launch failed: %s", who, hipGetErrorString(e));
   }
   clear_error();
   return PA_OK;

@@ -6,6 +6,9 @@
 // normalised in f16, stable split-softmax merge; llama.cpp PR #13 HRX,
 // Changes: per-block normalisation scale):
 //     M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p
+// The rows are (b, h) for decode and (b, t, h) for chunks (Hq then counts
+// Tq*Hq rows per sequence); a partition that held no key for a row has
+// m = -inf and l = 0 and so weight 0.
 // The merge reads every partial byte once, so it is spread wide: a workgroup
 // takes one (b, h) and 64 output columns; its 256 threads are 8 column octets
 // x 32 partition classes (p mod 32). A thread reads 8 binary16 columns (16
@@ -43,6 +46,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   const int b = bh / a.Hq;
   int L = a.seq_len[b];
   L = L < 0 ? 0 : (L > a.cap_tokens ? a.cap_tokens : L);
+  if (L < a.min_len) L = 0;       // a chunk longer than its sequence (flagged by the chunk kernel)
   const int P = (L + a.psize - 1) / a.psize;
   float* dst = a.out + int64_t(bh) * a.D + col0;
   if (P == 0) {

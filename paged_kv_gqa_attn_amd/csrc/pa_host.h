@@ -72,6 +72,27 @@ constexpr int lds_ring_slots(int kt, int vt, int D) {
                     : kLdsRingBytes / lds_slot_bytes(kt, vt, D, lds_groups(kt, vt, D)));
 }
 
+// Arguments of one chunk launch (multi-token queries), validated on the host.
+struct ChunkArgs {
+  const float* q;          // [B][Tq][Hq][D]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* table;    // nullptr = contiguous layout
+  const int32_t* seq_len;
+  float* out;              // [B][Tq][Hq][D], direct mode
+  uint16_t* part_o;        // [B][Tq*Hq][p_max][D] binary16 bits
+  float* part_ml;          // [B][Tq*Hq][p_max][2]
+  uint32_t* status;
+  int32_t B, Tq, Hq, Hkv, D, r;
+  int32_t nblocks, max_blocks, bs_shift;
+  int32_t psize, p_max, grid;
+  int32_t cap_tokens;
+  int32_t k_type, v_type;
+  int32_t direct;
+  float qscale;            // scale * log2(e)
+};
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
+
 // Whole-block copies inside one pool (copy-on-write); up to kCopyPairs pairs
 // per launch travel in the kernel arguments.
 constexpr int kCopyPairs = 64;
@@ -102,6 +123,7 @@ struct MergeArgs {
   const int32_t* seq_len;
   float* out;
   int32_t B, Hq, D, psize, p_max, cap_tokens;
+  int32_t min_len;         // 0 < seq_len < min_len counts as empty (chunks: Tq)
 };
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

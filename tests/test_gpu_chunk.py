@@ -1,0 +1,148 @@
+"""GPU parity of the chunk path (multi-token queries with causal masking in
+the chunk: llama.cpp PR #13 HRX, Roadmap item 3; TensorFold PR #1418, What:
+paged equals contiguous bit for bit) against oracle.chunk, through the C ABI.
+
+Tolerance as for decode (per-row max-abs error relative to the row's
+max-abs output): 2e-3 when K and V are F16, 5e-3 when either is quantised."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import pa_mod, rel_err_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+PAIRS = [(k, v) for k in synth.FORMATS for v in synth.FORMATS]
+
+
+def _case(lens, Tq, seed, **kw):
+    kw.setdefault("junk", "nan")
+    c = synth.make_case(lens, seed=seed, **kw)
+    g = torch.Generator().manual_seed(seed + 555)
+    qc = torch.randn((c.B, Tq, c.Hq, c.D), generator=g)
+    return c, qc
+
+
+def _plan(c, Tq, **kw):
+    pa = pa_mod()
+    shape = pa.shape_of(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.nblocks, c.max_blocks, c.k_fmt,
+                        c.v_fmt)
+    return pa.paged_attn_chunk_plan(shape, Tq, max(c.seq_lens), total_tokens=sum(c.seq_lens),
+                                    scale=c.scale, **kw)
+
+
+def _run(c, qc, plan, table="case"):
+    pa = pa_mod()
+    g = c.to(DEV)
+    ws = pa.workspace(plan, DEV)
+    out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
+    tab = g.table if table == "case" else table
+    pa.paged_attn_chunk(plan, qc.to(DEV), g.k_pool, g.v_pool, tab, g.seq_len, ws, out)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _ref(c, qc):
+    kp, vp = c.k_pool.numpy().reshape(-1), c.v_pool.numpy().reshape(-1)
+    return oracle.chunk(qc, kp, vp, c.table, c.seq_len, Hkv=c.Hkv, D=c.D, block_size=c.block_size,
+                        k_fmt=c.k_fmt, v_fmt=c.v_fmt, nblocks=c.nblocks, max_blocks=c.max_blocks,
+                        scale=c.scale)
+
+
+def _check(c, qc, out):
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all(), "non-finite output"
+    err = rel_err_rows(got, _ref(c, qc))
+    worst = float(err.max())
+    assert worst <= tol_for(c), f"max row error {worst:.3e}"
+    return worst
+
+
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
+def test_nine_type_pairs(pair, D):
+    seed = 3 * synth.FORMATS.index(pair[0]) + synth.FORMATS.index(pair[1]) + D
+    c, qc = _case([300, 77, 16], 9, seed=seed, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 64}):
+        out, ws = _run(c, qc, _plan(c, 9, **kw))
+        _check(c, qc, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
+@pytest.mark.parametrize("Tq", [1, 2, 16, 33, 130])
+def test_chunk_lengths_and_partitions(Tq):
+    """Query tiles from one to many, partitions that start past some rows'
+    positions (those rows get empty partials), and a chunk as long as the
+    sequence (its first token sees key 0 only)."""
+    c, qc = _case([400, Tq, 1000], Tq, seed=Tq, k_fmt="q4_0", v_fmt="q8_0")
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 96}, {"force_partitions": 5}):
+        out, _ = _run(c, qc, _plan(c, Tq, **kw))
+        _check(c, qc, out)
+
+
+def test_tq_one_is_a_decode_step():
+    """A one-token chunk is a decode step: the same oracle, within tolerance of
+    the decode kernels' output."""
+    pa = pa_mod()
+    c, qc = _case([700, 5, 129], 1, seed=41, k_fmt="q8_0", v_fmt="q4_0")
+    out, _ = _run(c, qc, _plan(c, 1, partition_tokens=128))
+    dc = dataclasses.replace(c, q=qc[:, 0].contiguous())
+    ref = oracle.decode_case(dc)
+    assert float(rel_err_rows(out[:, 0].cpu().double().numpy(), ref).max()) <= tol_for(c)
+
+
+@pytest.mark.parametrize("pair", [("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "f16")])
+def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
+    """TensorFold PR #1418, What: the paged chunk equals the contiguous one bit
+    for bit (same tiles in the same order); repeated runs agree bit for bit."""
+    c, qc = _case([333, 64, 190], 12, seed=7, k_fmt=pair[0], v_fmt=pair[1])
+    cc = synth.contiguous_copy(c)
+    for kw in ({}, {"partition_tokens": 64}):
+        plan = _plan(c, 12, **kw)
+        plan_c = _plan(cc, 12, **kw)             # the contiguous pool has its own nblocks
+        assert (plan_c.psize, plan_c.grid) == (plan.psize, plan.grid)
+        o1, _ = _run(c, qc, plan)
+        o2, _ = _run(cc, qc, plan_c, table=None)
+        o3, _ = _run(c, qc, plan)
+        assert torch.equal(o1, o2) and torch.equal(o1, o3)
+        _check(c, qc, o1)
+
+
+def test_empty_and_too_short_sequences():
+    """L = 0 gives zero rows; 0 < L < Tq gives zero rows and the seq_len
+    status bit; the other sequences are untouched."""
+    pa = pa_mod()
+    c, qc = _case([0, 3, 50], 6, seed=13, k_fmt="q4_0", v_fmt="f16")
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 32}):
+        plan = _plan(c, 6, **kw)
+        g = c.to(DEV)
+        ws = pa.workspace(plan, DEV)
+        out = torch.full(tuple(qc.shape), float("nan"), device=DEV)
+        pa.paged_attn_chunk(plan, qc.to(DEV), g.k_pool, g.v_pool, g.table, g.seq_len, ws, out)
+        assert pa.paged_attn_status(ws) == pa.PA_STATUS_BAD_SEQ_LEN
+        o = out.cpu()
+        assert torch.all(o[0] == 0) and torch.all(o[1] == 0)
+        ok = dataclasses.replace(c, B=1, seq_lens=[50], seq_len=c.seq_len[2:], q=c.q[2:],
+                                 table=c.table[2:])
+        err = rel_err_rows(o[2:].double().numpy(), _ref(ok, qc[2:]))
+        assert float(err.max()) <= tol_for(c)
+
+
+def test_bad_block_id_sets_status_and_nans_only_that_sequence():
+    pa = pa_mod()
+    c, qc = _case([200, 150], 4, seed=17, k_fmt="q4_0", v_fmt="q4_0", junk="zero")
+    bad_table = c.table.clone()
+    bad_table[1, 3] = c.nblocks + 5
+    plan = _plan(c, 4, partition_tokens=64)
+    out, ws = _run(c, qc, plan, table=bad_table.to(DEV))
+    assert pa.paged_attn_status(ws) & pa.PA_STATUS_BAD_BLOCK_ID
+    o = out.cpu()
+    assert torch.isnan(o[1]).all()
+    good = dataclasses.replace(c, B=1, seq_lens=[200], seq_len=c.seq_len[:1], q=c.q[:1],
+                               table=c.table[:1])
+    assert float(rel_err_rows(o[:1].double().numpy(), _ref(good, qc[:1])).max()) <= tol_for(c)

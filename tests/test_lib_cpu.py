@@ -43,7 +43,7 @@ def test_header_declares_the_expected_entry_points():
                  "paged_kv_gather", "paged_attn_status", "kv_pool_alloc", "kv_pool_release",
                  "kv_pool_create", "kv_pool_destroy", "kv_pool_reset", "pa_last_error",
                  "kv_pool_fork", "kv_pool_cow", "kv_pool_refcount", "paged_table_update",
-                 "paged_kv_copy_blocks"]:
+                 "paged_kv_copy_blocks", "paged_attn_chunk_plan", "paged_attn_chunk"]:
         assert must in names, must
 
 
@@ -260,3 +260,36 @@ def test_copy_blocks_refusals_before_any_launch():
     rc = pa.lib.paged_kv_copy_blocks(fake + 8, 64, 4, _i32([0]), _i32([1]), 1, 0)
     assert rc == pa.PA_ERR_INVALID and "aligned" in pa.pa_last_error()
     assert pa.lib.paged_kv_copy_blocks(fake, 64, 4, None, None, 0, 0) == pa.PA_OK
+
+
+def test_chunk_plan_partitions_and_workspace():
+    """paged_attn_chunk_plan: one wave per (sequence, partition, kv head,
+    16-row query tile), about eight per compute unit; partials of 2D+8 bytes
+    per query row and partition."""
+    p = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.tq == 8 and p.psize % 32 == 0 and p.direct == 0
+    assert p.p_max == -(-32768 // p.psize)
+    units = 8 * p.p_max * 4 * 3                      # 8*6 = 48 rows per kv head: 3 tiles
+    assert p.grid == min(units, 256 * 8)
+    assert p.ws_bytes == -(-(256 + 8 * 8 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
+    d = pa.paged_attn_chunk_plan(_shape(B=1), 16, 200, num_cus=256)
+    assert d.direct == 1 and d.p_max == 1 and d.ws_bytes == 256
+    f = pa.paged_attn_chunk_plan(_shape(), 4, 1000, num_cus=256, partition_tokens=64)
+    assert f.psize == 64 and f.p_max == 16
+
+
+def test_chunk_refusals_before_any_launch():
+    for tq in (0, 4097):
+        with pytest.raises(pa.PaError) as e:
+            pa.paged_attn_chunk_plan(_shape(), tq, 100, num_cus=256)
+        assert e.value.code == pa.PA_ERR_INVALID and "paged_attn_chunk_plan" in str(e.value)
+    bogus = pa.PaChunkPlan()
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_chunk(bogus, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                            stream=0, ws_bytes=1 << 20)
+    assert e.value.code == pa.PA_ERR_INVALID and "paged_attn_chunk" in str(e.value)
+    p = pa.paged_attn_chunk_plan(_shape(), 4, 4096, num_cus=256)
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_chunk(p, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                            stream=0, ws_bytes=int(p.ws_bytes) - 1)
+    assert e.value.code == pa.PA_ERR_INVALID and "workspace" in str(e.value)
