@@ -26,6 +26,8 @@ constexpr int kMaxR = 16;
 constexpr int kTileTokens = 32;
 constexpr int kWavesPerUnit = 4;
 constexpr int kMaxChunk = 4096;   // query tokens per sequence in one chunk call
+// MI355X dense f16 MFMA peak over HBM peak (2.5 PFLOP/s / 8 TB/s), flop per byte
+constexpr double kFlopsPerByte = 2.5e15 / 8.0e12;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -434,7 +436,8 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
   const int64_t L = max_seq_len;
   const int64_t r = s.Hq / s.Hkv;
-  const int64_t qt = (int64_t(tq) * r + 15) / 16;           // 16-row query tiles per kv head
+  const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
+  const int64_t qt = (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // workgroup row blocks per kv head
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {
@@ -442,24 +445,40 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   } else if (force_partitions >= 1) {
     psize = round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
   } else {
-    // Occupancy-aware partitioning (lucebox PR #555, Summary), counting one
-    // wave per unit and eight waves per compute unit; never so fine that the
-    // partials (2D+8 bytes per query row, written and read once) exceed a
-    // quarter of the K/V bytes a partition streams.
-    const int64_t units_target = int64_t(num_cus) * 8;
-    const int64_t bal = round_up(std::max<int64_t>(1, ceil_div(tok * s.Hkv * qt, units_target)), kTileTokens);
+    // Occupancy-aware partitioning (lucebox PR #555, Summary), counting the
+    // workgroups a compute unit holds. Partials cost 2D+8 bytes per query row
+    // and partition, written and read once; a partition is never so short
+    // that this exceeds a quarter of what it saves, i.e. a quarter of the K/V
+    // bytes it streams (memory-bound chunks) or of the HBM time equal to its
+    // MFMA work at the machine's flop:byte ratio (compute-bound chunks,
+    // 4*D flops per query row and key), whichever floor is lower.
+    // Among the sizes above that floor, take the one that finishes soonest:
+    // the units run in ceil(units / slots) rounds of psize keys each (a
+    // round only partly filled costs as much as a full one).
+    const int64_t slots = int64_t(num_cus) * chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
     const int64_t rbk = pa_row_bytes(s.k_type, s.D), rbv = pa_row_bytes(s.v_type, s.D);
     const double part = double(tq) * s.Hq * (2.0 * s.D + 8.0) * 2.0;
-    const int64_t floor_tok = round_up(int64_t(std::ceil(part / (0.25 * double(s.Hkv) * double(rbk + rbv)))),
-                                       kTileTokens);
-    psize = std::max<int64_t>(std::max(bal, floor_tok), 128);
+    const double floor_hbm = part / (0.25 * double(s.Hkv) * double(rbk + rbv));
+    const double floor_mfma = part * kFlopsPerByte / (0.25 * double(tq) * s.Hq * 4.0 * s.D);
+    const int64_t floor_tok = std::max<int64_t>(
+        round_up(int64_t(std::ceil(std::min(floor_hbm, floor_mfma))), kTileTokens), 128);
+    psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
+    int64_t best = -1;
+    for (int64_t parts = 1; parts <= 64; ++parts) {
+      const int64_t ps = round_up(std::max<int64_t>(1, ceil_div(L, parts)), kTileTokens);
+      if (ps < floor_tok && parts > 1) break;
+      const int64_t bp = std::min<int64_t>(int64_t(s.B) * ceil_div(std::max<int64_t>(L, 1), ps),
+                                           ceil_div(tok, ps) + s.B);
+      const int64_t cost = ceil_div(std::max<int64_t>(1, bp * s.Hkv * qt), slots) * ps;
+      if (best < 0 || cost < best) { best = cost; psize = ps; }
+    }
   }
   if (psize >= L) psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
   if (psize > INT32_MAX - kTileTokens) return fail(PA_ERR_INVALID, "%s: partition size overflows", who);
   const int64_t p_max = std::max<int64_t>(1, ceil_div(L, psize));
   const bool direct = p_max == 1;
   const int64_t units = std::max<int64_t>(1, int64_t(s.B) * p_max * s.Hkv * qt);
-  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * 8);
+  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D));
   const uint64_t ws = chunk_ws_bytes(s, tq, int(p_max), direct);
   std::memset(plan, 0, sizeof *plan);
   plan->shape = s;
@@ -508,6 +527,7 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.k_type = s.k_type; a.v_type = s.v_type;
   a.direct = plan->direct;
   a.qscale = float(double(plan->scale) * 1.4426950408889634);
+  a.nt = chunk_wave_tiles(int64_t(plan->tq) * a.r, s.D);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_chunk(a, st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

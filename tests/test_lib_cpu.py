@@ -263,14 +263,16 @@ def test_copy_blocks_refusals_before_any_launch():
 
 
 def test_chunk_plan_partitions_and_workspace():
-    """paged_attn_chunk_plan: one wave per (sequence, partition, kv head,
-    16-row query tile), about eight per compute unit; partials of 2D+8 bytes
-    per query row and partition."""
+    """paged_attn_chunk_plan: a four-wave workgroup per (sequence, partition,
+    kv head, 64 query rows at D=256), two per compute unit; partials of 2D+8
+    bytes per query row and partition."""
     p = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.tq == 8 and p.psize % 32 == 0 and p.direct == 0
     assert p.p_max == -(-32768 // p.psize)
-    units = 8 * p.p_max * 4 * 3                      # 8*6 = 48 rows per kv head: 3 tiles
-    assert p.grid == min(units, 256 * 8)
+    units = 8 * p.p_max * 4 * 1                      # 8*6 = 48 rows per kv head: one block
+    assert p.grid == min(units, 256 * 2)
+    big = pa.paged_attn_chunk_plan(_shape(B=1), 512, 8192, num_cus=256)
+    assert big.grid == min(1 * big.p_max * 4 * 48, 512)      # 3072 rows: 48 blocks of 64
     assert p.ws_bytes == -(-(256 + 8 * 8 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
     d = pa.paged_attn_chunk_plan(_shape(B=1), 16, 200, num_cus=256)
     assert d.direct == 1 and d.p_max == 1 and d.ws_bytes == 256
