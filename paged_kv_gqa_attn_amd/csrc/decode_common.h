@@ -432,7 +432,7 @@ template <int D> struct VFmt<kQ4_0, D> : VQuantBase<kQ4_0, D> {
 // Scheduling: live partitions of sequence b are [0, ceil(L_b / psize)). The
 // workgroup computes the exclusive prefix unit_start[b] of their counts
 // (unit_start[B] = total) and the clamped lengths lens[b] in LDS; `scan` is
-// kThreads words of LDS scratch. seq_len outside [0, cap_tokens] sets status
+// kThreads/64 words of LDS scratch. seq_len outside [0, cap_tokens] sets status
 // bit 2 and is clamped.
 // ===========================================================================
 template <int kThreads>
@@ -451,21 +451,25 @@ __device__ __forceinline__ void live_partition_prefix(const DecodeArgs& a, int32
     local += (L + a.psize - 1) / a.psize;
   }
   if (st && blockIdx.x == 0) atomicOr(a.status, st);
-  // block-wide inclusive scan of `local` (Hillis-Steele over LDS)
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  // block-wide inclusive scan of `local`: within each wave by lane shuffles,
+  // then the wave totals through LDS (one barrier instead of one per step)
+  static_assert(kThreads % 64 == 0, "whole waves");
+  const int lane = tid & 63, w = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  int run = scan[tid] - local;
+  if (lane == 63) scan[w] = incl;
+  __syncthreads();
+  for (int k = 0; k < w; ++k) incl += scan[k];
+  int run = incl - local;
   for (int b = b0; b < b0 + per && b < a.B; ++b) {
     unit_start[b] = run;
     run += (lens[b] + a.psize - 1) / a.psize;
   }
-  if (tid == kThreads - 1) unit_start[a.B] = scan[tid];
+  if (tid == kThreads - 1) unit_start[a.B] = incl;
   __syncthreads();
 }
 

@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kNidS = 512;     // block ids staged per segment of a partition
+constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
 
 template <int KT, int VT, int D>
 struct LdsLayout {
@@ -145,7 +146,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   int32_t* unit_start = reinterpret_cast<int32_t*>(smem + a.ring_bytes);
   int32_t* lens = unit_start + (a.B + 1);
   int32_t* ids = unit_start + (((2 * a.B + 1) + 3) & ~3);
-  float* qs = reinterpret_cast<float*>(ring);          // q staging at unit start
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,30 +210,85 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
                                                  16u * vstride, RowRot<LY::RBV>::v);
     }
 
-    // ---- stage the 4r query rows of the quad (scaled by scale*log2 e) -------
-    __syncthreads();                        // the previous unit is done with the ring
-    {
-      const float* qg = a.q + (int64_t(b) * a.Hq + int64_t(4 * hg) * a.r) * D;
-      for (int i = tid; i < a.r * D; i += kThreads) {
-        float4 v = reinterpret_cast<const float4*>(qg)[i];
-        v.x *= a.qscale; v.y *= a.qscale; v.z *= a.qscale; v.w *= a.qscale;
-        reinterpret_cast<float4*>(qs)[i] = v;
-      }
-    }
-    __syncthreads();
+    // ---- the first segment's block ids and this lane's q values ------------
+    // Both global reads are in flight together; the first steps' DMA is then
+    // issued before the Q operand is built, so its latency covers that work.
+    int seg_t0 = t_begin;
+    int seg_t1 = min(t_end, seg_t0 + seg_tokens);
+    int jb0 = seg_t0 >> a.bs_shift;
+    int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+    // (every thread reads a live entry, so that the reads need no branch and
+    // are all in flight at once; entries past nb are not used)
+    int32_t idr[kIdRegs];
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k)
+      idr[k] = block_of(a.table, b, a.max_blocks, jb0 + min(tid + k * kThreads, nb - 1));
     // Q operand: column n = lane%16 holds head g*r+n (zero when n >= r)
-    f16x8 qop[S];
+    float qv[S][8];
     {
       const int n = m < a.r ? m : a.r - 1;
+      const float* qw = a.q + (int64_t(b) * a.Hq + int64_t(g) * a.r + n) * D;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[s][i] = qw[KF::dslot(j, s, i)];
+    }
+    __syncthreads();                        // the previous unit is done with the ring and ids[]
+    int bad = 0;
+    {
+      int badl = 0;
+#pragma unroll
+      for (int k = 0; k < kIdRegs; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < nb) {
+          int32_t id = idr[k];
+          if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+          ids[i] = id;
+        }
+      }
+      bad |= __syncthreads_or(badl);        // also publishes ids[]
+    }
+
+    // ---- DMA of step s of the current segment into ring slot s % R (each
+    // wave its share) ------------------------------------------------------------
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      const uint32_t slot = uint32_t(s % LY::R) * LY::SLOT;   // ring starts at LDS byte 0
+      const int t0 = seg_t0 + s * T;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int tg = t0 + 16 * gi;
+        const bool live = tg < seg_t1;
+        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+        const int slot0 = live ? (tg & bs_mask) : 0;
+        const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
+                                    live ? 16u * kstride : 0u);
+        const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
+                                    live ? 16u * vstride : 0u);
+#pragma unroll
+        for (int sub = 0; sub < LY::NIK; ++sub) {
+          const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
+          if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+        }
+#pragma unroll
+        for (int sub = 0; sub < LY::NIV; ++sub) {
+          const int q = G * LY::NIK + gi * LY::NIV + sub;
+          if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+        }
+      }
+    };
+    int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
+    for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);
+
+    f16x8 qop[S];
+    {
       const float keep = m < a.r ? 1.0f : 0.0f;
-      const float* qw = qs + (wave * a.r + n) * D;
 #pragma unroll
       for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           // Q4_0: the high-nibble slots meet K values in the x16 frame
           const float hs = (kKFold && KFmtHi<KT, D>::hi(i)) ? 0.0625f : 1.0f;
-          qop[s][i] = f16(qw[KF::dslot(j, s, i)] * keep * hs);
+          qop[s][i] = f16(qv[s][i] * a.qscale * keep * hs);
         }
     }
 
@@ -264,49 +319,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 vcorr = f32x4{0.f, 0.f, 0.f, 0.f};   // Q4_0 V: sum_t d_t p_t per row block
     int vshift = 0;                            // Q4_0 V: acc holds the sums times 2^-vshift
-    int bad = 0;
 
-    for (int seg_t0 = t_begin; seg_t0 < t_end; seg_t0 += seg_tokens) {
-      const int seg_t1 = min(t_end, seg_t0 + seg_tokens);
-      const int jb0 = seg_t0 >> a.bs_shift;
-      const int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
-      __syncthreads();                       // q staging, ids[] and the ring are free
-      int badl = 0;
-      for (int i = tid; i < nb; i += kThreads) {
-        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
-        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
-        ids[i] = id;
-      }
-      bad |= __syncthreads_or(badl);         // also publishes ids[]
-      const int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
-
-      // ---- DMA of step s into ring slot s&1 (each wave its share) ----------
-      auto issue = [&](int s) __attribute__((always_inline)) {
-        const uint32_t slot = uint32_t(s % LY::R) * LY::SLOT;   // ring starts at LDS byte 0
-        const int t0 = seg_t0 + s * T;
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-          const int tg = t0 + 16 * gi;
-          const bool live = tg < seg_t1;
-          const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
-          const int slot0 = live ? (tg & bs_mask) : 0;
-          const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
-                                      live ? 16u * kstride : 0u);
-          const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
-                                      live ? 16u * vstride : 0u);
-#pragma unroll
-          for (int sub = 0; sub < LY::NIK; ++sub) {
-            const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
-            if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
-          }
-#pragma unroll
-          for (int sub = 0; sub < LY::NIV; ++sub) {
-            const int q = G * LY::NIK + gi * LY::NIV + sub;
-            if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
-          }
-        }
-      };
-
+    for (;;) {
       // ---- compute step s from LDS: scores, online softmax (exp2), PV -------
       auto compute = [&](int s) __attribute__((always_inline)) {
         const unsigned char* slot = ring + (s % LY::R) * LY::SLOT;
@@ -474,7 +488,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
       };
 
       // ---- the ring: steps s+1 .. s+R-2 in flight while step s is computed -
-      for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);
+      // (the first R-1 steps of the segment are already issued)
       for (int s = 0; s < nsteps; ++s) {
         // every wave's DMA of step s has landed (this wave may still have the
         // DMA of the later steps outstanding: cw instructions each), and every
@@ -488,6 +502,23 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
         if (s + LY::R - 1 < nsteps) issue(s + LY::R - 1);
         compute(s);
       }
+
+      // ---- next segment: its block ids, then the first steps' DMA ----------
+      seg_t0 = seg_t1;
+      if (seg_t0 >= t_end) break;
+      seg_t1 = min(t_end, seg_t0 + seg_tokens);
+      jb0 = seg_t0 >> a.bs_shift;
+      nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // ids[] and the ring are free
+      int badl = 0;
+      for (int i = tid; i < nb; i += kThreads) {
+        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
+      }
+      bad |= __syncthreads_or(badl);         // also publishes ids[]
+      nsteps = (seg_t1 - seg_t0 + T - 1) / T;
+      for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);
     }
 
     const float l_run = sum_over_rows(l_lane);
@@ -532,13 +563,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   }
 }
 
-// LDS bytes of a launch: the ring (or the q staging of 4r rows, if larger),
-// then unit_start[B+1] | lens[B] | pad | ids[kNidS+1] (a segment of kNidS
-// blocks' worth of tokens that starts inside a block touches kNidS+1 blocks).
+// LDS bytes of a launch: the ring, then unit_start[B+1] | lens[B] | pad |
+// ids[kNidS+1] (a segment of kNidS blocks' worth of tokens that starts
+// inside a block touches kNidS+1 blocks).
 template <int KT, int VT, int D>
 size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
   using LY = LdsLayout<KT, VT, D>;
-  const size_t ring = std::max<size_t>(size_t(LY::R) * LY::SLOT, size_t(16) * a.r * D);
+  const size_t ring = size_t(LY::R) * LY::SLOT;
   *ring_bytes = int((ring + 15) & ~size_t(15));
   return size_t(*ring_bytes) + 4 * size_t(((2 * a.B + 1) + 3) & ~3) + 4 * size_t((kNidS + 1 + 3) & ~3);
 }

@@ -13,9 +13,15 @@
 // takes one (b, h) and 64 output columns; its 256 threads are 8 column octets
 // x 32 partition classes (p mod 32). A thread reads 8 binary16 columns (16
 // bytes) of each of its partitions and accumulates w_p o_p in fp32; the 32
-// classes are then summed through LDS in a fixed order. The first kPre
-// partitions of every class are loaded before the max is reduced, so their
-// latency overlaps the reduction.
+// classes are then summed in a fixed order (lane butterflies within a wave,
+// then the four waves through LDS). The first kPre partitions of every class
+// are loaded together with the m values the max needs, so one memory latency
+// covers both, and the max is reduced with lane shuffles and one barrier.
+// With many rows of few partitions (p_max <= kRowsMergeMax, e.g. a prefill
+// chunk's Tq*Hq rows) that layout leaves most threads idle and launches tens
+// of thousands of workgroups, and merge_rows_kernel is used instead: one
+// thread per (row, 8 output columns) walks the row's partitions in order, 8
+// rows per workgroup at D=256.
 // Loop bounds are the runtime partition count (llama.cpp PR #13, the
 // SGPR-exhaustion fix: a constant-folded bound fully unrolled the reduction).
 #include "pa_device.h"
@@ -36,10 +42,13 @@ __device__ __forceinline__ void axpy8(float* acc, float w, const f16x8& v) {
 }
 
 __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
-  __shared__ float red[kThreads];
-  __shared__ float part[kClasses][kCols + 1];
-  __shared__ float wpart[kClasses];
+  constexpr int kWaves = kThreads / 64;
+  __shared__ float wmax[kWaves];
+  __shared__ int wnan[kWaves];
+  __shared__ float part[kWaves][kCols];
+  __shared__ float wpart[kWaves];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int chunks = a.D / kCols;
   const int bh = blockIdx.x / chunks;
   const int col0 = (blockIdx.x - bh * chunks) * kCols;
@@ -57,52 +66,61 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   const int q = tid % kOcts, c = tid / kOcts;
   const f16* o = reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * a.D + col0 + 8 * q;
 
-  // the first kPre partitions of this thread's class, loaded ahead
+  // Loads in flight together: the first kPre partitions of this thread's
+  // class with their (m, l), and m of partition tid. Every address is a live
+  // partition (clamped to P-1), so no load waits behind a branch.
   f16x8 pre[kPre];
+  float2 mlp[kPre];
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
-    const int p = c + u * kClasses;
-    pre[u] = p < P ? *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D) : f16x8{};
+    const int pc = min(c + u * kClasses, P - 1);
+    pre[u] = *reinterpret_cast<const f16x8*>(o + int64_t(pc) * a.D);
+    mlp[u] = *reinterpret_cast<const float2*>(ml + 2 * pc);
   }
-
-  // pass 1: M = max_p m_p; a NaN m (a partition that met a bad block id)
-  // turns into a NaN max through the comparison below
-  float mx = -INFINITY;
-  bool nan_seen = false;
-  for (int p = tid; p < P; p += kThreads) {
+  float mx = ml[2 * min(tid, P - 1)];
+  bool nan_seen = mx != mx;
+  for (int p = tid + kThreads; p < P; p += kThreads) {
     const float mp = ml[2 * p];
     nan_seen |= mp != mp;
     mx = fmaxf(mx, mp);
   }
-  red[tid] = nan_seen ? __builtin_nanf("") : mx;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) {
-      const float x = red[tid], y = red[tid + off];
-      red[tid] = (x != x || y != y) ? __builtin_nanf("") : fmaxf(x, y);
-    }
-    __syncthreads();
-  }
-  const float M = red[0];
 
-  // pass 2: thread (octet q, class c) sums w_p o_p[8q..8q+7] over p = c mod kClasses
+  // M = max_p m_p: within the wave by lane shuffles, then over the waves. A
+  // NaN m (a partition that met a bad block id) makes the row NaN.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  nan_seen = __any(nan_seen);
+  if (lane == 0) {
+    wmax[wave] = mx;
+    wnan[wave] = nan_seen;
+  }
+  __syncthreads();
+  float M = wmax[0];
+  int any_nan = wnan[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    M = fmaxf(M, wmax[k]);
+    any_nan |= wnan[k];
+  }
+
+  // thread (octet q, class c) sums w_p o_p[8q..8q+7] over p = c mod kClasses
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
-    const int p = c + u * kClasses;
-    if (p < P) {
-      const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
-      wsum += w;
-      axpy8(acc, w, pre[u]);
-    }
+    // a clamped (dead) slot gets weight 0 and adds exactly 0
+    const float w = c + u * kClasses < P ? __builtin_amdgcn_exp2f(mlp[u].x - M) * mlp[u].y : 0.0f;
+    wsum += w;
+    axpy8(acc, w, pre[u]);
   }
   int p = c + kPre * kClasses;
   for (; p + kClasses < P; p += 2 * kClasses) {
     const f16x8 v0 = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
     const f16x8 v1 = *reinterpret_cast<const f16x8*>(o + int64_t(p + kClasses) * a.D);
-    const float w0 = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
-    const float w1 = __builtin_amdgcn_exp2f(ml[2 * (p + kClasses)] - M) * ml[2 * (p + kClasses) + 1];
+    const float2 x0 = *reinterpret_cast<const float2*>(ml + 2 * p);
+    const float2 x1 = *reinterpret_cast<const float2*>(ml + 2 * (p + kClasses));
+    const float w0 = __builtin_amdgcn_exp2f(x0.x - M) * x0.y;
+    const float w1 = __builtin_amdgcn_exp2f(x1.x - M) * x1.y;
     wsum += w0;
     axpy8(acc, w0, v0);
     wsum += w1;
@@ -110,32 +128,111 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   }
   if (p < P) {
     const f16x8 v = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
-    const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * p);
+    const float w = __builtin_amdgcn_exp2f(x.x - M) * x.y;
     wsum += w;
     axpy8(acc, w, v);
   }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) part[c][8 * q + k] = acc[k];
-  if (q == 0) wpart[c] = wsum;
-  __syncthreads();
 
-  // pass 3: sum the classes in a fixed order and normalise
+  // sum the classes in a fixed order: the wave's 8 classes (lane bits 3..5)
+  // by butterflies, then the waves through LDS
+#pragma unroll
+  for (int off = kOcts; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], off, 64);
+    wsum += __shfl_xor(wsum, off, 64);
+  }
+  if (lane < kOcts) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[wave][8 * lane + k] = acc[k];
+    if (lane == 0) wpart[wave] = wsum;
+  }
+  __syncthreads();
   if (tid < kCols) {
     float s = part[0][tid];
     float W = wpart[0];
-    for (int k = 1; k < kClasses; ++k) {
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
       s += part[k][tid];
       W += wpart[k];
     }
-    dst[tid] = M != M ? __builtin_nanf("") : s / W;
+    dst[tid] = any_nan ? __builtin_nanf("") : s / W;
   }
+}
+
+constexpr int kRowsMergeMax = 8;          // partitions per row it handles
+constexpr int kRowsMergeMinRows = 1024;   // fewer rows: the wide layout has more parallelism
+
+__global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a) {
+  const int octs = a.D / 8;
+  const int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t rows = int64_t(a.B) * a.Hq;
+  if (gid >= rows * octs) return;
+  const int64_t bh = gid / octs;
+  const int q = int(gid - bh * octs);
+  const int b = int(bh / a.Hq);
+  int L = a.seq_len[b];
+  L = L < 0 ? 0 : (L > a.cap_tokens ? a.cap_tokens : L);
+  if (L < a.min_len) L = 0;       // a chunk longer than its sequence (flagged by the chunk kernel)
+  const int P = (L + a.psize - 1) / a.psize;
+  float* dst = a.out + bh * a.D + 8 * q;
+  if (P == 0) {
+    *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const float* ml = a.part_ml + bh * a.p_max * 2;
+  const f16* o = reinterpret_cast<const f16*>(a.part_o) + bh * a.p_max * a.D + 8 * q;
+  // every load reads a live partition (p clamped to P-1), so that none needs
+  // a branch and all are in flight at once; dead slots are then masked
+  f16x8 v[kRowsMergeMax];
+  float mp[kRowsMergeMax], lp[kRowsMergeMax];
+#pragma unroll
+  for (int p = 0; p < kRowsMergeMax; ++p)
+    v[p] = *reinterpret_cast<const f16x8*>(o + int64_t(min(p, P - 1)) * a.D);
+#pragma unroll
+  for (int p = 0; p < kRowsMergeMax; ++p) {
+    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * min(p, P - 1));
+    mp[p] = p < P ? x.x : -INFINITY;
+    lp[p] = p < P ? x.y : 0.0f;
+  }
+  // a NaN m (a partition that met a bad block id) makes the row NaN
+  float M = -INFINITY;
+  bool nan_seen = false;
+#pragma unroll
+  for (int p = 0; p < kRowsMergeMax; ++p) {
+    nan_seen |= mp[p] != mp[p];
+    M = fmaxf(M, mp[p]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float W = 0.0f;
+  // (a dead slot has weight 2^-inf * 0 = 0 and holds a live partition's
+  // finite values, so it adds exactly 0: no branch)
+#pragma unroll
+  for (int p = 0; p < kRowsMergeMax; ++p) {
+    const float w = __builtin_amdgcn_exp2f(mp[p] - M) * lp[p];
+    W += w;
+    axpy8(acc, w, v[p]);
+  }
+  float r[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = nan_seen ? __builtin_nanf("") : acc[k] / W;
+  *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+  *reinterpret_cast<float4*>(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.D % kCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq * (a.D / kCols)), dim3(kThreads), 0, stream, a);
+  if (a.p_max <= kRowsMergeMax && int64_t(a.B) * a.Hq >= kRowsMergeMinRows) {
+    const int64_t threads = int64_t(a.B) * a.Hq * (a.D / 8);
+    const int64_t blocks = (threads + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_rows_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq * (a.D / kCols)), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

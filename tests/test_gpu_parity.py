@@ -181,13 +181,27 @@ def _ws_partials(ws, B, Hq, P, D):
     return o.double().numpy(), ml.double().numpy()
 
 
-def test_merge_kernel_on_oracle_partials():
+MERGE_CASES = {
+    "p5": ([300, 0, 97, 31], 8, 2),
+    "p10": ([600, 0, 97, 31], 8, 2),
+    "p32": ([2000, 0, 97, 31], 8, 2),
+    # 44 sequences x 24 heads = 1056 rows of at most 5 partitions: the
+    # row-per-thread merge layout
+    "rows_p5": ([0, 1, 64, 65, 300, 17, 128, 129] * 5 + [0, 300, 33, 200], 24, 4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_CASES))
+def test_merge_kernel_on_oracle_partials(name):
     """Write the oracle's own partials, o rounded to binary16, into the
     documented workspace layout and check the GPU merge against the oracle
     merge of the same values; and against the unrounded partials within what
-    binary16 rounding of o can move the result (2^-11 of the largest |o_p|)."""
+    binary16 rounding of o can move the result (2^-11 of the largest |o_p|).
+    Both merge layouts are covered: few rows (any partition count) and many
+    rows of at most 8 partitions."""
     pa = pa_mod()
-    case = _case([300, 0, 97, 31], k_fmt="f16", v_fmt="q8_0", seed=23, Hq=8, Hkv=2)
+    lens, Hq, Hkv = MERGE_CASES[name]
+    case = _case(lens, k_fmt="f16", v_fmt="q8_0", seed=23, Hq=Hq, Hkv=Hkv)
     plan = plan_for(case, partition_tokens=64)
     m, l, o, n = _oracle_partials(case, plan.psize)
     B, Hq, P, D = o.shape
@@ -208,7 +222,9 @@ def test_merge_kernel_on_oracle_partials():
     ref = oracle.merge(m, l, o, n)
     bound = 2.0 ** -11 * np.abs(o).max(axis=(2, 3)) + 1e-6 * np.abs(ref).max(axis=-1) + 1e-7
     assert np.all(np.abs(got - ref).max(axis=-1) <= bound)
-    assert np.all(got[1] == 0.0)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b] == 0.0)
 
 
 @pytest.mark.parametrize("path", PATHS)
