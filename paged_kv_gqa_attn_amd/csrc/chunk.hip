@@ -266,6 +266,8 @@ chunk_kernel(const ChunkArgs a) {
 #pragma unroll
             for (int k = 0; k < NTW; ++k) sc[k][gi] = mfma(kop, qop[k][s], sc[k][gi]);
           }
+        if constexpr (NTW == 1) mfma_settle(sc[0][0], sc[0][1]);
+        else mfma_settle(sc[0][0], sc[0][1], sc[1][0], sc[1][1]);
         // causal and end-of-partition mask, only where some row's limit falls
         // inside the tile
         if (t0 + kTile - 1 > lim_min) {

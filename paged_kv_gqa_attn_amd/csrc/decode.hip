@@ -233,6 +233,8 @@ decode_kernel(const DecodeArgs a) {
         for (int s = 0; s < S; ++s)
 #pragma unroll
           for (int gi = 0; gi < NG; ++gi) sc[gi] = mfma(KF::op(t.k[gi], s, ksh, mg), qop[s], sc[gi]);
+        if constexpr (NG == 1) mfma_settle(sc[0]);
+        else mfma_settle(sc[0], sc[1]);
         if (!full) {
 #pragma unroll
           for (int gi = 0; gi < NG; ++gi)

@@ -326,6 +326,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
         const unsigned char* slot = ring + (s % LY::R) * LY::SLOT;
         const int t0 = seg_t0 + s * T;
         const bool full = t0 + T <= t_end;
+        // tokens of the step left before t_end (wave-uniform): the row tests
+        // below compare it, less a constant, with the lane's fixed 4j or m, so
+        // that they cost no per-step vector arithmetic
+        const int rem = t_end - t0;
         typename KF::Raw kr[G];
         typename VF::Raw vr[2 * NP];
 #pragma unroll
@@ -341,31 +345,42 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           for (int gi = 0; gi < G; ++gi)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (t0 + 16 * gi + 4 * j + i >= t_end) VF::kill(vr[4 * gi + i]);
+              if (4 * j >= rem - 16 * gi - i) VF::kill(vr[4 * gi + i]);
         }
         // The fma form of the Q4_0 conversion needs |d| < 64 (-1024*d finite):
         // a step whose live scales exceed that is converted with d * 2^-k (exact
         // scaling) and the results are scaled back by 2^k in fp32, so every
         // step runs the same code.
-        // (the largest |d| of the lane as f16 bits; the shift is only worked
-        // out when some lane's reaches 64)
+        // (the largest |d| of the lane, as an f16 max with the abs modifier -
+        // three scales per instruction; a NaN scale does not count, it makes
+        // its values NaN whatever the shift; the shift is only worked out when
+        // some lane's reaches 64)
         int kk = 0, kv = 0;
         if constexpr (kKFold) {
-          uint32_t kb = 0;
+          f16 dk = f16(0.0f);
+          if (full) {
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) {
-            const bool live_row = full || t0 + 16 * gi + m < t_end;   // dead K rows are masked below
+            for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-            for (int bl = 0; bl < KF_NBL; ++bl)
-              kb = max(kb, live_row ? uint32_t(bitcast<uint16_t>(KF::dscale(kr[gi], bl, ksh))) & 0x7FFFu : 0u);
+              for (int bl = 0; bl < KF_NBL; ++bl)
+                dk = __builtin_fmaxf16(dk, __builtin_fabsf16(KF::dscale(kr[gi], bl, ksh)));
+          } else {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const bool live_row = m < rem - 16 * gi;   // dead K rows are masked below
+#pragma unroll
+              for (int bl = 0; bl < KF_NBL; ++bl)
+                if (live_row) dk = __builtin_fmaxf16(dk, __builtin_fabsf16(KF::dscale(kr[gi], bl, ksh)));
+            }
           }
-          if (__any(kb >= 0x5400u)) kk = wave_max_shift(scale_shift(bitcast<f16>(uint16_t(kb))));
+          if (__any(dk >= f16(64.0f))) kk = wave_max_shift(scale_shift(dk));
         }
         if constexpr (kVFold) {
-          uint32_t vb = 0;
+          // (dead V rows were killed above: their scale is 0)
+          f16 dv = f16(0.0f);
 #pragma unroll
-          for (int i = 0; i < 2 * NP; ++i) vb = max(vb, uint32_t(bitcast<uint16_t>(vr[i].d)) & 0x7FFFu);
-          if (__any(vb >= 0x5400u)) kv = wave_max_shift(scale_shift(bitcast<f16>(uint16_t(vb))));
+          for (int i = 0; i < 2 * NP; ++i) dv = __builtin_fmaxf16(dv, __builtin_fabsf16(vr[i].d));
+          if (__any(dv >= f16(64.0f))) kv = wave_max_shift(scale_shift(dv));
         }
 
         f32x4 sc[G];
@@ -405,12 +420,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) sc[gi] = mfma(KF::op(kr[gi], s2, ksh, mg), qop[s2], sc[gi]);
         }
+        if constexpr (G == 1) mfma_settle(sc[0]);
+        else mfma_settle(sc[0], sc[1]);
         if (!full) {
 #pragma unroll
           for (int gi = 0; gi < G; ++gi)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (t0 + 16 * gi + 4 * j + i >= t_end) sc[gi][i] = -INFINITY;
+              if (4 * j >= rem - 16 * gi - i) sc[gi][i] = -INFINITY;
         }
         // ---- online softmax ------------------------------------------------
         float mx = -INFINITY;

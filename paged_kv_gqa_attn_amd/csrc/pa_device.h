@@ -107,4 +107,23 @@ __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
   return r;
 }
 
+// Wait states after the last MFMA that wrote `a` (and `b`, ...), before any
+// later instruction reads them, whatever the branch layout. Reading an MFMA
+// result too early returns the old register contents; the compiler pads for
+// this, but the padding was observed missing on gfx950 (ROCm 7.2) for a read
+// in a block entered by a branch taken right after the MFMA: a partial-step
+// mask (`if (!full)`) between the score MFMAs and the softmax then fed stale
+// scores to every full step. 16 wait states cover the XDL ops used here (at
+// most pass count + 4). The values are asm operands so that every MFMA
+// producing them precedes the wait and every read of them follows it.
+__device__ __forceinline__ void mfma_settle(f32x4& a) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a));
+}
+__device__ __forceinline__ void mfma_settle(f32x4& a, f32x4& b) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void mfma_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 }  // namespace pa
