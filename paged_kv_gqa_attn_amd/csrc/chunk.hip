@@ -376,6 +376,8 @@ chunk_kernel(const ChunkArgs a) {
     }
 
     // ---- partial (or final) rows -------------------------------------------
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) mfma_settle(acc[k]);   // the last tile's PV MFMAs wrote them
     if (bad && tid == 0) atomicOr(a.status, 1u);
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {

@@ -309,6 +309,7 @@ decode_kernel(const DecodeArgs a) {
     }
 
     // ---- combine the four waves through LDS -------------------------------
+    mfma_settle(acc);   // the last tile's PV MFMAs wrote it
     const int n = m;
     if (wave > 0) {
       float* cw = comb + (wave - 1) * comb_stride;

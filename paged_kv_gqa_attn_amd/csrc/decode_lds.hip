@@ -538,6 +538,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
       for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);
     }
 
+    mfma_settle(acc, vcorr);   // the last step's PV MFMAs wrote them
     const float l_run = sum_over_rows(l_lane);
 
     // ---- Q4_0 V: add the -8 offset of every accumulated value -------------

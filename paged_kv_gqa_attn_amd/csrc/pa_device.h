@@ -125,5 +125,29 @@ __device__ __forceinline__ void mfma_settle(f32x4& a, f32x4& b) {
 __device__ __forceinline__ void mfma_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
+// The same for a whole accumulator array (8 or 16 tiles) and one more tile,
+// at the end of a loop whose last MFMAs wrote them.
+__device__ __forceinline__ void mfma_settle(f32x4 (&x)[8], f32x4& c) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]), "+v"(c));
+}
+__device__ __forceinline__ void mfma_settle(f32x4 (&x)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]));
+}
+__device__ __forceinline__ void mfma_settle(f32x4 (&x)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+                 "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+}
+__device__ __forceinline__ void mfma_settle(f32x4 (&x)[16], f32x4& c) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+                 "+v"(x[13]), "+v"(x[14]), "+v"(x[15]), "+v"(c));
+}
 
 }  // namespace pa
