@@ -17,8 +17,8 @@
 // then the four waves through LDS). The first kPre partitions of every class
 // are loaded together with the m values the max needs, so one memory latency
 // covers both, and the max is reduced with lane shuffles and one barrier.
-// With many rows of few partitions (p_max <= kRowsMergeMax, e.g. a prefill
-// chunk's Tq*Hq rows) that layout leaves most threads idle and launches tens
+// With many rows of few partitions (p_max <= 16, e.g. the Tq*Hq rows of a
+// prefill chunk or a verify window) that layout leaves most threads idle and launches tens
 // of thousands of workgroups, and merge_rows_kernel is used instead: one
 // thread per (row, 8 output columns) walks the row's partitions in order, 8
 // rows per workgroup at D=256.
@@ -67,17 +67,23 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   const f16* o = reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * a.D + col0 + 8 * q;
 
   // Loads in flight together: the first kPre partitions of this thread's
-  // class with their (m, l), and m of partition tid. Every address is a live
-  // partition (clamped to P-1), so no load waits behind a branch.
+  // class with their (m, l), and m of partition tid. They go through buffer
+  // resources that end at the row's last live partition, so a load past it
+  // returns 0 without touching memory and none needs a branch.
+  const rsrc_t ro = make_rsrc(reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * a.D,
+                              uint32_t(P) * uint32_t(a.D) * 2u);
+  const rsrc_t rml = make_rsrc(ml, uint32_t(P) * 8u);
+  const uint32_t ocol = uint32_t(col0 + 8 * q) * 2u;
   f16x8 pre[kPre];
   float2 mlp[kPre];
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
-    const int pc = min(c + u * kClasses, P - 1);
-    pre[u] = *reinterpret_cast<const f16x8*>(o + int64_t(pc) * a.D);
-    mlp[u] = *reinterpret_cast<const float2*>(ml + 2 * pc);
+    const uint32_t pu = uint32_t(c + u * kClasses);
+    pre[u] = bitcast<f16x8>(buf_u32x4(ro, pu * uint32_t(a.D) * 2u + ocol, 0));
+    mlp[u] = bitcast<float2>(buf_u32x2(rml, pu * 8u, 0));
   }
-  float mx = ml[2 * min(tid, P - 1)];
+  const float m0 = bitcast<float>(buf_u32(rml, uint32_t(tid) * 8u, 0));
+  float mx = tid < P ? m0 : -INFINITY;
   bool nan_seen = mx != mx;
   for (int p = tid + kThreads; p < P; p += kThreads) {
     const float mp = ml[2 * p];
@@ -108,7 +114,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   float wsum = 0.0f;
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
-    // a clamped (dead) slot gets weight 0 and adds exactly 0
+    // a slot past the last partition read zeros: weight 0, adds exactly 0
     const float w = c + u * kClasses < P ? __builtin_amdgcn_exp2f(mlp[u].x - M) * mlp[u].y : 0.0f;
     wsum += w;
     axpy8(acc, w, pre[u]);
@@ -160,9 +166,10 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   }
 }
 
-constexpr int kRowsMergeMax = 8;          // partitions per row it handles
 constexpr int kRowsMergeMinRows = 1024;   // fewer rows: the wide layout has more parallelism
 
+// NPM: the most partitions a row has (8 or 16)
+template <int NPM>
 __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a) {
   const int octs = a.D / 8;
   const int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
@@ -184,14 +191,15 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
   const float* ml = a.part_ml + bh * a.p_max * 2;
   const f16* o = reinterpret_cast<const f16*>(a.part_o) + bh * a.p_max * a.D + 8 * q;
   // every load reads a live partition (p clamped to P-1), so that none needs
-  // a branch and all are in flight at once; dead slots are then masked
-  f16x8 v[kRowsMergeMax];
-  float mp[kRowsMergeMax], lp[kRowsMergeMax];
+  // a branch and all are in flight at once; dead slots are then masked (the
+  // rows of a wave differ, so a per-row buffer resource would not be uniform)
+  f16x8 v[NPM];
+  float mp[NPM], lp[NPM];
 #pragma unroll
-  for (int p = 0; p < kRowsMergeMax; ++p)
+  for (int p = 0; p < NPM; ++p)
     v[p] = *reinterpret_cast<const f16x8*>(o + int64_t(min(p, P - 1)) * a.D);
 #pragma unroll
-  for (int p = 0; p < kRowsMergeMax; ++p) {
+  for (int p = 0; p < NPM; ++p) {
     const float2 x = *reinterpret_cast<const float2*>(ml + 2 * min(p, P - 1));
     mp[p] = p < P ? x.x : -INFINITY;
     lp[p] = p < P ? x.y : 0.0f;
@@ -200,7 +208,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
   float M = -INFINITY;
   bool nan_seen = false;
 #pragma unroll
-  for (int p = 0; p < kRowsMergeMax; ++p) {
+  for (int p = 0; p < NPM; ++p) {
     nan_seen |= mp[p] != mp[p];
     M = fmaxf(M, mp[p]);
   }
@@ -209,7 +217,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
   // (a dead slot has weight 2^-inf * 0 = 0 and holds a live partition's
   // finite values, so it adds exactly 0: no branch)
 #pragma unroll
-  for (int p = 0; p < kRowsMergeMax; ++p) {
+  for (int p = 0; p < NPM; ++p) {
     const float w = __builtin_amdgcn_exp2f(mp[p] - M) * lp[p];
     W += w;
     axpy8(acc, w, v[p]);
@@ -225,11 +233,14 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.D % kCols) return hipErrorInvalidValue;
-  if (a.p_max <= kRowsMergeMax && int64_t(a.B) * a.Hq >= kRowsMergeMinRows) {
+  if (a.p_max <= 16 && int64_t(a.B) * a.Hq >= kRowsMergeMinRows) {
     const int64_t threads = int64_t(a.B) * a.Hq * (a.D / 8);
     const int64_t blocks = (threads + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    if (a.p_max <= 8)
+      hipLaunchKernelGGL(merge_rows_kernel<8>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_rows_kernel<16>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq * (a.D / kCols)), dim3(kThreads), 0, stream, a);
   }
