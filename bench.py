@@ -22,6 +22,8 @@ object (the fp64 oracle timed on a bounded sample on the host cores).
   python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
   python bench.py --metadata     (paging-metadata update and copy-on-write timings)
   python bench.py --chunk NAME   (multi-token query attention, see CHUNKS)
+  python bench.py --sweep        (one line per batch size 1, 2, 4, 8 of the
+                                  uniform Q8_0 4K and Q4_0 32K / 128K workloads)
 """
 from __future__ import annotations
 
@@ -53,6 +55,13 @@ WORKLOADS = {
     "tiny_f16": ("tiny_f16", 1, 200, "tiny F16 B=1 L=200"),
     "slab_f16": ("slab_f16", 8, 65536, "F16 D=128 Hq=32 Hkv=8 bs=32 B=8 L=65536, pool past 2^32 elements"),
 }
+# the batch sweeps of the uniform workloads (B = 1, 2, 4 next to the B = 8 rows above)
+for _B in (1, 2, 4):
+    WORKLOADS[f"uniform_q4_0_128k_b{_B}"] = ("uniform_q4_0", _B, 131072, f"uniform Q4_0 B={_B} L=131072")
+    WORKLOADS[f"uniform_q4_0_32k_b{_B}"] = ("uniform_q4_0", _B, 32768, f"uniform Q4_0 B={_B} L=32768")
+    WORKLOADS[f"uniform_q8_0_4k_b{_B}"] = ("uniform_q8_0", _B, 4096, f"uniform Q8_0 B={_B} L=4096")
+SWEEP = [f"{w}_b{B}" for w in ("uniform_q8_0_4k", "uniform_q4_0_32k", "uniform_q4_0_128k")
+         for B in (1, 2, 4, 8)]
 DEFAULT = "uniform_q4_0_128k_b8"
 
 
@@ -543,6 +552,8 @@ def main():
                     help="measure paged_attn_chunk on this workload instead of the decode step")
     ap.add_argument("--metadata", action="store_true",
                     help="measure the paging-metadata entry points instead of the decode step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload of the batch sweep (no CPU baseline)")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.label, args.cmd, args.stem)
@@ -562,6 +573,12 @@ def main():
         return
     if args.chunk:
         run_chunk(args)
+        return
+    if args.sweep:
+        args.no_cpu_baseline = True
+        for name in SWEEP:
+            args.workload = name
+            run_bench(args)
         return
     run_bench(args)
 

@@ -35,6 +35,7 @@ constexpr int kCols = 64;                   // output columns per workgroup
 constexpr int kOcts = kCols / 8;            // 16-byte loads of 8 binary16 columns
 constexpr int kClasses = kThreads / kOcts;  // partition classes
 constexpr int kPre = 2;                     // partitions per class loaded ahead of the max
+constexpr int kBatch = 8;                   // partitions per class per later batch
 
 __device__ __forceinline__ void axpy8(float* acc, float w, const f16x8& v) {
 #pragma unroll
@@ -64,7 +65,6 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
   }
   const float* ml = a.part_ml + int64_t(bh) * a.p_max * 2;
   const int q = tid % kOcts, c = tid / kOcts;
-  const f16* o = reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * a.D + col0 + 8 * q;
 
   // Loads in flight together: the first kPre partitions of this thread's
   // class with their (m, l), and m of partition tid. They go through buffer
@@ -119,25 +119,24 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
     wsum += w;
     axpy8(acc, w, pre[u]);
   }
-  int p = c + kPre * kClasses;
-  for (; p + kClasses < P; p += 2 * kClasses) {
-    const f16x8 v0 = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
-    const f16x8 v1 = *reinterpret_cast<const f16x8*>(o + int64_t(p + kClasses) * a.D);
-    const float2 x0 = *reinterpret_cast<const float2*>(ml + 2 * p);
-    const float2 x1 = *reinterpret_cast<const float2*>(ml + 2 * (p + kClasses));
-    const float w0 = __builtin_amdgcn_exp2f(x0.x - M) * x0.y;
-    const float w1 = __builtin_amdgcn_exp2f(x1.x - M) * x1.y;
-    wsum += w0;
-    axpy8(acc, w0, v0);
-    wsum += w1;
-    axpy8(acc, w1, v1);
-  }
-  if (p < P) {
-    const f16x8 v = *reinterpret_cast<const f16x8*>(o + int64_t(p) * a.D);
-    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * p);
-    const float w = __builtin_amdgcn_exp2f(x.x - M) * x.y;
-    wsum += w;
-    axpy8(acc, w, v);
+  // the rest of the class in batches of kBatch partitions, all loads of a
+  // batch in flight at once (a row with hundreds of partitions, e.g. one
+  // long sequence alone, would otherwise pay one latency per partition pair)
+  for (int u0 = kPre; u0 * kClasses < P; u0 += kBatch) {
+    f16x8 v[kBatch];
+    float2 x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t pu = uint32_t(c + (u0 + u) * kClasses);
+      v[u] = bitcast<f16x8>(buf_u32x4(ro, pu * uint32_t(a.D) * 2u + ocol, 0));
+      x[u] = bitcast<float2>(buf_u32x2(rml, pu * 8u, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = c + (u0 + u) * kClasses < P ? __builtin_amdgcn_exp2f(x[u].x - M) * x[u].y : 0.0f;
+      wsum += w;
+      axpy8(acc, w, v[u]);
+    }
   }
 
   // sum the classes in a fixed order: the wave's 8 classes (lane bits 3..5)

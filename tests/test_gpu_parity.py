@@ -185,6 +185,7 @@ MERGE_CASES = {
     "p5": ([300, 0, 97, 31], 8, 2),
     "p10": ([600, 0, 97, 31], 8, 2),
     "p32": ([2000, 0, 97, 31], 8, 2),
+    "p313": ([20000, 0, 97, 4100], 8, 2),       # the batched loads past the first 64
     # 44 sequences x 24 heads = 1056 rows of at most 5 partitions: the
     # row-per-thread merge layout
     "rows_p5": ([0, 1, 64, 65, 300, 17, 128, 129] * 5 + [0, 300, 33, 200], 24, 4),

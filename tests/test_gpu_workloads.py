@@ -35,7 +35,7 @@ def test_uniform_q8_0_4k(B):
     _free()
 
 
-@pytest.mark.parametrize("B,L", [(1, 32768), (8, 32768), (2, 131072), (8, 131072)])
+@pytest.mark.parametrize("B,L", [(B, L) for L in (32768, 131072) for B in (1, 2, 4, 8)])
 def test_uniform_q4_0_long_context(B, L):
     case = synth.workload("uniform_q4_0", B=B, L=L, seed=1200 + B, device=DEV)
     out, plan = _run_auto(case)
