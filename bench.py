@@ -366,6 +366,7 @@ def pmc_pass(args):
 # name -> (synth workload, B, L, Tq, description)
 CHUNKS = {
     "verify_q4_0_32k_b8_t8": ("uniform_q4_0", 8, 32768, 8, "verify window Q4_0 B=8 L=32768 Tq=8"),
+    "verify_q4_0_32k_b8_t4": ("uniform_q4_0", 8, 32768, 4, "verify window Q4_0 B=8 L=32768 Tq=4"),
     "prefill_q4_0_8k_t512": ("uniform_q4_0", 1, 8192, 512, "prefill chunk Q4_0 B=1 L=8192 Tq=512"),
 }
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 MFMA, public figure
@@ -397,6 +398,8 @@ def run_chunk(args):
     shape = pa.shape_of(c0.B, c0.Hq, c0.Hkv, c0.D, c0.block_size, c0.nblocks, c0.max_blocks,
                         c0.k_fmt, c0.v_fmt)
     plan = pa.paged_attn_chunk_plan(shape, Tq, L, total_tokens=B * L)
+    if args.chunk_path:
+        plan.path = args.chunk_path
     ws = pa.workspace(plan, dev)
     out = torch.empty((B, Tq, c0.Hq, c0.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -439,6 +442,7 @@ def run_chunk(args):
         "config": {"workload": desc, "name": args.chunk, "B": B, "L": L, "Tq": Tq, "Hq": c0.Hq,
                    "Hkv": c0.Hkv, "D": c0.D, "k_type": c0.k_fmt, "v_type": c0.v_fmt,
                    "psize": plan.psize, "p_max": plan.p_max, "grid": plan.grid,
+                   "kernel": "window" if plan.path == 2 else "tile conversion",
                    "pool_copies": len(cases), "gpu_us_events": round(gpu_us, 2)},
         "roofline": {"bound": bound,
                      "hbm": {"achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -550,6 +554,8 @@ def main():
     ap.add_argument("--stem", default=None, help="profiles/ file stem (default decode_LABEL)")
     ap.add_argument("--chunk", default=None, choices=sorted(CHUNKS),
                     help="measure paged_attn_chunk on this workload instead of the decode step")
+    ap.add_argument("--chunk-path", type=int, default=0, choices=[0, 1, 2],
+                    help="with --chunk: force the chunk kernel (1 tile conversion, 2 window)")
     ap.add_argument("--metadata", action="store_true",
                     help="measure the paging-metadata entry points instead of the decode step")
     ap.add_argument("--sweep", action="store_true",

@@ -262,6 +262,13 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * PA_STATUS_BAD_SEQ_LEN. The key range is cut into partitions whose
  * partials (the decode layout with Tq*Hq rows per sequence) are reduced by
  * the same stable split-softmax merge; one partition writes out directly.
+ * Two kernels compute it: path 1 converts each key/value tile once per
+ * workgroup into LDS for four waves of query rows (any Tq); path 2, for
+ * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128) with Hkv
+ * a multiple of 4 (verify windows), streams the pool through the decode
+ * kernel's LDS ring, each wave serving one kv head with all of its rows. The plan picks path 2 where it
+ * applies; a caller may set path = 1 on such a plan to force the general
+ * kernel. Pools that are not 16-byte aligned run path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;
@@ -270,9 +277,10 @@ typedef struct pa_chunk_plan {
   int32_t psize;        /* keys per partition (multiple of 32) */
   int32_t p_max;        /* partitions of the longest admissible sequence */
   int32_t max_seq_len;
-  int32_t grid;         /* workgroups (one wave64 each) */
+  int32_t grid;         /* workgroups (four wave64s each) */
   int32_t num_cus;
   int32_t direct;       /* 1: one partition, no merge */
+  int32_t path;         /* 1: tile-conversion kernel, 2: window kernel */
   uint64_t ws_bytes;    /* workspace: status word + partials
                            (256 + B*Tq*Hq*p_max*(2D+8) bytes when direct == 0) */
 } pa_chunk_plan;

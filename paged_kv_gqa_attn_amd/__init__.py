@@ -53,13 +53,13 @@ class PaChunkPlan(ctypes.Structure):
                 ("psize", ctypes.c_int32), ("p_max", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("direct", ctypes.c_int32),
-                ("ws_bytes", ctypes.c_uint64)]
+                ("path", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64)]
 
     def __repr__(self):
         s = self.shape
         return (f"PaChunkPlan(B={s.B}, Tq={self.tq}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D}, "
                 f"psize={self.psize}, p_max={self.p_max}, grid={self.grid}, direct={self.direct}, "
-                f"ws_bytes={self.ws_bytes})")
+                f"path={self.path}, ws_bytes={self.ws_bytes})")
 
 
 class PaError(RuntimeError):

@@ -405,8 +405,12 @@ int32_t check_chunk_plan(const pa_chunk_plan* p, const char* who) {
   int32_t rc = check_shape(&p->shape, who);
   if (rc) return rc;
   if (p->tq < 1 || p->tq > kMaxChunk || p->psize < kTileTokens || p->psize % kTileTokens ||
-      p->p_max < 1 || p->grid < 1 || !(p->scale == p->scale) || p->direct != (p->p_max == 1))
+      p->p_max < 1 || p->grid < 1 || !(p->scale == p->scale) || p->direct != (p->p_max == 1) ||
+      (p->path != 1 && p->path != 2))
     return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_chunk_plan", who);
+  const pa_shape& s = p->shape;
+  if (p->path == 2 && !chunk_window_ok(int64_t(p->tq) * (s.Hq / s.Hkv), s.Hkv, s.k_type, s.v_type, s.D))
+    return fail(PA_ERR_UNSUPPORTED, "%s: plan path 2 (window kernel) does not take this chunk", who);
   return PA_OK;
 }
 }  // namespace
@@ -436,8 +440,14 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
   const int64_t L = max_seq_len;
   const int64_t r = s.Hq / s.Hkv;
+  // the window kernel takes short chunks (a workgroup per kv-head quad, one
+  // per CU); the tile-conversion kernel the rest (a workgroup per kv head and
+  // 64*nt query rows, one or two per CU)
+  const bool window = chunk_window_ok(int64_t(tq) * r, s.Hkv, s.k_type, s.v_type, s.D);
   const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
-  const int64_t qt = (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // workgroup row blocks per kv head
+  const int64_t qt = window ? 1 : (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // row blocks per unit
+  const int64_t heads_per_unit = window ? 4 : 1;
+  const int wgs_per_cu = window ? 1 : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {
@@ -455,7 +465,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
     // Among the sizes above that floor, take the one that finishes soonest:
     // the units run in ceil(units / slots) rounds of psize keys each (a
     // round only partly filled costs as much as a full one).
-    const int64_t slots = int64_t(num_cus) * chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
+    const int64_t slots = int64_t(num_cus) * wgs_per_cu;
     const int64_t rbk = pa_row_bytes(s.k_type, s.D), rbv = pa_row_bytes(s.v_type, s.D);
     const double part = double(tq) * s.Hq * (2.0 * s.D + 8.0) * 2.0;
     const double floor_hbm = part / (0.25 * double(s.Hkv) * double(rbk + rbv));
@@ -469,7 +479,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
       if (ps < floor_tok && parts > 1) break;
       const int64_t bp = std::min<int64_t>(int64_t(s.B) * ceil_div(std::max<int64_t>(L, 1), ps),
                                            ceil_div(tok, ps) + s.B);
-      const int64_t cost = ceil_div(std::max<int64_t>(1, bp * s.Hkv * qt), slots) * ps;
+      const int64_t cost = ceil_div(std::max<int64_t>(1, bp * (s.Hkv / heads_per_unit) * qt), slots) * ps;
       if (best < 0 || cost < best) { best = cost; psize = ps; }
     }
   }
@@ -477,8 +487,8 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   if (psize > INT32_MAX - kTileTokens) return fail(PA_ERR_INVALID, "%s: partition size overflows", who);
   const int64_t p_max = std::max<int64_t>(1, ceil_div(L, psize));
   const bool direct = p_max == 1;
-  const int64_t units = std::max<int64_t>(1, int64_t(s.B) * p_max * s.Hkv * qt);
-  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D));
+  const int64_t units = std::max<int64_t>(1, int64_t(s.B) * p_max * (s.Hkv / heads_per_unit) * qt);
+  const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * wgs_per_cu);
   const uint64_t ws = chunk_ws_bytes(s, tq, int(p_max), direct);
   std::memset(plan, 0, sizeof *plan);
   plan->shape = s;
@@ -490,6 +500,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   plan->grid = int32_t(grid);
   plan->num_cus = num_cus;
   plan->direct = direct ? 1 : 0;
+  plan->path = window ? 2 : 1;
   plan->ws_bytes = ws;
   clear_error();
   return PA_OK;
@@ -529,7 +540,9 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.qscale = float(double(plan->scale) * 1.4426950408889634);
   a.nt = chunk_wave_tiles(int64_t(plan->tq) * a.r, s.D);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_chunk(a, st);
+  // the window kernel's DMA chunks are 16-byte aligned only on aligned pools
+  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) == 0;
+  hipError_t e = plan->path == 2 && aligned ? launch_chunk_lds(a, st) : launch_chunk(a, st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   if (!plan->direct) {
     MergeArgs mg{};

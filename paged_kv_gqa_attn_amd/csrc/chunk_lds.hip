@@ -1,0 +1,594 @@
+// Multi-token queries with few query rows per kv head: the window kernel.
+//
+// What it computes is what chunk.hip computes (llama.cpp PR #13 HRX, Roadmap
+// item 3: multi-token queries over the preceding paged K/V with causal
+// attention inside the chunk; TensorFold PR #1418, What: paged prompt-chunk
+// attention): chunk token t of sequence b (length L) sits at position
+// L - Tq + t and attends to the keys at positions 0 .. L - Tq + t of kv head
+// g = h / r. It serves the chunks whose Tq*r query rows of a kv head fit
+// 16*NQ MFMA columns, NQ <= 2 at D = 256 and NQ <= 3 at D = 128 (what one
+// wave's registers hold next to the NQ*D/16 accumulator tiles: at r = 6 a
+// verify window of up to 5 tokens at D = 256, 8 at D = 128), where
+// converting each K/V tile into LDS operands for four waves of 16 rows
+// (chunk.hip) costs more LDS traffic than the rows are worth.
+//
+// It is the decode kernel's LDS ring with the query rows in place of the
+// heads: a workgroup of four wave64s takes a unit (sequence b, key partition
+// p, quad of kv heads hg), the DMA brings each 16-slot group of the four
+// heads' K and V rows into LDS as 1 KB contiguous instructions, and wave w
+// serves kv head 4*hg + w with all Tq*r of its query rows: each K and V row
+// it reads from LDS is converted once into the MFMA operand and used for its
+// NQ column groups. Each lane's row has its own causal limit; only steps
+// that cross some row's limit are masked, and a row with no key in the
+// partition writes m = -inf, l = 0. Partials use the decode layout with
+// Tq*Hq rows per sequence and go through the same merge.
+#include <type_traits>
+
+#include "decode_common.h"
+#include "lds_ring.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNidS = 512;     // block ids staged per segment of a partition
+constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
+
+// The ring of this kernel: one workgroup per CU (the column groups take the
+// registers of two), so it may use twice the decode kernel's LDS.
+template <int KT, int VT, int D, int NQ>
+struct WinRing {
+  using LY = LdsLayout<KT, VT, D>;
+  static constexpr int R = (2 * kLdsRingBytes) / LY::SLOT < 4 ? (2 * kLdsRingBytes) / LY::SLOT : 4;
+  static constexpr int BYTES = R * LY::SLOT;
+};
+
+template <int KT, int VT, int D, int NQ>
+__global__ void __launch_bounds__(kThreads, 1) chunk_lds_kernel(const ChunkArgs a) {
+  using KF = KFmt<KT, D>;
+  using VF = VFmt<VT, D>;
+  using WR = WinRing<KT, VT, D, NQ>;
+  using LY = typename WR::LY;
+  constexpr int RS = WR::R;      // ring slots
+  constexpr int S = D / 32;      // score MFMA steps
+  constexpr int E = D / 16;      // PV d-tiles
+  constexpr int G = LY::G;       // 16-row groups per step
+  constexpr int T = 16 * G;      // tokens per step
+  constexpr int NP = 2 * G;      // V row pairs per lane (4 rows per group)
+  constexpr bool kKFold = KT == kQ4_0;   // Q4_0 offsets folded into corrections
+  constexpr bool kVFold = VT == kQ4_0;
+  constexpr int KF_NBL = kKFold ? D / 128 : 1;   // ggml blocks per K lane window
+
+  unsigned char* const ring = g_lds;
+  int32_t* ids = reinterpret_cast<int32_t*>(g_lds + WR::BYTES);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int m = lane & 15;
+  const int j = lane >> 4;
+  const int R = a.Tq * a.r;                      // query rows per kv head (<= 16*NQ)
+  const int HG = a.Hkv / 4;
+  const int n_units = a.B * a.p_max * HG;
+  const int Gd = gridDim.x;
+  const int logical = xcd_logical(blockIdx.x, Gd);
+
+  const int cw = (LY::NI - wave + 3) / 4;              // DMA instructions this wave issues per step
+  // LDS offsets (within a group) of the rows this lane reads: K row m, V rows
+  // 4j+i, of the wave's head, at their rotated row positions
+  const int k_row = m * LY::SPK + ((wave + RowRot<LY::RBK>::k(m)) & 3) * LY::RBK + int(KF::lane_off(j));
+  int v_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v_row[i] = (4 * j + i) * LY::SPV + ((wave + RowRot<LY::RBV>::v(4 * j + i)) & 3) * LY::RBV;
+  const uint32_t kstride = uint32_t(a.Hkv) * LY::RBK;  // pool bytes between token slots
+  const uint32_t vstride = uint32_t(a.Hkv) * LY::RBV;
+  const uint32_t ksh = KF::shift(j);
+  const auto vl = VF::lane(m, 0u);
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int seg_tokens = kNidS << a.bs_shift;
+
+  for (int u = logical; u < n_units; u += Gd) {
+    // ---- locate the unit: (b*p_max + p)*HG + hg -------------------------------
+    const int hg = u % HG;
+    const int bp = u / HG;
+    const int b = bp / a.p_max;
+    const int p = bp - b * a.p_max;
+    int L = a.seq_len[b];
+    if (L < 0 || L > a.cap_tokens) {
+      if (tid == 0 && p == 0 && hg == 0) atomicOr(a.status, 2u);
+      L = L < 0 ? 0 : a.cap_tokens;
+    }
+    if (L > 0 && L < a.Tq) {             // the chunk is longer than the sequence
+      if (tid == 0 && p == 0 && hg == 0) atomicOr(a.status, 2u);
+      L = 0;
+    }
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int g = 4 * hg + wave;                        // this wave's kv head
+    const int P = L > 0 ? (L + a.psize - 1) / a.psize : 0;
+    const int t_begin = p * a.psize;
+    const int t_end = min(L, t_begin + a.psize);
+    // this lane's query row in column group k: row n = 16k + m, i.e. chunk
+    // token n / r of head g*r + n % r; its last visible key; rows past R are
+    // dead columns (zero q, reference +inf, never written)
+    bool valid[NQ];
+    int64_t orow[NQ];
+    int lim[NQ];
+    int lim_min = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int row = 16 * k + m;
+      valid[k] = row < R;
+      const int t = valid[k] ? row / a.r : 0;
+      const int h = g * a.r + (valid[k] ? row - t * a.r : 0);
+      orow[k] = (int64_t(b) * a.Tq + t) * a.Hq + h;   // row of out / partials
+      lim[k] = valid[k] ? min(L - a.Tq + t, t_end - 1) : t_begin - 1;
+      if (valid[k]) lim_min = min(lim_min, lim[k]);
+    }
+    if (L == 0) {
+      // an empty (or refused) sequence: zero rows in direct mode; the merge
+      // writes its zero rows otherwise
+      if (a.direct && j == 0) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k)
+          if (valid[k])
+            for (int d = 0; d < D; ++d) a.out[orow[k] * D + d] = 0.0f;
+      }
+      continue;
+    }
+    if (p >= P) continue;                 // no such partition: nothing to write
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+    lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+
+    const uint32_t khead = uint32_t(4 * hg) * LY::RBK;  // first head's offset in a slot
+    const uint32_t vhead = uint32_t(4 * hg) * LY::RBV;
+    // this lane's pool offset in each DMA instruction q = wave + 4i of a step
+    uint32_t dvoff[LY::NIW];
+#pragma unroll
+    for (int i = 0; i < LY::NIW; ++i) {
+      const int q = wave + 4 * i;
+      if (q < G * LY::NIK)
+        dvoff[i] = chunk_voff<LY::CPK, LY::RBK>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
+                                                 RowRot<LY::RBK>::k);
+      else
+        dvoff[i] = chunk_voff<LY::CPV, LY::RBV>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
+                                                 16u * vstride, RowRot<LY::RBV>::v);
+    }
+
+    // ---- the first segment's block ids and the first column group's q
+    // values, in flight together; the first steps' DMA is issued before the
+    // Q operands are built
+    int seg_t0 = t_begin;
+    int seg_t1 = min(t_end, seg_t0 + seg_tokens);
+    int jb0 = seg_t0 >> a.bs_shift;
+    int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+    int32_t idr[kIdRegs];
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k)
+      idr[k] = block_of(a.table, b, a.max_blocks, jb0 + min(tid + k * kThreads, nb - 1));
+    auto load_q = [&](int k, float (&qv)[S][8]) __attribute__((always_inline)) {
+      const float* qw = a.q + (valid[k] ? orow[k] : orow[0]) * D;   // a dead column reads a live row
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[s][i] = qw[KF::dslot(j, s, i)];
+    };
+    float qv[S][8];
+    load_q(0, qv);
+    __syncthreads();                        // the previous unit is done with the ring and ids[]
+    int bad = 0;
+    {
+      int badl = 0;
+#pragma unroll
+      for (int k = 0; k < kIdRegs; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < nb) {
+          int32_t id = idr[k];
+          if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+          ids[i] = id;
+        }
+      }
+      bad |= __syncthreads_or(badl);        // also publishes ids[]
+    }
+
+    // ---- DMA of step s of the current segment into ring slot s % RS ----------
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      const uint32_t slot = uint32_t(s % RS) * LY::SLOT;   // ring starts at LDS byte 0
+      const int t0 = seg_t0 + s * T;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int tg = t0 + 16 * gi;
+        const bool live = tg < seg_t1;
+        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+        const int slot0 = live ? (tg & bs_mask) : 0;
+        const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
+                                    live ? 16u * kstride : 0u);
+        const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
+                                    live ? 16u * vstride : 0u);
+#pragma unroll
+        for (int sub = 0; sub < LY::NIK; ++sub) {
+          const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
+          if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+        }
+#pragma unroll
+        for (int sub = 0; sub < LY::NIV; ++sub) {
+          const int q = G * LY::NIK + gi * LY::NIV + sub;
+          if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+        }
+      }
+    };
+    int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
+    for (int s = 0; s < RS - 1 && s < nsteps; ++s) issue(s);
+
+    // ---- Q operands, column group by column group, and the Q4_0 K offset
+    // corrections (the first group's q values are already loaded)
+    f16x8 qop[NQ][S];
+    float kcorr[NQ][KF_NBL];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      if (k > 0) load_q(k, qv);
+      const float keep = valid[k] ? a.qscale : 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          // Q4_0: the high-nibble slots meet K values in the x16 frame
+          const float hs = (kKFold && KFmtHi<KT, D>::hi(i)) ? 0.0625f : 1.0f;
+          qop[k][s][i] = f16(qv[s][i] * keep * hs);
+        }
+#pragma unroll
+      for (int bl = 0; bl < KF_NBL; ++bl) {
+        float qsum = 0.0f;
+#pragma unroll
+        for (int s2 = 4 * bl; s2 < 4 * bl + 4; ++s2)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qsum += float(qop[k][s2][i]) * (KFmtHi<KT, D>::hi(i) ? 16.0f : 1.0f);
+        kcorr[k][bl] = -8.0f * qsum;
+      }
+    }
+
+    // reference max: +inf in dead columns (their p is exactly 0), -inf until
+    // the row has seen a key
+    float m_run[NQ], l_lane[NQ];
+    f32x4 acc[NQ][E];
+    f32x4 vcorr[NQ];              // Q4_0 V: sum_t d_t p_t per row block
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      m_run[k] = valid[k] ? -INFINITY : INFINITY;
+      l_lane[k] = 0.0f;
+      vcorr[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[k][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int vshift = 0;               // Q4_0 V: acc holds the sums times 2^-vshift
+
+    for (;;) {
+      // ---- compute step s from LDS: scores, online softmax (exp2), PV -------
+      auto compute = [&](int s) __attribute__((always_inline)) {
+        const unsigned char* slot = ring + (s % RS) * LY::SLOT;
+        const int t0 = seg_t0 + s * T;
+        const bool full = t0 + T <= t_end;
+        const int rem = t_end - t0;
+        typename KF::Raw kr[G];
+        typename VF::Raw vr[2 * NP];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) KF::load_lds(kr[gi], slot + gi * LY::NIK * 1024 + k_row);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            VF::load_lds(vr[4 * gi + i], slot + LY::VOFF + gi * LY::NIV * 1024 + v_row[i], vl);
+        if (!full) {
+          // zero V rows past the partition end so 0 * junk never reaches PV
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * j >= rem - 16 * gi - i) VF::kill(vr[4 * gi + i]);
+        }
+        // Q4_0 scale range (see the decode kernel): |d| < 64 for the fma form
+        int kk = 0, kv = 0;
+        if constexpr (kKFold) {
+          f16 dk = f16(0.0f);
+          if (full) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+              for (int bl = 0; bl < KF_NBL; ++bl)
+                dk = __builtin_fmaxf16(dk, __builtin_fabsf16(KF::dscale(kr[gi], bl, ksh)));
+          } else {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const bool live_row = m < rem - 16 * gi;   // dead K rows are masked below
+#pragma unroll
+              for (int bl = 0; bl < KF_NBL; ++bl)
+                if (live_row) dk = __builtin_fmaxf16(dk, __builtin_fabsf16(KF::dscale(kr[gi], bl, ksh)));
+            }
+          }
+          if (__any(dk >= f16(64.0f))) kk = wave_max_shift(scale_shift(dk));
+        }
+        if constexpr (kVFold) {
+          f16 dv = f16(0.0f);
+#pragma unroll
+          for (int i = 0; i < 2 * NP; ++i) dv = __builtin_fmaxf16(dv, __builtin_fabsf16(vr[i].d));
+          if (__any(dv >= f16(64.0f))) kv = wave_max_shift(scale_shift(dv));
+        }
+
+        // ---- scores: each K operand serves the NQ column groups ------------
+        f32x4 sc[NQ][G];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k)
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) sc[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kKFold) {
+          const f16x2 sk = pow2_neg_f16x2(kk);
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) {
+            f16x2 d2[KF_NBL], c2[KF_NBL];
+#pragma unroll
+            for (int bl = 0; bl < KF_NBL; ++bl) {
+              d2[bl] = splat2(KF::dscale(kr[gi], bl, ksh)) * sk;
+              c2[bl] = d2[bl] * f16x2{-1024.0f16, -1024.0f16};
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2) {
+              const f16x8 kop = KF::op_n16(kr[gi], s2, ksh, mg, d2, c2);
+#pragma unroll
+              for (int k = 0; k < NQ; ++k) sc[k][gi] = mfma(kop, qop[k][s2], sc[k][gi]);
+            }
+          }
+          if (kk) {
+            const float up = __builtin_ldexpf(1.0f, kk);
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+#pragma unroll
+              for (int gi = 0; gi < G; ++gi) sc[k][gi] *= up;
+          }
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int bl = 0; bl < KF_NBL; ++bl) {
+              const float dsc = float(KF::dscale(kr[gi], bl, ksh));
+#pragma unroll
+              for (int k = 0; k < NQ; ++k)
+                sc[k][gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(dsc, kcorr[k][bl], sc[k][gi], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+          for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const f16x8 kop = KF::op(kr[gi], s2, ksh, mg);
+#pragma unroll
+              for (int k = 0; k < NQ; ++k) sc[k][gi] = mfma(kop, qop[k][s2], sc[k][gi]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+          if constexpr (G == 1) mfma_settle(sc[k][0]);
+          else mfma_settle(sc[k][0], sc[k][1]);
+        }
+        // causal and end-of-partition mask, only where some row's limit falls
+        // inside the step (lim <= t_end - 1 covers the slots past the end)
+        if (t0 + T - 1 > lim_min) {
+#pragma unroll
+          for (int k = 0; k < NQ; ++k)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (t0 + 16 * gi + 4 * j + i > lim[k]) sc[k][gi][i] = -INFINITY;
+        }
+        // ---- online softmax per column group (lazy rescale; a row whose
+        // reference does not move keeps its sums, which also covers rows with
+        // no key yet and the dead columns)
+        typename OpVec<NP>::type pop[NQ];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+            mx = fmaxf(mx, fmaxf(fmaxf(sc[k][gi][0], sc[k][gi][1]), fmaxf(sc[k][gi][2], sc[k][gi][3])));
+          if (__any(mx > m_run[k] + kSlack)) {
+            const float m_new = fmaxf(m_run[k], max_over_rows(mx));
+            const float alpha = m_new == m_run[k] ? 1.0f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
+            l_lane[k] *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[k][e] *= alpha;
+            vcorr[k] *= alpha;
+            m_run[k] = m_new;
+          }
+          // a row with no key yet keeps m = -inf: its p are exp2(-inf) = 0
+          const float m_use = m_run[k] == -INFINITY ? 0.0f : m_run[k];
+          float pr[2 * NP];
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[4 * gi + i] = __builtin_amdgcn_exp2f(sc[k][gi][i] - m_use);
+          float ps = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 2 * NP; i += 4) ps += (pr[i] + pr[i + 1]) + (pr[i + 2] + pr[i + 3]);
+          l_lane[k] += ps;
+#pragma unroll
+          for (int i = 0; i < 2 * NP; ++i) pop[k][i] = f16(pr[i]);
+        }
+        auto pv = [&](typename OpVec<NP>::type av, const typename OpVec<NP>::type& bv, f32x4 c)
+            __attribute__((always_inline)) {
+          if constexpr (NP == 4) return mfma(av, bv, c);
+          else return mfma16(av, bv, c);
+        };
+        __builtin_amdgcn_s_setprio(1);
+        // ---- PV: each V operand serves the NQ column groups -----------------
+        if constexpr (VF::kQuant) {
+          uint32_t q[2 * NP][VF::ND];
+          f16x2 dd[NP];
+#pragma unroll
+          for (int i = 0; i < 2 * NP; ++i) VF::realign(vr[i], vl.sh, q[i]);
+#pragma unroll
+          for (int qq = 0; qq < NP; ++qq) dd[qq] = f16x2{vr[2 * qq].d, vr[2 * qq + 1].d};
+          if constexpr (kVFold) {
+            if (kv != vshift) {
+              const float f = __builtin_ldexpf(1.0f, vshift - kv);
+#pragma unroll
+              for (int k = 0; k < NQ; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[k][e] *= f;
+              vshift = kv;
+            }
+            const f16x2 sv = pow2_neg_f16x2(kv);
+            f16x2 ds[NP], cc[NP];
+#pragma unroll
+            for (int qq = 0; qq < NP; ++qq) {
+              ds[qq] = dd[qq] * sv;
+              cc[qq] = ds[qq] * f16x2{-1024.0f16, -1024.0f16};
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const auto vop = VF::template op_n16<NP>(q, ds, cc, e, mg);
+#pragma unroll
+              for (int k = 0; k < NQ; ++k) acc[k][e] = pv(vop, pop[k], acc[k][e]);
+            }
+            const auto dop = OpVec<NP>::pack(dd);
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) vcorr[k] = pv(dop, pop[k], vcorr[k]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const auto vop = VF::template op_q<NP>(q, dd, e, mg);
+#pragma unroll
+              for (int k = 0; k < NQ; ++k) acc[k][e] = pv(vop, pop[k], acc[k][e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const auto vop = VF::template op<NP>(vr, e);
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) acc[k][e] = pv(vop, pop[k], acc[k][e]);
+          }
+        }
+      };
+
+      // ---- the ring: steps s+1 .. s+RS-1 in flight while step s is computed
+      for (int s = 0; s < nsteps; ++s) {
+        const int later = min(RS - 2, nsteps - 1 - s);
+        wait_dma_then_barrier(later * cw);
+        __builtin_amdgcn_s_setprio(3);
+        if (s + RS - 1 < nsteps) issue(s + RS - 1);
+        compute(s);
+      }
+
+      // ---- next segment: its block ids, then the first steps' DMA ----------
+      seg_t0 = seg_t1;
+      if (seg_t0 >= t_end) break;
+      seg_t1 = min(t_end, seg_t0 + seg_tokens);
+      jb0 = seg_t0 >> a.bs_shift;
+      nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // ids[] and the ring are free
+      int badl = 0;
+      for (int i = tid; i < nb; i += kThreads) {
+        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
+      }
+      bad |= __syncthreads_or(badl);         // also publishes ids[]
+      nsteps = (seg_t1 - seg_t0 + T - 1) / T;
+      for (int s = 0; s < RS - 1 && s < nsteps; ++s) issue(s);
+    }
+
+    // ---- partial (or final) rows -------------------------------------------
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) mfma_settle(acc[k], vcorr[k]);   // the last step's PV MFMAs wrote them
+    if (bad && tid == 0) atomicOr(a.status, 1u);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const float l_run = sum_over_rows(l_lane[k]);
+      if constexpr (kVFold) {
+        // add the -8 offset of every accumulated value, undo the x16 frame
+        const float f = __builtin_ldexpf(1.0f, vshift);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float fe = VFmtHi<VT, D>::hi(e) ? f * 0.0625f : f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[k][e][i] = acc[k][e][i] * fe - 8.0f * vcorr[k][i];
+        }
+      }
+      if (!valid[k]) continue;
+      const float inv = bad ? __builtin_nanf("") : (l_run > 0.0f ? 1.0f / l_run : 0.0f);
+      if (a.direct) {
+        float* dst = a.out + orow[k] * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = acc[k][e][i] * inv;
+      } else {
+        const int64_t prow = orow[k] * a.p_max + p;
+        f16* dst = reinterpret_cast<f16*>(a.part_o) + prow * D;
+        if (j == 0) {
+          a.part_ml[2 * prow] = bad ? __builtin_nanf("") : (l_run > 0.0f ? m_run[k] : -INFINITY);
+          a.part_ml[2 * prow + 1] = l_run;
+        }
+#pragma unroll
+        for (int e = 0; e < E; e += 2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            store_f16_pair(dst, VF::dv(4 * j + i, e), acc[k][e][i] * inv, acc[k][e + 1][i] * inv);
+      }
+    }
+  }
+}
+
+template <int KT, int VT, int D, int NQ>
+hipError_t launch_nq(const ChunkArgs& a, hipStream_t stream) {
+  constexpr size_t lds = size_t(WinRing<KT, VT, D, NQ>::BYTES) + 4 * size_t((kNidS + 1 + 3) & ~3);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&chunk_lds_kernel<KT, VT, D, NQ>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((chunk_lds_kernel<KT, VT, D, NQ>), dim3(a.grid), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int KT, int VT, int D>
+hipError_t launch_typed(const ChunkArgs& a, hipStream_t stream) {
+  if constexpr (lds_groups(KT, VT, D) == 0) {
+    return hipErrorInvalidValue;
+  } else {
+    const int nq = (a.Tq * a.r + 15) / 16;
+    if (nq == 1) return launch_nq<KT, VT, D, 1>(a, stream);
+    if (nq == 2) return launch_nq<KT, VT, D, 2>(a, stream);
+    if constexpr (D == 128) {
+      if (nq == 3) return launch_nq<KT, VT, D, 3>(a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const ChunkArgs& a, hipStream_t stream) {
+  switch (a.k_type * 3 + a.v_type) {
+    case 0: return launch_typed<kF16, kF16, D>(a, stream);
+    case 1: return launch_typed<kF16, kQ8_0, D>(a, stream);
+    case 2: return launch_typed<kF16, kQ4_0, D>(a, stream);
+    case 3: return launch_typed<kQ8_0, kF16, D>(a, stream);
+    case 4: return launch_typed<kQ8_0, kQ8_0, D>(a, stream);
+    case 5: return launch_typed<kQ8_0, kQ4_0, D>(a, stream);
+    case 6: return launch_typed<kQ4_0, kF16, D>(a, stream);
+    case 7: return launch_typed<kQ4_0, kQ8_0, D>(a, stream);
+    case 8: return launch_typed<kQ4_0, kQ4_0, D>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_lds(const ChunkArgs& a, hipStream_t stream) {
+  if (a.Hkv % 4) return hipErrorInvalidValue;
+  if (a.D == 256) return launch_d<256>(a, stream);
+  if (a.D == 128) return launch_d<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -92,7 +92,20 @@ struct ChunkArgs {
   float qscale;            // scale * log2(e)
   int32_t nt;              // 16-row query tiles per wave (chunk_wave_tiles)
 };
+// Whether the window kernel takes a chunk with `rows` query rows per kv head
+// (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
+// registers hold with their accumulators; Hkv % 4 == 0; the shapes
+// lds_groups() admits.
+constexpr int chunk_window_rows(int D) { return D == 256 ? 32 : 48; }
+constexpr bool chunk_window_ok(int64_t rows, int hkv, int kt, int vt, int D) {
+  return (D == 128 || D == 256) && rows <= chunk_window_rows(D) && hkv % 4 == 0 &&
+         lds_groups(kt, vt, D) > 0;
+}
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
+// The window kernel (chunk_lds.hip): the decode kernel's LDS ring, each wave
+// one kv head with all of its Tq*r query rows (chunk_window_ok); pools
+// 16-byte aligned.
+hipError_t launch_chunk_lds(const ChunkArgs& a, hipStream_t stream);
 // Query tiles per wave of the chunk kernel for R = Tq*r rows per kv head (a
 // workgroup of four waves takes 64*nt rows; two tiles per wave fit the
 // registers at D = 128 only), and its workgroups per CU (two waves per SIMD

@@ -3,7 +3,10 @@ the chunk: llama.cpp PR #13 HRX, Roadmap item 3; TensorFold PR #1418, What:
 paged equals contiguous bit for bit) against oracle.chunk, through the C ABI.
 
 Tolerance as for decode (per-row max-abs error relative to the row's
-max-abs output): 2e-3 when K and V are F16, 5e-3 when either is quantised."""
+max-abs output): 2e-3 when K and V are F16, 5e-3 when either is quantised.
+Two kernels compute a chunk (plan path 1: tile conversion for any Tq; path
+2: the window kernel for few query rows per kv head); the tests marked with
+a `path` parameter run each on the same inputs."""
 import dataclasses
 
 import numpy as np
@@ -28,12 +31,34 @@ def _case(lens, Tq, seed, **kw):
     return c, qc
 
 
-def _plan(c, Tq, **kw):
+def window_ok(c, Tq):
+    """Whether the window kernel (plan path 2) takes the chunk: quads of kv
+    heads, one 16-slot group of K and V of four heads in a 36 KB ring slot
+    (no F16 side at D=256), and Tq*r query rows per kv head that fit one wave
+    (32 at D=256, 48 at D=128)."""
+    rb = {"f16": 2 * c.D, "q8_0": 34 * c.D // 32, "q4_0": 18 * c.D // 32}
+    per_group = sum(-(-16 * 4 * rb[f] // 1024) for f in (c.k_fmt, c.v_fmt)) * 1024
+    rows = Tq * (c.Hq // c.Hkv)
+    return c.Hkv % 4 == 0 and per_group <= 36864 and rows <= (32 if c.D == 256 else 48)
+
+
+def _plan(c, Tq, path=None, **kw):
+    """paged_attn_chunk_plan for the case; path=1/2 forces the kernel (a chunk
+    the window kernel does not take is skipped for path 2)."""
     pa = pa_mod()
     shape = pa.shape_of(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.nblocks, c.max_blocks, c.k_fmt,
                         c.v_fmt)
-    return pa.paged_attn_chunk_plan(shape, Tq, max(c.seq_lens), total_tokens=sum(c.seq_lens),
+    plan = pa.paged_attn_chunk_plan(shape, Tq, max(c.seq_lens), total_tokens=sum(c.seq_lens),
                                     scale=c.scale, **kw)
+    assert plan.path == (2 if window_ok(c, Tq) else 1)
+    if path is not None:
+        if path == 2 and not window_ok(c, Tq):
+            pytest.skip("the window kernel does not take this chunk")
+        plan.path = path
+    return plan
+
+
+PATHS = [1, 2]
 
 
 def _run(c, qc, plan, table="case"):
@@ -74,37 +99,54 @@ def test_nine_type_pairs(pair, D):
         assert pa_mod().paged_attn_status(ws) == 0
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
+def test_nine_type_pairs_short_window(pair, D, path):
+    """A 5-token window (30 query rows per kv head) on both kernels."""
+    seed = 3 * synth.FORMATS.index(pair[0]) + synth.FORMATS.index(pair[1]) + D + 77
+    c, qc = _case([300, 77, 16], 5, seed=seed, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 64}):
+        out, ws = _run(c, qc, _plan(c, 5, path=path, **kw))
+        _check(c, qc, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("Tq", [1, 2, 16, 33, 130])
-def test_chunk_lengths_and_partitions(Tq):
+def test_chunk_lengths_and_partitions(Tq, path):
     """Query tiles from one to many, partitions that start past some rows'
     positions (those rows get empty partials), and a chunk as long as the
     sequence (its first token sees key 0 only)."""
     c, qc = _case([400, Tq, 1000], Tq, seed=Tq, k_fmt="q4_0", v_fmt="q8_0")
     for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 96}, {"force_partitions": 5}):
-        out, _ = _run(c, qc, _plan(c, Tq, **kw))
+        out, _ = _run(c, qc, _plan(c, Tq, path=path, **kw))
         _check(c, qc, out)
 
 
-def test_tq_one_is_a_decode_step():
+@pytest.mark.parametrize("path", PATHS)
+def test_tq_one_is_a_decode_step(path):
     """A one-token chunk is a decode step: the same oracle, within tolerance of
     the decode kernels' output."""
     pa = pa_mod()
     c, qc = _case([700, 5, 129], 1, seed=41, k_fmt="q8_0", v_fmt="q4_0")
-    out, _ = _run(c, qc, _plan(c, 1, partition_tokens=128))
+    out, _ = _run(c, qc, _plan(c, 1, path=path, partition_tokens=128))
     dc = dataclasses.replace(c, q=qc[:, 0].contiguous())
     ref = oracle.decode_case(dc)
     assert float(rel_err_rows(out[:, 0].cpu().double().numpy(), ref).max()) <= tol_for(c)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("pair", [("f16", "f16"), ("q4_0", "q4_0"), ("q8_0", "f16")])
-def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
+def test_paged_equals_contiguous_bitwise_and_deterministic(pair, path):
     """TensorFold PR #1418, What: the paged chunk equals the contiguous one bit
     for bit (same tiles in the same order); repeated runs agree bit for bit."""
-    c, qc = _case([333, 64, 190], 12, seed=7, k_fmt=pair[0], v_fmt=pair[1])
+    Tq = 12 if path == 1 else 4
+    c, qc = _case([333, 64, 190], Tq, seed=7, k_fmt=pair[0], v_fmt=pair[1])
     cc = synth.contiguous_copy(c)
     for kw in ({}, {"partition_tokens": 64}):
-        plan = _plan(c, 12, **kw)
-        plan_c = _plan(cc, 12, **kw)             # the contiguous pool has its own nblocks
+        plan = _plan(c, Tq, path=path, **kw)
+        plan_c = _plan(cc, Tq, path=path, **kw)  # the contiguous pool has its own nblocks
         assert (plan_c.psize, plan_c.grid) == (plan.psize, plan.grid)
         o1, _ = _run(c, qc, plan)
         o2, _ = _run(cc, qc, plan_c, table=None)
@@ -113,13 +155,15 @@ def test_paged_equals_contiguous_bitwise_and_deterministic(pair):
         _check(c, qc, o1)
 
 
-def test_empty_and_too_short_sequences():
+@pytest.mark.parametrize("path", PATHS)
+def test_empty_and_too_short_sequences(path):
     """L = 0 gives zero rows; 0 < L < Tq gives zero rows and the seq_len
     status bit; the other sequences are untouched."""
     pa = pa_mod()
-    c, qc = _case([0, 3, 50], 6, seed=13, k_fmt="q4_0", v_fmt="f16")
+    Tq = 6 if path == 1 else 5
+    c, qc = _case([0, 3, 50], Tq, seed=13, k_fmt="q4_0", v_fmt="q8_0")
     for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 32}):
-        plan = _plan(c, 6, **kw)
+        plan = _plan(c, Tq, path=path, **kw)
         g = c.to(DEV)
         ws = pa.workspace(plan, DEV)
         out = torch.full(tuple(qc.shape), float("nan"), device=DEV)
@@ -133,12 +177,13 @@ def test_empty_and_too_short_sequences():
         assert float(err.max()) <= tol_for(c)
 
 
-def test_bad_block_id_sets_status_and_nans_only_that_sequence():
+@pytest.mark.parametrize("path", PATHS)
+def test_bad_block_id_sets_status_and_nans_only_that_sequence(path):
     pa = pa_mod()
     c, qc = _case([200, 150], 4, seed=17, k_fmt="q4_0", v_fmt="q4_0", junk="zero")
     bad_table = c.table.clone()
     bad_table[1, 3] = c.nblocks + 5
-    plan = _plan(c, 4, partition_tokens=64)
+    plan = _plan(c, 4, path=path, partition_tokens=64)
     out, ws = _run(c, qc, plan, table=bad_table.to(DEV))
     assert pa.paged_attn_status(ws) & pa.PA_STATUS_BAD_BLOCK_ID
     o = out.cpu()
@@ -146,3 +191,22 @@ def test_bad_block_id_sets_status_and_nans_only_that_sequence():
     good = dataclasses.replace(c, B=1, seq_lens=[200], seq_len=c.seq_len[:1], q=c.q[:1],
                                table=c.table[:1])
     assert float(rel_err_rows(o[:1].double().numpy(), _ref(good, qc[:1])).max()) <= tol_for(c)
+
+
+@pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "q4_0"), ("f16", "q8_0")])
+@pytest.mark.parametrize("D", [256, 128])
+def test_both_kernels_agree(pair, D):
+    """The same chunk on both kernels with the same partitioning: they differ
+    only in the order of fp32 accumulation (and the f16 rounding of the
+    operands, the same on both)."""
+    Tq = 5 if D == 256 else 8
+    c, qc = _case([2000, 700, 33], Tq, seed=101 + D, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    if not window_ok(c, Tq):
+        pytest.skip("the window kernel does not take this chunk")
+    for kw in ({}, {"partition_tokens": 256}):
+        o1, _ = _run(c, qc, _plan(c, Tq, path=1, **kw))
+        o2, _ = _run(c, qc, _plan(c, Tq, path=2, **kw))
+        g1, g2 = o1.cpu().double().numpy(), o2.cpu().double().numpy()
+        assert np.isfinite(g2).all()
+        assert float(rel_err_rows(g2, g1).max()) <= 2e-3
+        _check(c, qc, o2)
