@@ -72,7 +72,7 @@ def source_hash() -> str:
     """Hash of the decode kernels' sources: counter summaries taken on other
     sources are not used for `traffic`."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "decode_lds.hip", "decode_common.h", "pa_device.h", "pa_host.h"):
+    for name in ("decode.hip", "decode_lds.hip", "lds_ring.h", "decode_common.h", "pa_device.h", "pa_host.h"):
         with open(os.path.join(ROOT, "paged_kv_gqa_attn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
