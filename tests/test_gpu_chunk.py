@@ -193,14 +193,19 @@ def test_bad_block_id_sets_status_and_nans_only_that_sequence(path):
     assert float(rel_err_rows(o[:1].double().numpy(), _ref(good, qc[:1])).max()) <= tol_for(c)
 
 
+@pytest.mark.parametrize("heads", [(24, 4), (32, 8)], ids=["r6", "r4-two-quads"])
 @pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "q4_0"), ("f16", "q8_0")])
 @pytest.mark.parametrize("D", [256, 128])
-def test_both_kernels_agree(pair, D):
-    """The same chunk on both kernels with the same partitioning: they differ
-    only in the order of fp32 accumulation (and the f16 rounding of the
-    operands, the same on both)."""
-    Tq = 5 if D == 256 else 8
-    c, qc = _case([2000, 700, 33], Tq, seed=101 + D, k_fmt=pair[0], v_fmt=pair[1], D=D)
+def test_both_kernels_agree(pair, D, heads):
+    """The same chunk on both kernels with the same partitioning, to the
+    format tolerance: besides the order of fp32 accumulation they round the
+    quantised values differently (the window kernel folds the Q4_0 offset
+    into correction MFMAs as the decode kernel does; the tile kernel converts
+    (n - 8) * d directly). Hkv = 8 gives two kv-head quads per sequence."""
+    Hq, Hkv = heads
+    Tq = (32 if D == 256 else 48) // (Hq // Hkv)
+    c, qc = _case([2000, 700, 33], Tq, seed=101 + D + Hkv, k_fmt=pair[0], v_fmt=pair[1], D=D,
+                  Hq=Hq, Hkv=Hkv)
     if not window_ok(c, Tq):
         pytest.skip("the window kernel does not take this chunk")
     for kw in ({}, {"partition_tokens": 256}):
@@ -208,5 +213,5 @@ def test_both_kernels_agree(pair, D):
         o2, _ = _run(c, qc, _plan(c, Tq, path=2, **kw))
         g1, g2 = o1.cpu().double().numpy(), o2.cpu().double().numpy()
         assert np.isfinite(g2).all()
-        assert float(rel_err_rows(g2, g1).max()) <= 2e-3
+        assert float(rel_err_rows(g2, g1).max()) <= tol_for(c)
         _check(c, qc, o2)
