@@ -215,3 +215,30 @@ def test_both_kernels_agree(pair, D, heads):
         assert np.isfinite(g2).all()
         assert float(rel_err_rows(g2, g1).max()) <= tol_for(c)
         _check(c, qc, o2)
+
+
+def test_unaligned_pools_run_the_tile_kernel():
+    """Pools that are not 16-byte aligned run the tile-conversion kernel even
+    under a window plan: the result equals a path-1 run bit for bit."""
+    c, qc = _case([500, 77], 4, seed=231, k_fmt="q4_0", v_fmt="q8_0")
+    g = c.to(DEV)
+
+    def shifted(pool):
+        raw = torch.empty(pool.numel() + 4, dtype=torch.uint8, device=DEV)
+        view = raw[4:].view(pool.shape)
+        view.copy_(pool)
+        assert view.data_ptr() % 16 == 4
+        return view
+
+    plan2 = _plan(c, 4, path=2, partition_tokens=128)
+    plan1 = _plan(c, 4, path=1, partition_tokens=128)
+    pa = pa_mod()
+    outs = []
+    for plan, kp, vp in ((plan2, shifted(g.k_pool), shifted(g.v_pool)), (plan1, g.k_pool, g.v_pool)):
+        ws = pa.workspace(plan, DEV)
+        out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
+        pa.paged_attn_chunk(plan, qc.to(DEV), kp, vp, g.table, g.seq_len, ws, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    _check(c, qc, outs[0])
