@@ -193,8 +193,11 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_lds_kernel(const ChunkArgs 
       bad |= __syncthreads_or(badl);        // also publishes ids[]
     }
 
-    // ---- DMA of step s of the current segment into ring slot s % RS ----------
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    // ---- DMA of step s of the current segment into ring slot s % RS (each
+    // wave its share: instructions q with q % 4 == W, W the wave index as a
+    // compile-time constant, so that the selection costs no branches) ---------
+    auto issue_as = [&](auto wc, int s) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
       const uint32_t slot = uint32_t(s % RS) * LY::SLOT;   // ring starts at LDS byte 0
       const int t0 = seg_t0 + s * T;
 #pragma unroll
@@ -210,13 +213,21 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_lds_kernel(const ChunkArgs 
 #pragma unroll
         for (int sub = 0; sub < LY::NIK; ++sub) {
           const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
-          if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+          if (q % 4 == W) dma16(kr, slot + q * 1024, dvoff[q / 4]);
         }
 #pragma unroll
         for (int sub = 0; sub < LY::NIV; ++sub) {
           const int q = G * LY::NIK + gi * LY::NIV + sub;
-          if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+          if (q % 4 == W) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
         }
+      }
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      switch (wave) {
+        case 0: issue_as(std::integral_constant<int, 0>{}, s); break;
+        case 1: issue_as(std::integral_constant<int, 1>{}, s); break;
+        case 2: issue_as(std::integral_constant<int, 2>{}, s); break;
+        default: issue_as(std::integral_constant<int, 3>{}, s); break;
       }
     };
     int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
@@ -473,8 +484,12 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_lds_kernel(const ChunkArgs 
 
       // ---- the ring: steps s+1 .. s+RS-1 in flight while step s is computed
       for (int s = 0; s < nsteps; ++s) {
-        const int later = min(RS - 2, nsteps - 1 - s);
-        wait_dma_then_barrier(later * cw);
+        if constexpr (RS == 2) {
+          wait_dma_then_barrier(0);
+        } else {
+          const int later = min(RS - 2, nsteps - 1 - s);
+          wait_dma_then_barrier(later * cw);
+        }
         __builtin_amdgcn_s_setprio(3);
         if (s + RS - 1 < nsteps) issue(s + RS - 1);
         compute(s);

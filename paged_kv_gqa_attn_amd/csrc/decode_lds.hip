@@ -166,8 +166,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     }
 
     // ---- DMA of step s of the current segment into ring slot s % R (each
-    // wave its share) ------------------------------------------------------------
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    // wave its share: instructions q with q % 4 == W, W the wave index as a
+    // compile-time constant, so that the selection costs no branches) ---------
+    auto issue_as = [&](auto wc, int s) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
       const uint32_t slot = uint32_t(s % LY::R) * LY::SLOT;   // ring starts at LDS byte 0
       const int t0 = seg_t0 + s * T;
 #pragma unroll
@@ -183,13 +185,21 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 #pragma unroll
         for (int sub = 0; sub < LY::NIK; ++sub) {
           const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
-          if (q % 4 == wave) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+          if (q % 4 == W) dma16(kr, slot + q * 1024, dvoff[q / 4]);
         }
 #pragma unroll
         for (int sub = 0; sub < LY::NIV; ++sub) {
           const int q = G * LY::NIK + gi * LY::NIV + sub;
-          if (q % 4 == wave) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+          if (q % 4 == W) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
         }
+      }
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      switch (wave) {
+        case 0: issue_as(std::integral_constant<int, 0>{}, s); break;
+        case 1: issue_as(std::integral_constant<int, 1>{}, s); break;
+        case 2: issue_as(std::integral_constant<int, 2>{}, s); break;
+        default: issue_as(std::integral_constant<int, 3>{}, s); break;
       }
     };
     int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
@@ -426,8 +436,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
         // every wave's DMA of step s has landed (this wave may still have the
         // DMA of the later steps outstanding: cw instructions each), and every
         // wave is done with step s-1, whose slot the next issue overwrites
-        const int later = min(LY::R - 2, nsteps - 1 - s);
-        wait_dma_then_barrier(later * cw);
+        if constexpr (LY::R == 2) {
+          wait_dma_then_barrier(0);
+        } else {
+          const int later = min(LY::R - 2, nsteps - 1 - s);
+          wait_dma_then_barrier(later * cw);
+        }
         // Issue priority: the DMA and the score / softmax chain (short,
         // latency bound) go ahead of the other workgroup's wave on this SIMD,
         // whose VALU-heavy PV part then fills the gaps (measured 3-8% faster).
