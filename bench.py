@@ -18,6 +18,9 @@ GB/s against 8 TB/s from hipEvents on the launch stream) and a cpu_baseline
 object (the fp64 oracle timed on a bounded sample on the host cores).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
+      (defaults 400 and 100: after idle the GPU's clocks take some tens of
+      milliseconds of sustained load to settle, and a 50-step run after 5
+      warmup steps measured the default workload ~8% slower)
   python bench.py --summarize-stats DIR --label NAME   (rocprofv3 --stats CSV -> profiles/)
   python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
   python bench.py --metadata     (paging-metadata update and copy-on-write timings)
@@ -538,8 +541,8 @@ def run_metadata(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=1000)
     ap.add_argument("--force-partitions", type=int, default=0)
