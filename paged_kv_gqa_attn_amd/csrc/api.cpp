@@ -440,14 +440,16 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
   const int64_t L = max_seq_len;
   const int64_t r = s.Hq / s.Hkv;
-  // the window kernel takes short chunks (a workgroup per kv-head quad, one
-  // per CU); the tile-conversion kernel the rest (a workgroup per kv head and
-  // 64*nt query rows, one or two per CU)
+  // the window kernel takes short chunks (a workgroup per kv-head quad, two
+  // per CU for at most 16 query rows per kv head, else one); the
+  // tile-conversion kernel the rest (a workgroup per kv head and 64*nt query
+  // rows, one or two per CU)
   const bool window = chunk_window_ok(int64_t(tq) * r, s.Hkv, s.k_type, s.v_type, s.D);
   const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
   const int64_t qt = window ? 1 : (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // row blocks per unit
   const int64_t heads_per_unit = window ? 4 : 1;
-  const int wgs_per_cu = window ? 1 : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
+  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(int(ceil_div(int64_t(tq) * r, 16)))
+                                : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {

@@ -34,17 +34,21 @@ constexpr int kThreads = 256;
 constexpr int kNidS = 512;     // block ids staged per segment of a partition
 constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
 
-// The ring of this kernel: one workgroup per CU (the column groups take the
-// registers of two), so it may use twice the decode kernel's LDS.
+// The ring of this kernel. With one column group (at most 16 query rows per
+// kv head) the registers fit two workgroups per CU, and the ring is the
+// decode kernel's; with more, one workgroup per CU takes the registers of
+// two, so it may use twice the decode kernel's LDS.
 template <int KT, int VT, int D, int NQ>
 struct WinRing {
   using LY = LdsLayout<KT, VT, D>;
-  static constexpr int R = (2 * kLdsRingBytes) / LY::SLOT < 4 ? (2 * kLdsRingBytes) / LY::SLOT : 4;
+  static constexpr int kWgsPerCu = chunk_window_wgs_per_cu(NQ);
+  static constexpr int R = kWgsPerCu == 2 ? LY::R
+                           : ((2 * kLdsRingBytes) / LY::SLOT < 4 ? (2 * kLdsRingBytes) / LY::SLOT : 4);
   static constexpr int BYTES = R * LY::SLOT;
 };
 
 template <int KT, int VT, int D, int NQ>
-__global__ void __launch_bounds__(kThreads, 1) chunk_lds_kernel(const ChunkArgs a) {
+__global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_lds_kernel(const ChunkArgs a) {
   using KF = KFmt<KT, D>;
   using VF = VFmt<VT, D>;
   using WR = WinRing<KT, VT, D, NQ>;
