@@ -242,3 +242,40 @@ def test_unaligned_pools_run_the_tile_kernel():
         outs.append(out)
     assert torch.equal(outs[0], outs[1])
     _check(c, qc, outs[0])
+
+
+@pytest.mark.parametrize("Tq", [2, 4, 8])
+def test_verify_windows_at_full_size(Tq):
+    """Verify windows of 2, 4 and 8 tokens over Q4_0 K/V, B=8 x 32768 tokens
+    (the chunk benchmark's workloads), on the automatic plan: the window
+    kernel at two workgroups per CU for 12 query rows per kv head, at one
+    for 24, the tile kernel for 48. One sequence per case (2, 4, 0) is
+    checked against the oracle, which reads host copies of just its blocks."""
+    from gpu_util import BlockSubset
+    pa = pa_mod()
+    case = synth.workload("uniform_q4_0", B=8, L=32768, seed=1500 + Tq, device=DEV)
+    qc = torch.randn((case.B, Tq, case.Hq, case.D), generator=torch.Generator().manual_seed(1600 + Tq))
+    shape = pa.shape_of(case.B, case.Hq, case.Hkv, case.D, case.block_size, case.nblocks,
+                        case.max_blocks, case.k_fmt, case.v_fmt)
+    plan = pa.paged_attn_chunk_plan(shape, Tq, max(case.seq_lens), total_tokens=sum(case.seq_lens),
+                                    scale=case.scale)
+    assert plan.path == (2 if Tq * case.Hq // case.Hkv <= 32 else 1)
+    ws = pa.workspace(plan, DEV)
+    out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
+    pa.paged_attn_chunk(plan, qc.to(DEV), case.k_pool, case.v_pool, case.table, case.seq_len, ws, out)
+    torch.cuda.synchronize()
+    assert pa.paged_attn_status(ws) == 0
+    tab = case.table.cpu()
+    for b in (Tq % case.B,):
+        n = -(-case.seq_lens[b] // case.block_size)
+        blocks = tab[b, :n].tolist()
+        ref = oracle.chunk(qc[b:b + 1], BlockSubset(case.k_pool, blocks), BlockSubset(case.v_pool, blocks),
+                           tab[b:b + 1], case.seq_len[b:b + 1].cpu(), Hkv=case.Hkv, D=case.D,
+                           block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
+                           nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
+        got = out[b:b + 1].cpu().double().numpy()
+        assert np.isfinite(got).all(), f"sequence {b}: non-finite output"
+        worst = float(rel_err_rows(got, ref).max())
+        assert worst <= tol_for(case), f"sequence {b}: max row error {worst:.3e}"
+    del case, ws, out
+    torch.cuda.empty_cache()
