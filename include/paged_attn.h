@@ -266,9 +266,10 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * workgroup into LDS for four waves of query rows (any Tq); path 2, for
  * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128) with Hkv
  * a multiple of 4 (verify windows), streams the pool through the decode
- * kernel's LDS ring, each wave serving one kv head with all of its rows. The plan picks path 2 where it
- * applies; a caller may set path = 1 on such a plan to force the general
- * kernel. Pools that are not 16-byte aligned run path 1.
+ * kernel's LDS ring, each wave serving one kv head with all of its rows. The
+ * plan picks path 2 where it applies; a caller may set path = 1 on such a
+ * plan to force the general kernel. Pools that are not 16-byte aligned run
+ * path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;
