@@ -401,7 +401,7 @@ def run_chunk(args):
     qs = [torch.randn((B, Tq, c0.Hq, c0.D), generator=g, device=dev) for _ in cases]
     shape = pa.shape_of(c0.B, c0.Hq, c0.Hkv, c0.D, c0.block_size, c0.nblocks, c0.max_blocks,
                         c0.k_fmt, c0.v_fmt)
-    plan = pa.paged_attn_chunk_plan(shape, Tq, L, total_tokens=B * L)
+    plan = pa.paged_attn_chunk_plan(shape, Tq, L, total_tokens=B * L, force_partitions=args.force_partitions)
     if args.chunk_path:
         plan.path = args.chunk_path
     ws = pa.workspace(plan, dev)
