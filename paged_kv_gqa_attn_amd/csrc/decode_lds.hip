@@ -98,7 +98,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   const uint32_t ksh = KF::shift(j);
   const auto vl = VF::lane(m, 0u);
   const uint32_t mg = opaque_vgpr(kMagic);
-  const int bs_mask = (1 << a.bs_shift) - 1;
   const int seg_tokens = kNidS << a.bs_shift;
 
   for (int u = logical; u < n_units; u += Gd) {
@@ -165,42 +164,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
       bad |= __syncthreads_or(badl);        // also publishes ids[]
     }
 
-    // ---- DMA of step s of the current segment into ring slot s % R (each
-    // wave its share: instructions q with q % 4 == W, W the wave index as a
-    // compile-time constant, so that the selection costs no branches) ---------
-    auto issue_as = [&](auto wc, int s) __attribute__((always_inline)) {
-      constexpr int W = decltype(wc)::value;
-      const uint32_t slot = uint32_t(s % LY::R) * LY::SLOT;   // ring starts at LDS byte 0
-      const int t0 = seg_t0 + s * T;
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const int tg = t0 + 16 * gi;
-        const bool live = tg < seg_t1;
-        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
-        const int slot0 = live ? (tg & bs_mask) : 0;
-        const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
-                                    live ? 16u * kstride : 0u);
-        const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
-                                    live ? 16u * vstride : 0u);
-#pragma unroll
-        for (int sub = 0; sub < LY::NIK; ++sub) {
-          const int q = gi * LY::NIK + sub;            // instruction q is issued by wave q % 4
-          if (q % 4 == W) dma16(kr, slot + q * 1024, dvoff[q / 4]);
-        }
-#pragma unroll
-        for (int sub = 0; sub < LY::NIV; ++sub) {
-          const int q = G * LY::NIK + gi * LY::NIV + sub;
-          if (q % 4 == W) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
-        }
-      }
-    };
+    // ---- DMA of step s of the current segment into ring slot s % LY::R (each
+    // wave its share) -----------------------------------------------------------
     auto issue = [&](int s) __attribute__((always_inline)) {
-      switch (wave) {
-        case 0: issue_as(std::integral_constant<int, 0>{}, s); break;
-        case 1: issue_as(std::integral_constant<int, 1>{}, s); break;
-        case 2: issue_as(std::integral_constant<int, 2>{}, s); break;
-        default: issue_as(std::integral_constant<int, 3>{}, s); break;
-      }
+      issue_step<LY>(wave, a, uint32_t(s % LY::R) * LY::SLOT, seg_t0 + s * T, seg_t1, ids, jb0, kstride,
+                     vstride, dvoff);
     };
     int nsteps = (seg_t1 - seg_t0 + T - 1) / T;
     for (int s = 0; s < LY::R - 1 && s < nsteps; ++s) issue(s);

@@ -79,6 +79,53 @@ __device__ __forceinline__ void dma16(rsrc_t R, uint32_t dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, kDmaNonTemporal);
 }
 
+// DMA of one step into the ring slot at LDS byte `slot`: the LY::G 16-slot
+// groups of K and V of tokens t0 .. t0 + 16*LY::G - 1 of the current segment
+// (block ids[] staged from block jb0; groups at or past seg_t1 get a
+// zero-size resource and read nothing). Wave W issues the instructions q
+// with q % 4 == W; W is a compile-time constant, so the selection costs no
+// branches. dvoff[i] is this lane's pool offset in instruction W + 4i.
+template <class LY, int W, class Args>
+__device__ __forceinline__ void issue_step_as(const Args& a, uint32_t slot, int t0, int seg_t1,
+                                              const int32_t* ids, int jb0, uint32_t kstride,
+                                              uint32_t vstride, const uint32_t* dvoff) {
+  constexpr int G = LY::G;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int tg = t0 + 16 * gi;
+    const bool live = tg < seg_t1;
+    const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+    const int slot0 = live ? (tg & bs_mask) : 0;
+    const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
+                                live ? 16u * kstride : 0u);
+    const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
+                                live ? 16u * vstride : 0u);
+#pragma unroll
+    for (int sub = 0; sub < LY::NIK; ++sub) {
+      const int q = gi * LY::NIK + sub;
+      if (q % 4 == W) dma16(kr, slot + q * 1024, dvoff[q / 4]);
+    }
+#pragma unroll
+    for (int sub = 0; sub < LY::NIV; ++sub) {
+      const int q = G * LY::NIK + gi * LY::NIV + sub;
+      if (q % 4 == W) dma16(vr, slot + LY::VOFF + (gi * LY::NIV + sub) * 1024, dvoff[q / 4]);
+    }
+  }
+}
+// The same for the calling wave (one switch on the wave index).
+template <class LY, class Args>
+__device__ __forceinline__ void issue_step(int wave, const Args& a, uint32_t slot, int t0, int seg_t1,
+                                           const int32_t* ids, int jb0, uint32_t kstride,
+                                           uint32_t vstride, const uint32_t* dvoff) {
+  switch (wave) {
+    case 0: issue_step_as<LY, 0>(a, slot, t0, seg_t1, ids, jb0, kstride, vstride, dvoff); break;
+    case 1: issue_step_as<LY, 1>(a, slot, t0, seg_t1, ids, jb0, kstride, vstride, dvoff); break;
+    case 2: issue_step_as<LY, 2>(a, slot, t0, seg_t1, ids, jb0, kstride, vstride, dvoff); break;
+    default: issue_step_as<LY, 3>(a, slot, t0, seg_t1, ids, jb0, kstride, vstride, dvoff); break;
+  }
+}
+
 // s_waitcnt vmcnt(n) (n wave-uniform, at most 15; larger n waits for more
 // than needed, which is safe) followed by the workgroup barrier. The asm
 // memory clobber keeps every LDS read of the step after the barrier.
