@@ -92,14 +92,14 @@ struct ChunkArgs {
   float qscale;            // scale * log2(e)
   int32_t nt;              // 16-row query tiles per wave (chunk_wave_tiles)
 };
-// Whether the window kernel takes a chunk with `rows` query rows per kv head
-// (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
-// registers hold with their accumulators; Hkv % 4 == 0; the shapes
-// lds_groups() admits.
 // Workgroups per CU of the window chunk kernel with NQ column groups of 16
 // query rows: two when one group fits (the decode kernel's register and LDS
 // budget), else one.
 constexpr int chunk_window_wgs_per_cu(int nq) { return nq == 1 ? 2 : 1; }
+// Whether the window kernel takes a chunk with `rows` query rows per kv head
+// (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
+// registers hold with their accumulators; Hkv % 4 == 0; the shapes
+// lds_groups() admits.
 constexpr int chunk_window_rows(int D) { return D == 256 ? 32 : 48; }
 constexpr bool chunk_window_ok(int64_t rows, int hkv, int kt, int vt, int D) {
   return (D == 128 || D == 256) && rows <= chunk_window_rows(D) && hkv % 4 == 0 &&
