@@ -279,3 +279,16 @@ def test_verify_windows_at_full_size(Tq):
         assert worst <= tol_for(case), f"sequence {b}: max row error {worst:.3e}"
     del case, ws, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("Tq", [2, 5])
+def test_more_units_than_workgroups(Tq, path):
+    """A chunk plan for a 2-CU device: each workgroup takes many units in
+    turn, across sequences of different lengths (one empty)."""
+    c, qc = _case([3000, 77, 1000, 0, 513], Tq, seed=71 + Tq, k_fmt="q4_0", v_fmt="q4_0")
+    plan = _plan(c, Tq, path=path, num_cus=2, partition_tokens=256)
+    assert plan.grid < sum(-(-L // 256) for L in c.seq_lens)
+    out, ws = _run(c, qc, plan)
+    _check(c, qc, out)
+    assert pa_mod().paged_attn_status(ws) == 0

@@ -312,3 +312,20 @@ def test_mixed_scales_within_one_sequence():
     for force in (0, 1, 4):
         out, _ = run(g, plan_for(case, force_partitions=force))
         check_parity(case, out)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "f16")])
+def test_more_units_than_workgroups(pair, path):
+    """A plan for a 2-CU device: a handful of workgroups each take many
+    (sequence, partition) units in turn, across sequences of different
+    lengths (one empty), so every unit start after the first (block ids,
+    q values, ring reuse) runs."""
+    case = _case([3000, 77, 1000, 0, 513], k_fmt=pair[0], v_fmt=pair[1], seed=61)
+    g = case.to(DEV)
+    plan = plan_for(case, path=path, num_cus=2, partition_tokens=256)
+    units = sum(-(-L // 256) for L in case.seq_lens) * (case.Hkv // 4 if plan.path == 2 else 1)
+    assert plan.grid < units
+    out, ws = run(g, plan)
+    assert pa_mod().paged_attn_status(ws) == 0
+    check_parity(case, out)
