@@ -17,11 +17,12 @@
 // then the four waves through LDS). The first kPre partitions of every class
 // are loaded together with the m values the max needs, so one memory latency
 // covers both, and the max is reduced with lane shuffles and one barrier.
-// With many rows of few partitions (p_max <= 16, e.g. the Tq*Hq rows of a
-// prefill chunk or a verify window) that layout leaves most threads idle and launches tens
-// of thousands of workgroups, and merge_rows_kernel is used instead: one
-// thread per (row, 8 output columns) walks the row's partitions in order, 8
-// rows per workgroup at D=256.
+// With many rows of few partitions (p_max <= 16 over at least 1024 rows, or
+// p_max <= 32 over at least 512, e.g. the Tq*Hq rows of a prefill chunk or
+// a verify window) that layout leaves most threads idle and launches
+// thousands of workgroups, and merge_rows_kernel is used instead: one thread
+// per (row, 8 output columns) reads all of the row's partitions at once and
+// sums them in order, 8 rows per workgroup at D=256.
 // Loop bounds are the runtime partition count (llama.cpp PR #13, the
 // SGPR-exhaustion fix: a constant-folded bound fully unrolled the reduction).
 #include "pa_device.h"
@@ -166,6 +167,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
 }
 
 constexpr int kRowsMergeMinRows = 1024;   // fewer rows: the wide layout has more parallelism
+                                          // (half as many when up to 32 partitions per row)
 
 // NPM: the most partitions a row has (8 or 16)
 template <int NPM>
@@ -232,14 +234,17 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.D % kCols) return hipErrorInvalidValue;
-  if (a.p_max <= 16 && int64_t(a.B) * a.Hq >= kRowsMergeMinRows) {
-    const int64_t threads = int64_t(a.B) * a.Hq * (a.D / 8);
+  const int64_t rows = int64_t(a.B) * a.Hq;
+  if ((a.p_max <= 16 && rows >= kRowsMergeMinRows) || (a.p_max <= 32 && rows >= kRowsMergeMinRows / 2)) {
+    const int64_t threads = rows * (a.D / 8);
     const int64_t blocks = (threads + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.p_max <= 8)
       hipLaunchKernelGGL(merge_rows_kernel<8>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
-    else
+    else if (a.p_max <= 16)
       hipLaunchKernelGGL(merge_rows_kernel<16>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_rows_kernel<32>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq * (a.D / kCols)), dim3(kThreads), 0, stream, a);
   }

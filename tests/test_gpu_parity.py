@@ -191,6 +191,8 @@ MERGE_CASES = {
     "rows_p5": ([0, 1, 64, 65, 300, 17, 128, 129] * 5 + [0, 300, 33, 200], 24, 4),
     # ... and of at most 16 partitions
     "rows_p16": ([0, 1, 64, 65, 1000, 17, 640, 129] * 5 + [0, 1000, 33, 200], 24, 4),
+    # 27 x 24 = 648 rows of at most 32 partitions
+    "rows_p32": ([0, 1, 64, 65, 2000, 17, 1280, 129] * 3 + [0, 2048, 33], 24, 4),
 }
 
 
@@ -201,7 +203,7 @@ def test_merge_kernel_on_oracle_partials(name):
     merge of the same values; and against the unrounded partials within what
     binary16 rounding of o can move the result (2^-11 of the largest |o_p|).
     Both merge layouts are covered: few rows (any partition count) and many
-    rows of at most 8 or 16 partitions."""
+    rows of at most 8, 16 or 32 partitions."""
     pa = pa_mod()
     lens, Hq, Hkv = MERGE_CASES[name]
     case = _case(lens, k_fmt="f16", v_fmt="q8_0", seed=23, Hq=Hq, Hkv=Hkv)
