@@ -18,7 +18,7 @@
 // are loaded together with the m values the max needs, so one memory latency
 // covers both, and the max is reduced with lane shuffles and one barrier.
 // With many rows of few partitions (p_max <= 16 over at least 1024 rows, or
-// p_max <= 32 over at least 256, e.g. the Tq*Hq rows of a prefill chunk or
+// p_max <= 32 over at least 512, e.g. the Tq*Hq rows of a prefill chunk or
 // a verify window) that layout leaves most threads idle and launches
 // thousands of workgroups, and merge_rows_kernel is used instead: one thread
 // per (row, 8 output columns) reads all of the row's partitions at once and
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
 }
 
 constexpr int kRowsMergeMinRows = 1024;   // fewer rows: the wide layout has more parallelism
-                                          // (a quarter as many when up to 32 partitions per row)
+                                          // (half as many when up to 32 partitions per row)
 
 // NPM: the most partitions a row has (8 or 16)
 template <int NPM>
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a)
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.D % kCols) return hipErrorInvalidValue;
   const int64_t rows = int64_t(a.B) * a.Hq;
-  if ((a.p_max <= 16 && rows >= kRowsMergeMinRows) || (a.p_max <= 32 && rows >= kRowsMergeMinRows / 4)) {
+  if ((a.p_max <= 16 && rows >= kRowsMergeMinRows) || (a.p_max <= 32 && rows >= kRowsMergeMinRows / 2)) {
     const int64_t threads = rows * (a.D / 8);
     const int64_t blocks = (threads + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
