@@ -40,14 +40,16 @@ extern __shared__ __align__(16) unsigned char g_lds[];
 
 // LDS placement of the four head rows of a slot. Within slot t, head w's row
 // is stored at row position (w + rot(t)) mod 4, so that the 64 lanes of a
-// wave, which read the same head from 16 slots (K) or 4 slots (V) at once,
-// spread over the LDS banks (a plain copy puts 16 K rows 576 bytes apart on
-// the same few banks). Only rows made of whole 16-byte chunks can be moved
-// this way (row_bytes % 16 == 0); other rows keep rot = 0.
+// wave, which read the same head's K rows from 16 slots at once, spread over
+// the LDS banks (a plain copy puts those 16 rows 576 bytes apart on the same
+// few banks; measured 5% slower). The V rows a wave reads at once come from 4
+// slots and keep their pool order: rotating them measured 0.5-1% slower.
+// Only rows made of whole 16-byte chunks can be moved this way
+// (row_bytes % 16 == 0); other rows keep rot = 0.
 template <int RB> struct RowRot {
   static constexpr bool on = RB % 16 == 0;
-  __device__ static int k(int t) { return on ? (t >> 2) & 3 : 0; }          // K: 16 slots
-  __device__ static int v(int t) { return on ? ((t >> 2) & 1) << 1 : 0; }   // V: 4 slots
+  __device__ static int k(int t) { return on ? (t >> 2) & 3 : 0; }   // K: 16 slots
+  __device__ static int v(int) { return 0; }                        // V: 4 slots
 };
 
 // Pool offset of the chunk lane l fetches in the 1 KB DMA instruction `sub`
