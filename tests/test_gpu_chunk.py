@@ -112,6 +112,19 @@ def test_nine_type_pairs_short_window(pair, D, path):
         assert pa_mod().paged_attn_status(ws) == 0
 
 
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
+def test_nine_type_pairs_two_token_window(pair, D):
+    """A 2-token window (12 query rows per kv head): the window kernel at two
+    workgroups per CU with the decode kernel's ring, for every type pair."""
+    seed = 3 * synth.FORMATS.index(pair[0]) + synth.FORMATS.index(pair[1]) + D + 131
+    c, qc = _case([300, 77, 16], 2, seed=seed, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 64}):
+        out, ws = _run(c, qc, _plan(c, 2, path=2, **kw))
+        _check(c, qc, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("Tq", [1, 2, 16, 33, 130])
 def test_chunk_lengths_and_partitions(Tq, path):
