@@ -17,10 +17,12 @@ whole step), ms_per_step, a roofline object for the decode kernel (achieved
 GB/s against 8 TB/s from hipEvents on the launch stream) and a cpu_baseline
 object (the fp64 oracle timed on a bounded sample on the host cores).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME]
-      (defaults 400 and 100: after idle the GPU's clocks take some tens of
-      milliseconds of sustained load to settle, and a 50-step run after 5
-      warmup steps measured the default workload ~8% slower)
+  python bench.py [--steps K] [--warmup W] [--settle-ms S] [--workload NAME]
+      (defaults 200, 20 and 200: after idle the GPU's clocks take some tens
+      of milliseconds of sustained load to settle, so steps first run back to
+      back for S ms - recorded in the line as "settle" - then W warmup steps,
+      then the K timed steps with no event inside, then the same K steps
+      again with events around each decode launch for the kernel split)
   python bench.py --summarize-stats DIR --label NAME   (rocprofv3 --stats CSV -> profiles/)
   python bench.py --summarize-pmc DIR --label NAME     (rocprofv3 --pmc CSVs -> profiles/)
   python bench.py --metadata     (paging-metadata update and copy-on-write timings)
@@ -113,16 +115,16 @@ def build_cases(name, seed, device, min_bytes):
 
 
 def cpu_baseline(case, budget_s=20.0):
-    """Time the fp64 oracle on a bounded sample of the workload (whole (b, g)
-    groups, in order, until about budget_s of CPU work)."""
-    import numpy as np
+    """Time the fp64 oracle on a bounded sample of the workload: whole
+    (sequence, kv-head) groups, in order, dealt over a thread pool of one
+    worker per host core (at most 16, the CPU share of one GPU), each worker
+    with one BLAS thread, until about budget_s of wall time."""
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     import synth
+    from threadpoolctl import threadpool_limits
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cores))
     kp = case.k_pool.cpu().numpy().reshape(-1)
     vp = case.v_pool.cpu().numpy().reshape(-1)
     tab = case.table.cpu()
@@ -132,25 +134,37 @@ def cpu_baseline(case, budget_s=20.0):
     kw = dict(Hkv=case.Hkv, D=case.D, block_size=case.block_size, k_fmt=case.k_fmt,
               v_fmt=case.v_fmt, nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
     items = [(b, g) for b in range(case.B) for g in range(case.Hkv) if case.seq_lens[b] > 0]
-    done, nbytes, t0 = [], 0, time.perf_counter()
+    done = []
+    t0 = time.perf_counter()
     cpu0 = time.process_time()
-    for it in items:
-        oracle.decode_heads(q, kp, vp, tab, sl, items=[it], **kw)
-        done.append(it)
-        nbytes += case.seq_lens[it[0]] * (rbk + rbv)
-        if time.perf_counter() - t0 > budget_s:
-            break
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        pending, nxt = {}, 0
+        while nxt < len(items) or pending:
+            while nxt < len(items) and len(pending) < workers and time.perf_counter() - t0 < budget_s:
+                it = items[nxt]
+                pending[ex.submit(oracle.decode_heads, q, kp, vp, tab, sl, items=[it], **kw)] = it
+                nxt += 1
+            if not pending:
+                break
+            fin, _ = wait(list(pending), return_when=FIRST_COMPLETED)
+            for f in fin:
+                f.result()
+                done.append(pending.pop(f))
     wall = time.perf_counter() - t0
-    eff = (time.process_time() - cpu0) / max(wall, 1e-9)
+    busy = (time.process_time() - cpu0) / max(wall, 1e-9)
+    nbytes = sum(case.seq_lens[b] * (rbk + rbv) for b, _ in done)
     toks = sum(case.seq_lens[b] for b, _ in done)
     return {
         "value": round(nbytes / wall / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": int(workers),
         "kind": "oracle",
+        "host_cores": int(host_cores),
+        "busy_cores": round(busy, 1),
+        "blas_threads_per_worker": 1,
         "sample": (f"fp64 numpy oracle over {len(done)} of {len(items)} (sequence, kv-head) groups "
-                   f"({toks} token rows, {nbytes} K/V bytes) in {wall:.1f} s; "
-                   f"BLAS threads {threads}, mean busy cores {eff:.1f}"),
+                   f"({toks} token rows, {nbytes} K/V bytes) in {wall:.1f} s on a pool of {workers} "
+                   f"worker threads (one BLAS thread each; {busy:.1f} cores busy on average)"),
     }
 
 
@@ -200,21 +214,43 @@ def run_bench(args):
             ev_end.record(stream)
         pa.paged_attn_merge(plan, ws, c.seq_len, out, stream=sptr)
 
+    # Clock settle: after idle the GPU's clocks take some tens of milliseconds
+    # of sustained load to reach the level a serving loop runs at, so steps
+    # run back to back for at least --settle-ms first (synchronising every 16
+    # steps so the host never runs far ahead). Recorded in the JSON line.
+    settle_steps, settle_t0 = 0, time.perf_counter()
+    while (time.perf_counter() - settle_t0) * 1e3 < args.settle_ms:
+        for _ in range(16):
+            step(cases[settle_steps % len(cases)])
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - settle_t0) * 1e3
     for i in range(args.warmup):
         step(cases[i % len(cases)])
     torch.cuda.synchronize()
-    # Two timing events per step, around the decode launch: an event record
-    # costs the stream a few µs, so the merge is timed from the decode's end
+
+    # Timed region: exactly `steps` steps with no event inside (an event
+    # record costs the stream a few µs), bracketed by synchronisations.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(cases[i % len(cases)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us_events = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    # Kernel split: the same steps again with two events per step around the
+    # decode launch on its stream; the merge is timed from the decode's end
     # event to the next step's start event (one more event closes the loop).
     ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(cases[i % len(cases)], ev_start[i], ev_end[i])
     ev_start[args.steps].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     dec_ms = [ev_start[i].elapsed_time(ev_end[i]) for i in range(args.steps)]
     mrg_ms = [ev_end[i].elapsed_time(ev_start[i + 1]) for i in range(args.steps)]
     step_ms = [ev_start[i].elapsed_time(ev_start[i + 1]) for i in range(args.steps)]
@@ -234,6 +270,7 @@ def run_bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -248,7 +285,8 @@ def run_bench(args):
             "live_tokens": sum(c0.seq_lens), "psize": plan.psize, "p_max": plan.p_max,
             "grid": plan.grid, "decode_kernel": DECODE_KERNELS[plan.path - 1],
             "pool_copies": len(cases),
-            "step_us_median_events": round(med * 1e3, 2),
+            "step_us_events": round(step_us_events, 2),
+            "split_pass_step_us_median": round(med * 1e3, 2),
             "decode_us_mean": round(dec_avg * 1e3, 2),
             "merge_us_mean": round(sum(mrg_ms) / len(mrg_ms) * 1e3, 2),
             "step_pct_of_peak": round(100 * value / PEAK_GBS, 2),
@@ -413,6 +451,13 @@ def run_chunk(args):
         pa.paged_attn_chunk(plan, qs[i % len(cases)], c.k_pool, c.v_pool, c.table, c.seq_len, ws, out,
                             stream=stream)
 
+    settle_steps, settle_t0 = 0, time.perf_counter()   # clock settle, as in run_bench
+    while (time.perf_counter() - settle_t0) * 1e3 < args.settle_ms:
+        for _ in range(16):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - settle_t0) * 1e3
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -442,7 +487,8 @@ def run_chunk(args):
     line = {
         "metric": "paged chunk attention step (chunk kernel + merge)",
         "value": round(wall_us, 2), "unit": "us", "higher_is_better": False,
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "f16", "data": "synthetic",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps}, "dtype": "f16", "data": "synthetic",
         "config": {"workload": desc, "name": args.chunk, "B": B, "L": L, "Tq": Tq, "Hq": c0.Hq,
                    "Hkv": c0.Hkv, "D": c0.D, "k_type": c0.k_fmt, "v_type": c0.v_fmt,
                    "psize": plan.psize, "p_max": plan.p_max, "grid": plan.grid,
@@ -542,8 +588,10 @@ def run_metadata(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="back-to-back steps for at least this long before the warmup (recorded)")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=1000)
     ap.add_argument("--force-partitions", type=int, default=0)

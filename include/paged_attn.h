@@ -220,7 +220,13 @@ int32_t paged_attn_decode(const pa_plan* plan, const float* q, const void* k_poo
 int32_t paged_attn_merge(const pa_plan* plan, const void* ws, uint64_t ws_bytes,
                          const int32_t* seq_len, float* out, void* stream);
 
-/* paged_attn_step - paged_attn_decode followed by paged_attn_merge. */
+/*
+ * paged_attn_step - one whole decode step: paged_attn_decode followed by
+ * paged_attn_merge on the same stream (lucebox PR #555, Summary: a decode
+ * step attends over context partitions whose partials are then recombined by
+ * the split-softmax merge). Arguments, ownership and errors as for the two
+ * calls; the first refusal is returned and nothing after it is launched.
+ */
 int32_t paged_attn_step(const pa_plan* plan, const float* q, const void* k_pool,
                         const void* v_pool, const int32_t* block_table,
                         const int32_t* seq_len, void* ws, uint64_t ws_bytes, float* out,
@@ -244,14 +250,20 @@ int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
 
 /*
  * paged_attn_status - synchronise `stream`, then read and clear the status
- * word of ws into *flags (PA_STATUS_* bits).
+ * word of ws into *flags (PA_STATUS_* bits). The word is how the kernels
+ * report what only the device sees: a live block-table entry outside the
+ * pool or a seq_len outside the table's capacity (lucebox PR #555,
+ * Validation: bounds guards on corrupt block tables). ws is the workspace
+ * the decode, chunk or gather calls were given (its first 4 bytes).
+ * Returns PA_ERR_INVALID for null arguments and PA_ERR_HIP if the copy or
+ * the synchronisation fails; *flags is then unchanged.
  */
 int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
 
 /*
  * Multi-token queries over the paged pool: chunked prefill and verify windows
- * (llama.cpp PR #13 HRX, Roadmap item 3: multi-token queries over the
- * preceding paged K/V with causal attention inside the chunk; TensorFold PR
+ * (lucebox PR #555, Roadmap item 3: several query tokens per sequence attend
+ * over the K/V already in the pool, causally inside the chunk; TensorFold PR
  * #1418, What: paged prompt-chunk attention equal to the contiguous one).
  *
  * q and out are fp32 [B][Tq][Hq][D]. seq_len[b] = L counts the chunk's own
@@ -320,8 +332,8 @@ int32_t paged_table_update(int32_t* table, int32_t* seq_len, int32_t B, int32_t 
 
 /*
  * paged_kv_copy_blocks - copy whole blocks inside one pool: the device half
- * of copy-on-write (lucebox PR #555, Roadmap item 6: shared prefix blocks
- * with reference counting and copy-on-write). After kv_pool_cow hands an
+ * of copy-on-write (lucebox PR #555, Roadmap item 6: prefix blocks shared
+ * under reference counts and copied on write). After kv_pool_cow hands an
  * allocation a private id for a shared block, copy the shared block there
  * (in the K pool and in the V pool) before writing into it.
  *   pool          device memory, 16-byte aligned: nblocks blocks of
@@ -348,8 +360,8 @@ int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_t nblocks,
  * handle). Any use of a handle that was released, released twice or issued
  * before a reset returns PA_ERR_STALE_HANDLE and changes nothing.
  *
- * Prefix sharing (lucebox PR #555, Roadmap item 6: shared prefix blocks with
- * reference counting and copy-on-write): every block counts the allocations
+ * Prefix sharing (lucebox PR #555, Roadmap item 6: prefix blocks shared under
+ * reference counts and copied on write): every block counts the allocations
  * that hold it. kv_pool_fork starts an allocation with another's first
  * blocks; a block goes back to the pool the moment the last allocation
  * holding it is released; kv_pool_cow gives an allocation a private block in

@@ -35,8 +35,9 @@ Sources (page titles and sections):
 
 `partials` / `merge` give the split form: per context partition the running
 max m (base-2 logits), the sum l and the normalised output o, then the stable
-max-rescaling merge (lucebox PR #555 Summary, "stable split-softmax merge";
-llama.cpp PR #13 HRX, Changes, the multi-pass KV-block reduction). In exact
+max-rescaling merge (lucebox PR #555, Summary: the partitions are recombined
+by a numerically stable merge of the split softmax; llama.cpp PR #13 HRX,
+Changes: the multi-pass KV-block reduction). In exact
 arithmetic merge(partials(...)) equals decode(...).
 """
 from __future__ import annotations
@@ -211,9 +212,10 @@ def chunk(q, k_pool, v_pool, table, seq_len, *, Hkv: int, D: int, block_size: in
           k_fmt: str, v_fmt: str, nblocks: int, max_blocks: int,
           scale: Optional[float] = None) -> np.ndarray:
     """Multi-token query over the paged pool with causal masking inside the
-    chunk (llama.cpp PR #13 HRX, Roadmap item 3: multi-token queries over the
-    preceding paged K/V, causal attention within the chunk; TensorFold PR
-    #1418, What: paged prompt-chunk attention equal to the contiguous one).
+    chunk (lucebox PR #555, Roadmap item 3: several query tokens per sequence
+    attend over the K/V already in the pool, causally inside the chunk;
+    TensorFold PR #1418, What: paged prompt-chunk attention equal to the
+    contiguous one).
 
     q is [B, Tq, Hq, D]; seq_len[b] = L counts the chunk's own tokens, which
     are the last Tq of the sequence, so chunk token t sits at position
@@ -295,7 +297,7 @@ def partials(q, k_pool, v_pool, table, seq_len, *, Hkv: int, D: int, block_size:
 
 
 def merge(m: np.ndarray, l: np.ndarray, o: np.ndarray, nparts: np.ndarray) -> np.ndarray:
-    """Stable split-softmax merge of partition partials.
+    """Numerically stable merge of the partitions' split-softmax partials.
 
     For each (b, h) over its live partitions p < nparts[b]:
         M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p.

@@ -9,8 +9,8 @@ Sources (page titles and sections):
     Summary: the block table and sequence lengths stay resident on the device
     next to the K/V pool; a decode step uploads only the entries of fresh
     blocks (4 bytes each) instead of the whole live table.
-  * the same page, Roadmap item 6: prefix caching and copy-on-write, i.e.
-    shared prefix blocks with reference counting and copy-on-write.
+  * the same page, Roadmap item 6: prefix caching, where blocks of a common
+    prefix are shared under reference counts and copied before a write.
 
 Each function states the result directly: an update list applied entry by
 entry, a block copy as array slicing, and allocator state as a set of block

@@ -14,7 +14,10 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+# PAGED_ATTN_LIB names another build of the same C ABI (the tests' host-only
+# sanitizer build, whose kernel launchers all refuse); by default the in-tree
+# HIP library.
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(_HERE, "libpaged_attn.so")
 
 PA_F16, PA_Q8_0, PA_Q4_0 = 0, 1, 2
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_CAPACITY, PA_ERR_STALE_HANDLE, PA_ERR_HIP = (

@@ -1,7 +1,7 @@
 // Multi-token queries over the paged pool: chunked prefill and verify windows.
 //
-// What it computes (llama.cpp PR #13 HRX, Roadmap item 3: multi-token queries
-// over the preceding paged K/V with causal attention inside the chunk;
+// What it computes (lucebox PR #555, Roadmap item 3: several query tokens per
+// sequence attend over the K/V already in the pool, causally inside the chunk;
 // TensorFold PR #1418, What: paged prompt-chunk attention that equals the
 // contiguous one bit for bit): q is [B, Tq, Hq, D]; the chunk's Tq tokens are
 // the last Tq of each sequence, so chunk token t of sequence b (length L)

@@ -1,9 +1,9 @@
 // Multi-token queries with few query rows per kv head: the window kernel.
 //
-// What it computes is what chunk.hip computes (llama.cpp PR #13 HRX, Roadmap
-// item 3: multi-token queries over the preceding paged K/V with causal
-// attention inside the chunk; TensorFold PR #1418, What: paged prompt-chunk
-// attention): chunk token t of sequence b (length L) sits at position
+// What it computes is what chunk.hip computes (lucebox PR #555, Roadmap item
+// 3: several query tokens per sequence attend over the K/V already in the
+// pool, causally inside the chunk; TensorFold PR #1418, What: paged
+// prompt-chunk attention): chunk token t of sequence b (length L) sits at position
 // L - Tq + t and attends to the keys at positions 0 .. L - Tq + t of kv head
 // g = h / r. It serves the chunks whose Tq*r query rows of a kv head fit
 // 16*NQ MFMA columns, NQ <= 2 at D = 256 and NQ <= 3 at D = 128 (what one

@@ -382,6 +382,15 @@ decode_kernel(const DecodeArgs a) {
 template <int KT, int VT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = size_t(lds_words(a.B, a.r, D)) * 4;
+  // Large batches and head groups (e.g. B = 1024, or r = 16 at D = 256) need
+  // more than the default 64 KiB of dynamic LDS; a workgroup may use up to
+  // the CU's 160 KiB.
+  if (lds > 65536) {
+    const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<KT, VT, D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+  }
   hipLaunchKernelGGL((decode_kernel<KT, VT, D>), dim3(a.grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

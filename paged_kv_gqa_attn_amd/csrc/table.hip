@@ -1,8 +1,8 @@
 // Paging metadata and block maintenance on the device.
 //
 //   * copy_blocks_kernel: whole-block copies inside one pool, the device half
-//     of copy-on-write (lucebox PR #555, Roadmap item 6: shared prefix blocks
-//     with reference counts and copy-on-write). An allocation that is about
+//     of copy-on-write (lucebox PR #555, Roadmap item 6: prefix blocks shared
+//     under reference counts and copied on write). An allocation that is about
 //     to write into a block it shares receives a fresh block id from the
 //     allocator; the shared block's bytes are copied there first.
 //   * table_update_kernel: scatters a few (sequence, slot, value) entries

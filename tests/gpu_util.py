@@ -104,9 +104,8 @@ class BlockSubset:
 
     def __init__(self, pool_dev, block_ids):
         self.shape = tuple(pool_dev.shape)          # [nblocks, bs, Hkv, rb]
-        ids = sorted(set(int(i) for i in block_ids))
-        self.index = {b: k for k, b in enumerate(ids)}
-        sel = torch.tensor(ids, dtype=torch.int64, device=pool_dev.device)
+        self.ids = np.unique(np.asarray(list(block_ids), dtype=np.int64))
+        sel = torch.from_numpy(self.ids).to(pool_dev.device)
         self.data = pool_dev.index_select(0, sel).cpu().numpy()
 
     def read_rows(self, offsets, rbytes):
@@ -118,16 +117,24 @@ class BlockSubset:
         row = offsets // rb
         blk = row // (bs * hkv)
         within = row % (bs * hkv)
-        k = np.array([self.index[int(b)] for b in blk], dtype=np.int64)
-        flat = self.data.reshape(len(self.index), bs * hkv, rb)
+        k = np.searchsorted(self.ids, blk)
+        if blk.size and (k.max() >= self.ids.size or (self.ids[np.minimum(k, self.ids.size - 1)] != blk).any()):
+            raise KeyError("row of a block that was not copied")
+        flat = self.data.reshape(self.ids.size, bs * hkv, rb)
         return flat[k, within]
+
+
+def all_groups(case):
+    """Every (sequence, kv head) group of a case."""
+    return [(b, g) for b in range(case.B) for g in range(case.Hkv)]
 
 
 def sampled_parity(case_dev, out, items):
     """Oracle check of selected (b, g) groups of a device-resident case; the
     pool bytes the oracle reads are host copies of just those sequences'
-    blocks."""
+    blocks. The whole output must be finite, sampled or not."""
     import types
+    assert bool(torch.isfinite(out).all()), "non-finite values in the output"
     tab = case_dev.table.cpu()
     blocks = set()
     for b, _ in items:

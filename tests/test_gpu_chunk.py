@@ -1,5 +1,5 @@
 """GPU parity of the chunk path (multi-token queries with causal masking in
-the chunk: llama.cpp PR #13 HRX, Roadmap item 3; TensorFold PR #1418, What:
+the chunk: lucebox PR #555, Roadmap item 3; TensorFold PR #1418, What:
 paged equals contiguous bit for bit) against oracle.chunk, through the C ABI.
 
 Tolerance as for decode (per-row max-abs error relative to the row's

@@ -1,8 +1,8 @@
 """GPU checks of the paging-metadata entry points against oracle/metadata.py
 (bit for bit), and an end-to-end decode over a shared prefix with
 copy-on-write (lucebox PR #555, Summary: resident paging metadata updated
-per fresh block; Roadmap item 6: shared prefix blocks with reference counting
-and copy-on-write)."""
+per fresh block; Roadmap item 6: prefix blocks shared under reference counts
+and copied on write)."""
 import numpy as np
 import pytest
 import torch

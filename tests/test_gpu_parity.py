@@ -331,3 +331,31 @@ def test_more_units_than_workgroups(pair, path):
     out, ws = run(g, plan)
     assert pa_mod().paged_attn_status(ws) == 0
     check_parity(case, out)
+
+
+def test_register_kernel_sixteen_heads_per_group_f16_d256():
+    """F16 K and V at D=256 with r = 16 (Hq = 64, Hkv = 4): a shape the LDS
+    ring does not take, so the register kernel runs it, with more than the
+    default 64 KiB of dynamic LDS for its cross-wave combine."""
+    case = _case([300, 45, 0], Hq=64, Hkv=4, D=256, k_fmt="f16", v_fmt="f16", seed=331)
+    g = case.to(DEV)
+    for force in (0, 1, 3):
+        plan = plan_for(case, path=1, force_partitions=force)
+        out, ws = run(g, plan)
+        check_parity(case, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
+def test_largest_batch_on_the_register_kernel():
+    """B = 1024 short sequences (above the LDS kernel's 256): the batch prefix
+    of live partitions alone is 8 KB of LDS."""
+    rng = np.random.default_rng(337)
+    lens = [int(x) for x in rng.integers(0, 40, size=1024)]
+    case = _case(lens, k_fmt="q4_0", v_fmt="q8_0", seed=337)
+    g = case.to(DEV)
+    for force in (0, 2):
+        plan = plan_for(case, force_partitions=force)
+        assert plan.path == 1
+        out, ws = run(g, plan)
+        check_parity(case, out)
+        assert pa_mod().paged_attn_status(ws) == 0

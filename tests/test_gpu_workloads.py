@@ -1,6 +1,7 @@
-"""GPU parity at the pages' workload sizes, on sampled (sequence, kv-head)
-groups the oracle computes one by one, in the launch configuration bench.py
-times (automatic plan, all K/V bytes resident on the device)."""
+"""GPU parity at the pages' workload sizes, on every (sequence, kv-head) group
+(the oracle computes them one by one from host copies of the blocks they
+use), in the launch configuration bench.py times (automatic plan, all K/V
+bytes resident on the device). The whole output must also be finite."""
 import gc
 
 import numpy as np
@@ -8,7 +9,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import plan_for, run, sampled_parity, pa_mod
+from gpu_util import all_groups, plan_for, run, sampled_parity, pa_mod
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -30,8 +31,7 @@ def _run_auto(case):
 def test_uniform_q8_0_4k(B):
     case = synth.workload("uniform_q8_0", B=B, L=4096, seed=1100 + B, device=DEV)
     out, _ = _run_auto(case)
-    items = sorted({(0, 0), (B - 1, 3), (B // 2, 1)})
-    sampled_parity(case, out, items)
+    sampled_parity(case, out, all_groups(case))
     _free()
 
 
@@ -40,7 +40,7 @@ def test_uniform_q4_0_long_context(B, L):
     case = synth.workload("uniform_q4_0", B=B, L=L, seed=1200 + B, device=DEV)
     out, plan = _run_auto(case)
     assert plan.p_max > 1
-    sampled_parity(case, out, [(0, 0), (B - 1, 3)])
+    sampled_parity(case, out, all_groups(case))
     _free()
 
 
@@ -48,14 +48,14 @@ def test_ragged_128k_plus_7x8k():
     case = synth.workload("ragged_q4_0", seed=1300, device=DEV)
     assert sum(case.seq_lens) == 188416
     out, _ = _run_auto(case)
-    sampled_parity(case, out, [(0, 0), (0, 3), (3, 1), (7, 2)])
+    sampled_parity(case, out, all_groups(case))
     _free()
 
 
 def test_ragged_small_4k_plus_7x256_all_heads():
     case = synth.workload("ragged_small_q4_0", seed=1301, device=DEV)
     out, _ = _run_auto(case)
-    sampled_parity(case, out, [(b, g) for b in range(8) for g in range(4)])
+    sampled_parity(case, out, all_groups(case))
     _free()
 
 
@@ -89,6 +89,6 @@ def test_slab_past_2pow32_elements_gather_and_decode():
             assert not torch.equal(dst[hi], wrapped)
             del dst, ref, wrapped
     out, _ = _run_auto(case)
-    sampled_parity(case, out, [(0, 0), (3, 7), (7, 4)])
+    sampled_parity(case, out, all_groups(case))
     del case, out
     _free()

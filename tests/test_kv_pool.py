@@ -116,8 +116,8 @@ def test_model_based_fuzz():
 
 
 def test_fork_shares_the_prefix_and_counts_references():
-    """lucebox PR #555, Roadmap item 6: shared prefix blocks with reference
-    counting."""
+    """lucebox PR #555, Roadmap item 6: prefix blocks shared under reference
+    counts."""
     p = pa.KvPool(8)
     h, ids = p.alloc(3)
     f = p.fork(h, 2)

@@ -11,7 +11,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_attn.h")
-LIB = os.path.join(ROOT, "paged_kv_gqa_attn_amd", "libpaged_attn.so")
+LIB = os.environ.get("PAGED_ATTN_LIB") or os.path.join(ROOT, "paged_kv_gqa_attn_amd", "libpaged_attn.so")
 
 
 def _ensure_built():

@@ -1,5 +1,5 @@
 """Pins of oracle.chunk (multi-token queries with causal masking inside the
-chunk: llama.cpp PR #13 HRX, Roadmap item 3; TensorFold PR #1418, What)
+chunk: lucebox PR #555, Roadmap item 3; TensorFold PR #1418, What)
 against things other than its own formula: the pure-Python brute-force
 decode of test_oracle.py run on the sequence cut at each chunk token's
 position, the reduction to a decode step at Tq = 1, and planted mistakes

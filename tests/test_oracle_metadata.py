@@ -1,7 +1,7 @@
 """Pins of the paging-metadata definitions in oracle/metadata.py against
 hand-worked cases (lucebox PR #555, Summary: resident block table updated
-entry by entry; Roadmap item 6: shared prefix blocks with reference counting
-and copy-on-write)."""
+entry by entry; Roadmap item 6: prefix blocks shared under reference counts
+and copied on write)."""
 import numpy as np
 import pytest
 
