@@ -233,6 +233,28 @@ int32_t paged_attn_step(const pa_plan* plan, const float* q, const void* k_pool,
                         void* stream);
 
 /*
+ * paged_attn_step_noalloc - paged_attn_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same decode + merge kernels, with the workspace
+ * in a static device array of 64 MiB per GPU that the library holds from its
+ * load until the process ends, instead of a caller-provided ws. The caller
+ * still passes q, the pools, the table, seq_len and out, laid out as for
+ * paged_attn_step; the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and enqueues nothing but the kernels.
+ *   Returns PA_ERR_INVALID when plan->ws_bytes exceeds the 64 MiB scratch,
+ *   PA_ERR_HIP when the scratch's device address cannot be obtained, else as
+ *   paged_attn_step.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ *   GPU (other streams, other host threads) race and must be serialised by the
+ *   caller. The scratch's status word is not readable: a corrupt block table
+ *   shows only as NaN rows of the sequence concerned, and a clamped seq_len
+ *   not at all (use paged_attn_step with a workspace to read the status).
+ */
+int32_t paged_attn_step_noalloc(const pa_plan* plan, const float* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* seq_len, float* out, void* stream);
+
+/*
  * paged_kv_gather - copy raw encoded rows out of a pool through the table,
  * with the same 64-bit address computation the decode kernel uses (the
  * mlxcel issue #2153 page, Scope: the gather path).

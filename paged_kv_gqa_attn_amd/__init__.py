@@ -27,7 +27,7 @@ TYPES = {"f16": PA_F16, "q8_0": PA_Q8_0, "q4_0": PA_Q4_0}
 
 __all__ = ["PaShape", "PaPlan", "PaError", "lib", "pa_row_bytes", "pa_last_error",
            "paged_attn_plan", "paged_attn_decode", "paged_attn_merge", "paged_attn_step",
-           "paged_kv_gather", "paged_attn_status", "KvPool", "workspace", "shape_of"]
+           "paged_attn_step_noalloc", "paged_kv_gather", "paged_attn_status", "KvPool", "workspace", "shape_of"]
 
 
 class PaShape(ctypes.Structure):
@@ -90,6 +90,7 @@ def _load():
         "paged_attn_decode": (i32, [P(PaPlan), vp, vp, vp, vp, vp, vp, u64, vp, vp]),
         "paged_attn_merge": (i32, [P(PaPlan), vp, u64, vp, vp, vp]),
         "paged_attn_step": (i32, [P(PaPlan), vp, vp, vp, vp, vp, vp, u64, vp, vp]),
+        "paged_attn_step_noalloc": (i32, [P(PaPlan), vp, vp, vp, vp, vp, vp, vp]),
         "paged_kv_gather": (i32, [P(PaPlan), vp, i32, vp, i32, i32, i32, vp, vp, vp]),
         "paged_attn_status": (i32, [vp, vp, P(u32)]),
         "kv_pool_create": (i32, [i32, P(vp)]),
@@ -186,6 +187,14 @@ def paged_attn_step(plan: PaPlan, q, k_pool, v_pool, block_table, seq_len, ws, o
     _check(lib.paged_attn_step(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                _ptr(block_table), _ptr(seq_len), _ptr(ws), nb, _ptr(out),
                                _stream(stream)))
+
+
+def paged_attn_step_noalloc(plan: PaPlan, q, k_pool, v_pool, block_table, seq_len, out,
+                            stream=None) -> None:
+    """paged_attn_step with the library's static per-GPU scratch as workspace
+    (no allocation; calls overlapping on one GPU race)."""
+    _check(lib.paged_attn_step_noalloc(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_table), _ptr(seq_len), _ptr(out), _stream(stream)))
 
 
 def paged_kv_gather(plan: PaPlan, pool, which: int, block_table, b: int, t0: int, n: int, dst,

@@ -279,6 +279,23 @@ extern "C" int32_t paged_attn_step(const pa_plan* plan, const float* q, const vo
   return paged_attn_merge(plan, ws, ws_bytes, seq_len, out, stream);
 }
 
+extern "C" int32_t paged_attn_step_noalloc(const pa_plan* plan, const float* q, const void* k_pool,
+                                           const void* v_pool, const int32_t* block_table,
+                                           const int32_t* seq_len, float* out, void* stream) {
+  const char* who = "paged_attn_step_noalloc";
+  int32_t rc = check_plan(plan, who);
+  if (rc) return rc;
+  if (plan->ws_bytes > kNoAllocScratchBytes)
+    return fail(PA_ERR_INVALID, "%s: the plan needs %llu bytes of workspace, the static scratch holds %llu",
+                who, (unsigned long long)plan->ws_bytes, (unsigned long long)kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: no address for the static scratch: %s", who, hipGetErrorString(e));
+  return paged_attn_step(plan, q, k_pool, v_pool, block_table, seq_len, scratch, kNoAllocScratchBytes, out,
+                         stream);
+}
+
 extern "C" int32_t paged_kv_gather(const pa_plan* plan, const void* pool, int32_t which,
                                    const int32_t* block_table, int32_t b, int32_t t0, int32_t n,
                                    void* dst, void* ws, void* stream) {

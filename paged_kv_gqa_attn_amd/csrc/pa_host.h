@@ -154,6 +154,12 @@ struct MergeArgs {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
+// Workspace of paged_attn_step_noalloc: a file-scope device array of this
+// many bytes per GPU (step_noalloc.hip). noalloc_scratch returns its device
+// address on the current device (looked up once per device).
+constexpr uint64_t kNoAllocScratchBytes = 64ull << 20;
+hipError_t noalloc_scratch(void** addr);
+
 struct GatherArgs {
   const uint8_t* pool;
   const int32_t* table;    // nullptr = contiguous layout

@@ -19,6 +19,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs&, hipStream_t) { return hipEr
 hipError_t launch_table_update(const TableUpdateArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_gather(const GatherArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
+hipError_t noalloc_scratch(void**) { return hipErrorNoBinaryForGpu; }
 
 }  // namespace pa
 

@@ -43,7 +43,8 @@ def test_header_declares_the_expected_entry_points():
                  "paged_kv_gather", "paged_attn_status", "kv_pool_alloc", "kv_pool_release",
                  "kv_pool_create", "kv_pool_destroy", "kv_pool_reset", "pa_last_error",
                  "kv_pool_fork", "kv_pool_cow", "kv_pool_refcount", "paged_table_update",
-                 "paged_kv_copy_blocks", "paged_attn_chunk_plan", "paged_attn_chunk"]:
+                 "paged_kv_copy_blocks", "paged_attn_chunk_plan", "paged_attn_chunk",
+                 "paged_attn_step_noalloc"]:
         assert must in names, must
 
 
@@ -211,6 +212,18 @@ def test_decode_argument_checks_before_any_launch():
         pa.paged_kv_gather(plan, fake, 0, fake, 8, 0, 1, fake, stream=0)
     with pytest.raises(pa.PaError):
         pa.paged_kv_gather(plan, fake, 0, fake, 0, 8192 * 16, 1, fake, stream=0)
+
+
+def test_noalloc_step_refuses_plans_beyond_its_scratch_before_any_launch():
+    """paged_attn_step_noalloc checks the plan's workspace against its 64 MiB
+    static scratch before it touches the device."""
+    plan = pa.paged_attn_plan(_shape(B=1024, Hq=64, nblocks=600000), 131072, num_cus=256,
+                              partition_tokens=256)
+    assert plan.ws_bytes > 64 << 20
+    fake = 0x1000
+    rc = pa.lib.paged_attn_step_noalloc(ctypes.byref(plan), fake, fake, fake, fake, fake, fake, 0)
+    assert rc == pa.PA_ERR_INVALID
+    assert "paged_attn_step_noalloc" in pa.pa_last_error() and "static scratch" in pa.pa_last_error()
 
 
 def test_direct_plan_merge_is_a_no_op():
