@@ -201,6 +201,8 @@ def run_bench(args):
                         c0.k_fmt, c0.v_fmt)
     plan = pa.paged_attn_plan(shape, max(c0.seq_lens), total_tokens=sum(c0.seq_lens),
                               force_partitions=args.force_partitions)
+    if args.single_launch:
+        plan.fused = 1
     ws = pa.workspace(plan, dev)
     out = torch.empty((c0.B, c0.Hq, c0.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -261,7 +263,10 @@ def run_bench(args):
     ms_per_step = wall * 1e3 / args.steps
     value = (dec_bytes + mrg_bytes) / (ms_per_step * 1e-3) / 1e9
     dec_avg = sum(dec_ms) / len(dec_ms)
-    achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
+    # a single-launch plan's decode kernel also reads the partials back and
+    # writes out: all of the step's bytes are that one kernel's
+    kern_bytes = dec_bytes + mrg_bytes if plan.fused else dec_bytes
+    achieved = kern_bytes / (dec_avg * 1e-3) / 1e9
     med = sorted(step_ms)[len(step_ms) // 2]
     line = {
         "metric": METRIC,
@@ -284,6 +289,7 @@ def run_bench(args):
             "k_type": c0.k_fmt, "v_type": c0.v_fmt, "seq_lens": sorted(set(c0.seq_lens)),
             "live_tokens": sum(c0.seq_lens), "psize": plan.psize, "p_max": plan.p_max,
             "grid": plan.grid, "decode_kernel": DECODE_KERNELS[plan.path - 1],
+            "single_launch_merge": bool(plan.fused),
             "pool_copies": len(cases),
             "step_us_events": round(step_us_events, 2),
             "split_pass_step_us_median": round(med * 1e3, 2),
@@ -596,6 +602,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1000)
     ap.add_argument("--force-partitions", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="decode and merge in one launch (plan.fused = 1; the planner's default is two)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)

@@ -85,10 +85,15 @@ enum {
 enum {
   PA_STATUS_BAD_BLOCK_ID = 1, /* a live table entry was < 0 or >= nblocks; that
                                  sequence's output rows are NaN */
-  PA_STATUS_BAD_SEQ_LEN = 2   /* seq_len[b] < 0 or longer than the plan admits
+  PA_STATUS_BAD_SEQ_LEN = 2,  /* seq_len[b] < 0 or longer than the plan admits
                                  (min(max_blocks*block_size, p_max*psize), at
                                  least plan->max_seq_len); it was clamped into
                                  range */
+  PA_STATUS_MERGE_WAIT = 4    /* single-launch merge: a merge slice found its
+                                 completion counter past the partition count
+                                 (counters not zero at the call) or waited
+                                 longer than one second; its 64 columns are
+                                 NaN */
 };
 
 typedef struct pa_shape {
@@ -119,10 +124,24 @@ typedef struct pa_plan {
                            B <= 256, no F16 side at D=256 and 16-byte aligned
                            pools, else path 1 runs), 1 = register-streaming.
                            paged_attn_plan picks 2 where the shape allows it; a
-                           caller may set 1 to force the register kernel. The
-                           two kernels differ only in the order of fp32
-                           accumulation. */
+                           caller may set 1 to force the register kernel (and
+                           must then set fused = 0). The two kernels differ
+                           only in the order of fp32 accumulation. */
+  int32_t fused;        /* 1: single launch - the LDS-staged decode kernel also
+                           merges the partials (its last workgroups to finish
+                           take the merge slices once their partitions are in,
+                           counted by atomic completion counters in ws:
+                           llama.cpp PR #13 HRX, Changes: the reduction inside
+                           the same self-synchronising launch; lucebox PR #555,
+                           Roadmap item 4) and paged_attn_merge is a no-op.
+                           Allowed on path 2 when not direct and the merge is
+                           of the wide layout (not the row-per-thread one).
+                           paged_attn_plan leaves it 0: on MI355X the separate
+                           merge launch measured faster at every shape tried.
+                           Both give the same bits. */
+  int32_t reserved;     /* 0 */
   uint64_t ws_bytes;    /* workspace bytes paged_attn_decode/merge need */
+  uint64_t part_offset; /* byte offset of the partials in ws (see layout) */
 } pa_plan;
 
 /* Bytes of one encoded row of D values of `type`, or a negative PA_ERR_*. */
@@ -161,14 +180,26 @@ int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t tota
  * Workspace layout (ws, plan->ws_bytes bytes, device memory, 256-byte aligned):
  *   [0, 4)      uint32 status word (PA_STATUS_* bits); must be zero before the
  *               first decode; paged_attn_status reads and clears it
- *   [4, 256)    reserved
- *   partials    only when plan->direct == 0, at offset 256:
+ *   [4, 12)     uint32 item counter and leave counter of the single-launch
+ *               merge (plan->fused)
+ *   [12, 256)   reserved
+ *   [256, part_offset)
+ *               uint32 done[B*ceil(Hkv/4)], one every 1040 words (4160 bytes):
+ *               partitions finished per (sequence, kv-head quad), for the
+ *               single-launch merge
+ *               The counters [4, 12) and done[] must be zero before the first
+ *               fused decode (the workspace is zero-filled once); every fused
+ *               decode leaves them zero (its last workgroup resets them), and
+ *               no other call writes them. Calls that share one workspace must
+ *               not overlap in time.
+ *   partials    only when plan->direct == 0, at offset plan->part_offset
+ *               (256 + 4160*B*ceil(Hkv/4) rounded up to 256):
  *               uint16 o[B][Hq][p_max][D]  normalised output of each partition
  *                                          as IEEE binary16, rounded to nearest
  *                                          even (lucebox PR #555, Summary:
  *                                          normalised f16 partials; |o| never
  *                                          exceeds the largest |V| value)
- *               float ml[B][Hq][p_max][2]  at offset 256 + 2*B*Hq*p_max*D:
+ *               float ml[B][Hq][p_max][2]  at offset part_offset + 2*B*Hq*p_max*D:
  *                                          (m, l): m is a reference value of
  *                                          the base-2 logits x = log2(e)*scale*q.k
  *                                          of the partition with
@@ -316,8 +347,11 @@ typedef struct pa_chunk_plan {
   int32_t num_cus;
   int32_t direct;       /* 1: one partition, no merge */
   int32_t path;         /* 1: tile-conversion kernel, 2: window kernel */
-  uint64_t ws_bytes;    /* workspace: status word + partials
-                           (256 + B*Tq*Hq*p_max*(2D+8) bytes when direct == 0) */
+  uint64_t ws_bytes;    /* workspace: header + partials (part_offset +
+                           B*Tq*Hq*p_max*(2D+8) bytes when direct == 0) */
+  uint64_t part_offset; /* byte offset of the partials in ws: the decode
+                           layout's (the header and done[] counters are left
+                           alone, so one workspace may serve both) */
 } pa_chunk_plan;
 
 /* Plan a chunk launch; arguments as for paged_attn_plan plus tq (the number

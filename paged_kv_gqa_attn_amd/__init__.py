@@ -22,7 +22,7 @@ LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(_HERE, "libpaged_att
 PA_F16, PA_Q8_0, PA_Q4_0 = 0, 1, 2
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_CAPACITY, PA_ERR_STALE_HANDLE, PA_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
-PA_STATUS_BAD_BLOCK_ID, PA_STATUS_BAD_SEQ_LEN = 1, 2
+PA_STATUS_BAD_BLOCK_ID, PA_STATUS_BAD_SEQ_LEN, PA_STATUS_MERGE_WAIT = 1, 2, 4
 TYPES = {"f16": PA_F16, "q8_0": PA_Q8_0, "q4_0": PA_Q4_0}
 
 __all__ = ["PaShape", "PaPlan", "PaError", "lib", "pa_row_bytes", "pa_last_error",
@@ -42,13 +42,15 @@ class PaPlan(ctypes.Structure):
                 ("p_max", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("direct", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("ws_bytes", ctypes.c_uint64)]
+                ("fused", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ws_bytes", ctypes.c_uint64), ("part_offset", ctypes.c_uint64)]
 
     def __repr__(self):
         s = self.shape
         return (f"PaPlan(B={s.B}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D}, bs={s.block_size}, "
                 f"psize={self.psize}, p_max={self.p_max}, grid={self.grid}, "
-                f"direct={self.direct}, path={self.path}, ws_bytes={self.ws_bytes})")
+                f"direct={self.direct}, path={self.path}, fused={self.fused}, "
+                f"ws_bytes={self.ws_bytes}, part_offset={self.part_offset})")
 
 
 class PaChunkPlan(ctypes.Structure):
@@ -56,7 +58,8 @@ class PaChunkPlan(ctypes.Structure):
                 ("psize", ctypes.c_int32), ("p_max", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("direct", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64)]
+                ("path", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64),
+                ("part_offset", ctypes.c_uint64)]
 
     def __repr__(self):
         s = self.shape

@@ -68,20 +68,31 @@ bool lds_path_ok(const pa_shape& s) {
   return s.Hkv % 4 == 0 && s.B <= kLdsMaxB && lds_groups(s.k_type, s.v_type, s.D) > 0;
 }
 
+// The single-launch merge runs the wide merge layout's slices; where the
+// separate merge would take the row-per-thread layout, the step stays two
+// launches (so that both paths give the same bits).
+bool fused_merge_ok(const pa_shape& s, int p_max) {
+  return !merge_rows_layout(int64_t(s.B) * s.Hq, p_max) && s.D % kMergeColsHost == 0;
+}
+
 int32_t check_plan(const pa_plan* p, const char* who) {
   if (!p) return fail(PA_ERR_INVALID, "%s: null plan", who);
   int32_t rc = check_shape(&p->shape, who);
   if (rc) return rc;
   if (p->psize < kTileTokens || p->psize % kTileTokens || p->p_max < 1 || p->grid < 1 ||
-      !(p->scale == p->scale) || p->direct != (p->p_max == 1) || (p->path != 1 && p->path != 2))
+      !(p->scale == p->scale) || p->direct != (p->p_max == 1) || (p->path != 1 && p->path != 2) ||
+      (p->fused != 0 && p->fused != 1) || p->part_offset != ws_part_offset(p->shape.B, p->shape.Hkv))
     return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_plan", who);
   if (p->path == 2 && !lds_path_ok(p->shape))
     return fail(PA_ERR_UNSUPPORTED, "%s: plan path 2 (LDS-staged kernel) does not take this shape", who);
+  if (p->fused && (p->path != 2 || p->direct || !fused_merge_ok(p->shape, p->p_max)))
+    return fail(PA_ERR_INVALID, "%s: a fused plan needs path 2, partitions and the wide merge layout "
+                "(set fused = 0 for two launches)", who);
   return PA_OK;
 }
 
 uint64_t ws_bytes_for(const pa_shape& s, int p_max, bool direct) {
-  uint64_t bytes = 256;
+  uint64_t bytes = ws_part_offset(s.B, s.Hkv);
   if (!direct) bytes += uint64_t(s.B) * s.Hq * p_max * (2u * uint64_t(s.D) + 8u);
   return (bytes + 255) & ~uint64_t(255);
 }
@@ -185,6 +196,11 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
   int64_t bp_upper = int64_t(s.B) * p_max;
   if (total_tokens > 0) bp_upper = std::min(bp_upper, ceil_div(total_tokens, psize) + s.B);
   const int64_t units = std::max<int64_t>(1, bp_upper * per_bp);
+  // The single launch (fused) is left to the caller: on MI355X the separate
+  // merge launch measured faster at every shape tried (the in-launch merge
+  // runs at two workgroups per CU and behind its waits, where the merge
+  // kernel spreads every slice over the whole GPU at once).
+  const bool fused = false;
   const int64_t grid = std::min<int64_t>(units, int64_t(num_cus) * (lds ? 2 : 8));
 
   std::memset(plan, 0, sizeof *plan);
@@ -197,7 +213,9 @@ extern "C" int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, i
   plan->num_cus = num_cus;
   plan->direct = direct ? 1 : 0;
   plan->path = lds ? 2 : 1;
+  plan->fused = fused ? 1 : 0;
   plan->ws_bytes = ws_bytes_for(s, int(p_max), direct);
+  plan->part_offset = ws_part_offset(s.B, s.Hkv);
   clear_error();
   return PA_OK;
 }
@@ -211,7 +229,8 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   if (rc) return rc;
   if (!q || !k_pool || !v_pool || !seq_len || !ws)
     return fail(PA_ERR_INVALID, "%s: null q, k_pool, v_pool, seq_len or ws", who);
-  if (plan->direct && !out) return fail(PA_ERR_INVALID, "%s: direct mode needs out", who);
+  if ((plan->direct || plan->fused) && !out)
+    return fail(PA_ERR_INVALID, "%s: direct mode and fused plans need out", who);
   if (ws_bytes < plan->ws_bytes)
     return fail(PA_ERR_INVALID, "%s: workspace of %llu bytes, plan needs %llu", who,
                 (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
@@ -224,7 +243,10 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   a.seq_len = seq_len;
   a.out = out;
   a.status = static_cast<uint32_t*>(ws);
-  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+  a.work = static_cast<uint32_t*>(ws) + 1;
+  a.leave = static_cast<uint32_t*>(ws) + 2;
+  a.done = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
+  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + plan->part_offset);
   a.part_ml = reinterpret_cast<float*>(a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D);
   a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.r = s.Hq / s.Hkv;
   a.nblocks = s.nblocks; a.max_blocks = s.max_blocks; a.block_size = s.block_size;
@@ -235,11 +257,30 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   a.k_type = s.k_type; a.v_type = s.v_type;
   a.direct = plan->direct;
   a.qscale = float(double(plan->scale) * 1.4426950408889634);   // scale * log2(e)
+  a.merge_items = s.B * s.Hq * (s.D / kMergeColsHost);
+  a.wait_ticks = 100000000ull;                                   // one second of the 100 MHz clock
   // the LDS-staged kernel's DMA chunks are 16-byte aligned only on aligned pools
   const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) == 0;
-  hipError_t e = plan->path == 2 && aligned ? launch_decode_lds(a, static_cast<hipStream_t>(stream))
-                                            : launch_decode_regs(a, static_cast<hipStream_t>(stream));
+  const bool lds = plan->path == 2 && aligned;
+  a.fused = plan->fused && lds ? 1 : 0;
+  // a single launch also runs the merge slices: more workgroups, up to the
+  // two per CU the units use at most
+  if (a.fused) a.grid = int32_t(std::min<int64_t>(int64_t(plan->grid) + a.merge_items, 2ll * plan->num_cus));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = lds ? launch_decode_lds(a, st) : launch_decode_regs(a, st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  if (plan->fused && !lds) {
+    // a fused plan whose pools sent it to the register kernel: merge separately
+    MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
+    m.seq_len = seq_len;
+    m.out = out;
+    m.B = s.B; m.Hq = s.Hq; m.D = s.D; m.psize = plan->psize; m.p_max = plan->p_max;
+    m.cap_tokens = a.cap_tokens;
+    e = launch_merge(m, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: merge launch failed: %s", who, hipGetErrorString(e));
+  }
   clear_error();
   return PA_OK;
 }
@@ -249,14 +290,14 @@ extern "C" int32_t paged_attn_merge(const pa_plan* plan, const void* ws, uint64_
   const char* who = "paged_attn_merge";
   int32_t rc = check_plan(plan, who);
   if (rc) return rc;
-  if (plan->direct) { clear_error(); return PA_OK; }
+  if (plan->direct || plan->fused) { clear_error(); return PA_OK; }   // done by the decode
   if (!ws || !seq_len || !out) return fail(PA_ERR_INVALID, "%s: null ws, seq_len or out", who);
   if (ws_bytes < plan->ws_bytes)
     return fail(PA_ERR_INVALID, "%s: workspace of %llu bytes, plan needs %llu", who,
                 (unsigned long long)ws_bytes, (unsigned long long)plan->ws_bytes);
   const pa_shape& s = plan->shape;
   MergeArgs a{};
-  a.part_o = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(ws) + 256);
+  a.part_o = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(ws) + plan->part_offset);
   a.part_ml = reinterpret_cast<const float*>(a.part_o + uint64_t(s.B) * s.Hq * plan->p_max * s.D);
   a.seq_len = seq_len;
   a.out = out;
@@ -412,7 +453,7 @@ extern "C" int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_
 
 namespace {
 uint64_t chunk_ws_bytes(const pa_shape& s, int tq, int p_max, bool direct) {
-  uint64_t bytes = 256;
+  uint64_t bytes = ws_part_offset(s.B, s.Hkv);
   if (!direct) bytes += uint64_t(s.B) * uint64_t(tq) * s.Hq * p_max * (2u * uint64_t(s.D) + 8u);
   return (bytes + 255) & ~uint64_t(255);
 }
@@ -423,7 +464,7 @@ int32_t check_chunk_plan(const pa_chunk_plan* p, const char* who) {
   if (rc) return rc;
   if (p->tq < 1 || p->tq > kMaxChunk || p->psize < kTileTokens || p->psize % kTileTokens ||
       p->p_max < 1 || p->grid < 1 || !(p->scale == p->scale) || p->direct != (p->p_max == 1) ||
-      (p->path != 1 && p->path != 2))
+      (p->path != 1 && p->path != 2) || p->part_offset != ws_part_offset(p->shape.B, p->shape.Hkv))
     return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_chunk_plan", who);
   const pa_shape& s = p->shape;
   if (p->path == 2 && !chunk_window_ok(int64_t(p->tq) * (s.Hq / s.Hkv), s.Hkv, s.k_type, s.v_type, s.D))
@@ -521,6 +562,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   plan->direct = direct ? 1 : 0;
   plan->path = window ? 2 : 1;
   plan->ws_bytes = ws;
+  plan->part_offset = ws_part_offset(s.B, s.Hkv);
   clear_error();
   return PA_OK;
 }
@@ -546,7 +588,7 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.seq_len = seq_len;
   a.out = out;
   a.status = static_cast<uint32_t*>(ws);
-  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+  a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + plan->part_offset);
   a.part_ml = reinterpret_cast<float*>(a.part_o + rows * plan->p_max * s.D);
   a.B = s.B; a.Tq = plan->tq; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.r = s.Hq / s.Hkv;
   a.nblocks = s.nblocks; a.max_blocks = s.max_blocks;

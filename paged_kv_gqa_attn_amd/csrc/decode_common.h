@@ -270,6 +270,24 @@ __device__ __forceinline__ void store_f16_pair(f16* row, int d, float x0, float 
   *reinterpret_cast<f16x2*>(row + d) = f16x2{f16(x0), f16(x1)};
 }
 
+// The same pair, and one fp32 value, stored device-coherently (sc1: written
+// through past this XCD's L2), for partials that workgroups of the same launch
+// read back (the single-launch merge); the stored bits are the same.
+__device__ __forceinline__ void store_f16_pair_dev(f16* row, int d, float x0, float x1) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(row + d), bitcast<uint32_t>(f16x2{f16(x0), f16(x1)}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes, device-coherent (global_store_dwordx4 sc1; the caller waits for
+// it with s_waitcnt vmcnt(0) where the order matters: the compiler does not
+// count this store).
+__device__ __forceinline__ void store_u32x4_dev(void* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_f32_dev(float* p, float x) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), bitcast<uint32_t>(x), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int VT, int D> struct VFmt;
 
 template <int D> struct VFmt<kF16, D> {

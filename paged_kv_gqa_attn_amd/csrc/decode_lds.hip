@@ -30,11 +30,26 @@
 //     MFMAs for 32-token steps, 16x16x16 for the PV of 16-token steps.
 //   * No cross-wave combine: a wave owns all tokens of its head group, so it
 //     writes its partial (or output) rows directly.
+//   * Single launch (plan->fused): the merge runs in the same launch (the
+//     llama.cpp PR #13 HRX page, Changes: the reduction inside the same
+//     self-synchronising launch with an atomic completion counter, no second
+//     dispatch). Workgroups claim items from a counter in the workspace:
+//     every decode unit; a workgroup whose claim comes after the last unit
+//     turns to its share of the merge slices (a query-head row and 64 output
+//     columns, the separate merge's workgroup, same code). A unit stores its
+//     partial device-coherently and adds one to its (sequence, head quad)'s
+//     done counter; a slice waits for its counter to reach the sequence's
+//     partition count. Merging starts only after every unit has been claimed,
+//     and a workgroup holding a claimed unit never waits, so every wait ends
+//     (each wait is also bounded by one second of the constant clock). The
+//     last workgroup to leave zeroes the counters for the next launch. Which
+//     workgroup computes a unit does not change its bits.
 #include <algorithm>
 #include <type_traits>
 
 #include "decode_common.h"
 #include "lds_ring.h"
+#include "merge_common.h"
 
 namespace pa {
 namespace {
@@ -42,6 +57,28 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kNidS = 512;     // block ids staged per segment of a partition
 constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
+static_assert(kThreads == kMergeThreads && kMergeCols == kMergeColsHost, "merge slices run on this workgroup");
+
+// Single-launch merge: one claim from the item counter (relaxed: the claim
+// itself orders nothing).
+__device__ __forceinline__ uint32_t claim_item(uint32_t* work) {
+  return __hip_atomic_fetch_add(work, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits (one thread) until *cnt equals `target`, for at most `ticks` of the
+// 100 MHz constant clock. 1 when reached; 0 on time-out or when the count has
+// passed the target (the counters were not zero at the launch).
+__device__ __forceinline__ int wait_count(const uint32_t* cnt, uint32_t target, uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    const uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v == target) return 1;
+    if (v > target || wall_clock64() - t0 > ticks) return 0;
+    // every poll is a device-coherent load of one memory line, so hundreds
+    // of waiting workgroups would load the one memory channel that holds it
+    // and slow the K/V stream of the units still running: poll sparsely
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
 
 template <int KT, int VT, int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArgs a) {
@@ -62,6 +99,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   int32_t* unit_start = reinterpret_cast<int32_t*>(smem + a.ring_bytes);
   int32_t* lens = unit_start + (a.B + 1);
   int32_t* ids = unit_start + (((2 * a.B + 1) + 3) & ~3);
+  int32_t* bcast = ids + ((kNidS + 1 + 3) & ~3);      // single launch: claimed items, flags
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -69,6 +107,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   const int m = lane & 15;
   const int j = lane >> 4;
 
+  // single launch: the first claim is in flight while the prefix reads seq_len
+  uint32_t first = 0;
+  if (a.fused && tid == 0) first = claim_item(a.work);
   live_partition_prefix<kThreads>(a, lens, unit_start, reinterpret_cast<int*>(ring));
   const int n_bp = __builtin_amdgcn_readfirstlane(unit_start[a.B]);
   const int HG = a.Hkv / 4;
@@ -100,7 +141,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   const uint32_t mg = opaque_vgpr(kMagic);
   const int seg_tokens = kNidS << a.bs_shift;
 
-  for (int u = logical; u < n_units; u += Gd) {
+  int u = logical;
+  if (a.fused) {
+    if (tid == 0) bcast[0] = int(first);
+    __syncthreads();
+    u = __builtin_amdgcn_readfirstlane(bcast[0]);
+  }
+  while (u < n_units) {
     // ---- locate the unit -----------------------------------------------------
     const int bp = u / HG;
     const int hg = u - bp * HG;
@@ -451,8 +498,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     }
 
     // ---- partial (or final) rows of the wave's r heads --------------------
+    // Partials go out as whole rows: every wave stages its r rows (binary16)
+    // in the idle ring and copies them with 16-byte stores, so each 512-byte
+    // (D = 256) row reaches memory as whole lines. The stores are
+    // device-coherent (written through past this XCD's L2) so that a single
+    // launch can merge them in the same launch; as whole lines they cost no
+    // more than write-back stores.
     const int n = m;
     if (bad && tid == 0) atomicOr(a.status, 1u);
+    unsigned char* const stage = ring + wave * (a.r * 2 * D);   // this wave's rows
+    if (!a.direct) __syncthreads();      // every wave is done reading the ring
     if (n < a.r) {
       const int h = g * a.r + n;
       const float inv = bad ? __builtin_nanf("") : 1.0f / l_run;
@@ -464,30 +519,109 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
           for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = acc[e][i] * inv;
       } else {
         const int64_t row = (int64_t(b) * a.Hq + h) * a.p_max + p;
-        f16* dst = reinterpret_cast<f16*>(a.part_o) + row * D;
         if (j == 0) {
-          a.part_ml[2 * row] = bad ? __builtin_nanf("") : m_run;
-          a.part_ml[2 * row + 1] = l_run;
+          store_f32_dev(a.part_ml + 2 * row, bad ? __builtin_nanf("") : m_run);
+          store_f32_dev(a.part_ml + 2 * row + 1, l_run);
         }
+        f16* srow = reinterpret_cast<f16*>(stage) + n * D;
 #pragma unroll
         for (int e = 0; e < E; e += 2)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            store_f16_pair(dst, VF::dv(4 * j + i, e), acc[e][i] * inv, acc[e + 1][i] * inv);
+            store_f16_pair(srow, VF::dv(4 * j + i, e), acc[e][i] * inv, acc[e + 1][i] * inv);
       }
+    }
+    if (!a.direct) {
+      __syncthreads();                   // the staged rows are complete
+      constexpr int kRowChunks = D / 8;  // 16-byte chunks of a binary16 row
+      const int64_t row0 = (int64_t(b) * a.Hq + g * a.r) * a.p_max + p;
+      for (int c = lane; c < a.r * kRowChunks; c += 64) {
+        const int n2 = c / kRowChunks, w = c - n2 * kRowChunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + n2 * (2 * D) + 16 * w);
+        store_u32x4_dev(reinterpret_cast<uint8_t*>(a.part_o) + ((row0 + int64_t(n2) * a.p_max) * D) * 2 + 16 * w, v);
+      }
+    }
+    if (!a.fused) {
+      u += Gd;
+      continue;
+    }
+    // single launch: publish the partial - every thread waits until its
+    // device-coherent stores are performed, then one increment of the unit's
+    // done counter (no cache write-back needed: nothing of the partial sits
+    // in L2 only) - and claim the next item
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // (also the 16-byte asm stores)
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_fetch_add(a.done + (b * HG + hg) * kDoneStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      bcast[0] = int(claim_item(a.work));
+    }
+    __syncthreads();
+    u = __builtin_amdgcn_readfirstlane(bcast[0]);
+  }
+  if (!a.fused) return;
+
+  // ---- single launch: merge slices, then leave ----------------------------
+  // Slice i is query-head row bh = i / (D/64) and output columns
+  // 64 * (i % (D/64)) ..; it waits for every partition of the row's
+  // (sequence, head quad) and then runs the separate merge's code on them.
+  // Slices are dealt by workgroup index (slice blockIdx.x + k * grid): this
+  // workgroup got here because its claim came after the last unit, so every
+  // unit is already held by a running workgroup that does not wait.
+  MergeLds& mlds = *reinterpret_cast<MergeLds*>(ring);   // the ring is idle now
+  const int chunks = D / kMergeCols;
+  u = n_units + blockIdx.x;
+  while (u < n_units + a.merge_items) {
+    const int next = u + Gd;
+    const int item = u - n_units;
+    const int bh = item / chunks;
+    const int col0 = (item - bh * chunks) * kMergeCols;
+    const int b = bh / a.Hq;
+    const int hg = (bh - b * a.Hq) / a.r / 4;
+    const int P = (lens[b] + a.psize - 1) / a.psize;
+    if (tid == 0) bcast[1] = wait_count(a.done + (b * HG + hg) * kDoneStride, uint32_t(P), a.wait_ticks);
+    __syncthreads();
+    const int ok = bcast[1];
+    u = next;
+    float* dst = a.out + int64_t(bh) * D + col0;
+    if (ok) {
+      // (device-coherent loads: the partials come from this launch)
+      merge_slice<true>(reinterpret_cast<const f16*>(a.part_o) + int64_t(bh) * a.p_max * D,
+                  a.part_ml + int64_t(bh) * a.p_max * 2, P, D, col0, dst, mlds);
+    } else {
+      if (tid < kMergeCols) dst[tid] = __builtin_nanf("");
+      if (tid == 0) atomicOr(a.status, 4u);
+    }
+    __syncthreads();                      // bcast and the slice's LDS are free again
+  }
+  // every workgroup counts itself out; the last one zeroes the counters (all
+  // others have made their last claim and increment by then)
+  if (tid == 0) {
+    const uint32_t n = __hip_atomic_fetch_add(a.leave, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    bcast[2] = n == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (bcast[2]) {
+    for (int i = tid; i < a.B * HG; i += kThreads)
+      __hip_atomic_store(a.done + i * kDoneStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(a.work, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.leave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
 // LDS bytes of a launch: the ring, then unit_start[B+1] | lens[B] | pad |
-// ids[kNidS+1] (a segment of kNidS blocks' worth of tokens that starts
-// inside a block touches kNidS+1 blocks).
+// ids[kNidS+1] | bcast[4] (a segment of kNidS blocks' worth of tokens that
+// starts inside a block touches kNidS+1 blocks).
 template <int KT, int VT, int D>
 size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
   using LY = LdsLayout<KT, VT, D>;
+  static_assert(size_t(LY::R) * LY::SLOT >= sizeof(MergeLds), "merge slices reuse the ring");
+  static_assert(size_t(LY::R) * LY::SLOT >= 4 * 16 * 2 * D, "four waves stage up to 16 binary16 rows each");
   const size_t ring = size_t(LY::R) * LY::SLOT;
   *ring_bytes = int((ring + 15) & ~size_t(15));
-  return size_t(*ring_bytes) + 4 * size_t(((2 * a.B + 1) + 3) & ~3) + 4 * size_t((kNidS + 1 + 3) & ~3);
+  return size_t(*ring_bytes) + 4 * size_t(((2 * a.B + 1) + 3) & ~3) + 4 * size_t((kNidS + 1 + 3) & ~3) + 16;
 }
 
 template <int KT, int VT, int D>

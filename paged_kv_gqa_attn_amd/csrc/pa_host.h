@@ -32,7 +32,28 @@ struct DecodeArgs {
   int32_t direct;
   float qscale;            // scale * log2(e)
   int32_t ring_bytes;      // LDS-staged kernel: bytes of the K/V ring (set by its launcher)
+  // single-launch merge (LDS-staged kernel, fused == 1): items are claimed from
+  // *work (decode units first, then merge_items slices of 64 output columns),
+  // done[b*ceil(Hkv/4) + hg] counts finished partitions, *leave the
+  // workgroups that have left; the last one to leave zeroes all three
+  uint32_t* work;
+  uint32_t* leave;
+  uint32_t* done;
+  int32_t fused;
+  int32_t merge_items;
+  uint64_t wait_ticks;     // longest wait of a merge slice, 100 MHz constant-clock ticks
 };
+
+// Workspace header: status word, then the single-launch counters; done[]
+// from byte kWsHeader, one counter every kDoneStride words (4 KB + 64 B, so
+// that every counter sits in its own memory line and channel: the waiting
+// merge slices poll them, and a line polled by hundreds of workgroups slows
+// the K/V stream through its channel), partials from ws_part_offset().
+constexpr uint64_t kWsHeader = 256;
+constexpr int kDoneStride = 1040;
+constexpr uint64_t ws_part_offset(int32_t B, int32_t Hkv) {
+  return kWsHeader + ((4ull * kDoneStride * uint64_t(B) * uint64_t((Hkv + 3) / 4) + 255) & ~255ull);
+}
 
 // Decode kernels: register streaming (any supported shape) and LDS staged
 // (the shapes lds_groups() admits, Hkv % 4 == 0, B <= kLdsMaxB, pools
@@ -153,6 +174,14 @@ struct MergeArgs {
 };
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// Output columns of one slice of the wide merge layout (merge_common.h).
+constexpr int kMergeColsHost = 64;
+// Whether launch_merge takes the row-per-thread layout (many rows of few
+// partitions: at most 16 over 1024+ rows or 32 over 512+) rather than the
+// wide one (one workgroup per row and 64 columns, merge_common.h).
+constexpr bool merge_rows_layout(int64_t rows, int p_max) {
+  return (p_max <= 16 && rows >= 1024) || (p_max <= 32 && rows >= 512);
+}
 
 // Workspace of paged_attn_step_noalloc: a file-scope device array of this
 // many bytes per GPU (step_noalloc.hip). noalloc_scratch returns its device

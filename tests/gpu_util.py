@@ -45,6 +45,8 @@ def plan_for(case, path=None, **kw):
         if path == 2 and not lds_path_ok(case):
             pytest.skip("the LDS-staged kernel does not take this shape")
         plan.path = path
+        if path == 1:
+            plan.fused = 0               # the single-launch merge is the LDS kernel's
     return plan
 
 

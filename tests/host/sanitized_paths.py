@@ -43,8 +43,14 @@ def test_decode_merge_step_reach_the_launcher(kw, force):
                                                     stream=0, ws_bytes=ws))
     _refused_at_launch(lambda: pa.paged_attn_decode(plan, FAKE, FAKE, FAKE, None, FAKE, FAKE, out=FAKE,
                                                     stream=0, ws_bytes=ws))
-    if not plan.direct:
+    if plan.direct or plan.fused:                  # merged by the decode (or nothing to merge)
+        pa.paged_attn_merge(plan, FAKE, FAKE, FAKE, stream=0, ws_bytes=ws)
+    else:
         _refused_at_launch(lambda: pa.paged_attn_merge(plan, FAKE, FAKE, FAKE, stream=0, ws_bytes=ws))
+    if plan.fused:                                 # two launches: both reach a launcher
+        plan.fused = 0
+        _refused_at_launch(lambda: pa.paged_attn_merge(plan, FAKE, FAKE, FAKE, stream=0, ws_bytes=ws))
+        plan.fused = 1
     _refused_at_launch(lambda: pa.paged_attn_step(plan, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0,
                                                   ws_bytes=ws))
     _refused_at_launch(lambda: pa.paged_kv_gather(plan, FAKE, 1, FAKE, 0, 16, 100, FAKE, stream=0))

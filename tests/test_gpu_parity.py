@@ -171,13 +171,14 @@ def _oracle_partials(case, psize):
                            scale=case.scale)
 
 
-def _ws_partials(ws, B, Hq, P, D):
+def _ws_partials(ws, plan, B, Hq, P, D):
     """(o [B,Hq,P,D] from binary16, ml [B,Hq,P,2] fp32) read from a workspace
-    in the documented layout."""
+    in the documented layout (partials from plan.part_offset)."""
     raw = ws.detach().cpu()
     n_o = B * Hq * P * D
-    o = raw[256:256 + 2 * n_o].view(torch.float16).reshape(B, Hq, P, D)
-    ml = raw[256 + 2 * n_o:256 + 2 * n_o + 8 * B * Hq * P].view(torch.float32).reshape(B, Hq, P, 2)
+    at = int(plan.part_offset)
+    o = raw[at:at + 2 * n_o].view(torch.float16).reshape(B, Hq, P, D)
+    ml = raw[at + 2 * n_o:at + 2 * n_o + 8 * B * Hq * P].view(torch.float32).reshape(B, Hq, P, 2)
     return o.double().numpy(), ml.double().numpy()
 
 
@@ -208,6 +209,7 @@ def test_merge_kernel_on_oracle_partials(name):
     lens, Hq, Hkv = MERGE_CASES[name]
     case = _case(lens, k_fmt="f16", v_fmt="q8_0", seed=23, Hq=Hq, Hkv=Hkv)
     plan = plan_for(case, partition_tokens=64)
+    plan.fused = 0                      # the separate merge kernel is what is tested here
     m, l, o, n = _oracle_partials(case, plan.psize)
     B, Hq, P, D = o.shape
     assert P == plan.p_max
@@ -215,8 +217,9 @@ def test_merge_kernel_on_oracle_partials(name):
     ml = np.stack([m, l], axis=-1).astype(np.float32)
     ws = pa.workspace(plan, "cpu")
     n_o = B * Hq * P * D
-    ws[256:256 + 2 * n_o] = torch.from_numpy(o16.reshape(-1)).view(torch.uint8)
-    ws[256 + 2 * n_o:256 + 2 * n_o + 8 * B * Hq * P] = torch.from_numpy(ml.reshape(-1)).view(torch.uint8)
+    at = int(plan.part_offset)
+    ws[at:at + 2 * n_o] = torch.from_numpy(o16.reshape(-1)).view(torch.uint8)
+    ws[at + 2 * n_o:at + 2 * n_o + 8 * B * Hq * P] = torch.from_numpy(ml.reshape(-1)).view(torch.uint8)
     wsd = ws.to(DEV)
     out = torch.full((B, Hq, D), float("nan"), device=DEV)
     pa.paged_attn_merge(plan, wsd, case.seq_len.to(DEV), out)
@@ -246,7 +249,7 @@ def test_decode_partials_match_the_oracle_split_form(pair, path):
     m_r, l_r, o_r, n = _oracle_partials(case, plan.psize)
     B, Hq, P, D = o_r.shape
     assert P == plan.p_max
-    o, ml = _ws_partials(ws, B, Hq, P, D)
+    o, ml = _ws_partials(ws, plan, B, Hq, P, D)
     tol = tol_for(case)
     for b in range(B):
         for p in range(int(n[b])):

@@ -88,8 +88,10 @@ def test_plan_automatic_partitions_for_long_context():
     assert p.psize % 32 == 0 and p.psize >= 1024
     assert p.p_max == -(-131072 // p.psize)
     assert p.direct == 0
-    # binary16 o rows, then fp32 (m, l) pairs
-    assert p.ws_bytes == 256 + 8 * 24 * p.p_max * (2 * 256 + 8)
+    # header, done[] counters of 8 sequences x 1 head quad (rounded to 256
+    # bytes), then binary16 o rows and fp32 (m, l) pairs
+    assert p.part_offset == 256 + 8 * 4160
+    assert p.ws_bytes == p.part_offset + 8 * 24 * p.p_max * (2 * 256 + 8)
     assert 1 <= p.grid <= 256 * 8
     assert abs(p.scale - 1 / 16) < 1e-7
 
@@ -97,7 +99,7 @@ def test_plan_automatic_partitions_for_long_context():
 def test_plan_partial_traffic_floor_and_direct_mode():
     # a short batch: one partition covers it -> direct
     p = pa.paged_attn_plan(_shape(B=1), 200, num_cus=256)
-    assert p.direct == 1 and p.p_max == 1 and p.ws_bytes == 256
+    assert p.direct == 1 and p.p_max == 1 and p.ws_bytes == p.part_offset == 256 + 4352
     assert p.psize >= 200
     # register kernel (Hkv not a multiple of 4): the floor keeps partials
     # under ~4% of the K/V bytes of a partition
@@ -133,6 +135,50 @@ def test_plan_lds_path_fills_two_workgroups_per_cu():
 def test_plan_picks_the_decode_kernel(kw, path):
     p = pa.paged_attn_plan(_shape(**kw), 4096, num_cus=256)
     assert p.path == path
+
+
+def test_plan_single_launch_merge_choice_and_checks():
+    """fused (decode and merge in one launch) is the caller's choice (the
+    planner leaves it 0: two launches measured faster on MI355X); it is
+    accepted on the LDS kernel when partitions are merged with the wide
+    layout, refused on the register kernel, in direct mode and where the
+    merge takes the row-per-thread layout."""
+    fake = 0x1000
+
+    def decode(plan, out=fake):
+        pa.paged_attn_decode(plan, fake, fake, fake, fake, fake, fake, out=out, stream=0,
+                             ws_bytes=int(plan.ws_bytes))
+
+    p = pa.paged_attn_plan(_shape(), 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.path == 2 and p.fused == 0 and p.direct == 0 and p.grid == 512
+    d = pa.paged_attn_plan(_shape(B=1), 200, num_cus=256)
+    assert d.direct == 1 and d.fused == 0
+    d.fused = 1
+    with pytest.raises(pa.PaError) as e:
+        decode(d)
+    assert e.value.code == pa.PA_ERR_INVALID and "fused" in str(e.value)
+    # 64 sequences x 24 heads = 1536 rows of 16 partitions: row-per-thread merge
+    w = pa.paged_attn_plan(_shape(B=64, nblocks=200000), 4096, num_cus=256, force_partitions=16)
+    assert w.path == 2 and w.p_max <= 16 and w.fused == 0
+    w.fused = 1
+    with pytest.raises(pa.PaError) as e:
+        decode(w)
+    assert e.value.code == pa.PA_ERR_INVALID and "fused" in str(e.value)
+    p.fused = 1
+    p.path = 1
+    with pytest.raises(pa.PaError) as e:
+        pa.paged_attn_decode(p, fake, fake, fake, fake, fake, fake, out=fake, stream=0,
+                             ws_bytes=int(p.ws_bytes))
+    assert e.value.code == pa.PA_ERR_INVALID and "fused" in str(e.value)
+    p.path, p.fused = 2, 1
+    with pytest.raises(pa.PaError) as e:          # a fused decode writes out
+        pa.paged_attn_decode(p, fake, fake, fake, fake, fake, fake, out=None, stream=0,
+                             ws_bytes=int(p.ws_bytes))
+    assert e.value.code == pa.PA_ERR_INVALID
+    pa.paged_attn_merge(p, fake, fake, fake, stream=0, ws_bytes=int(p.ws_bytes))   # no-op
+    p.part_offset = 256
+    with pytest.raises(pa.PaError):
+        pa.paged_attn_merge(p, fake, fake, fake, stream=0, ws_bytes=int(p.ws_bytes))
 
 
 def test_plan_path_two_refused_where_the_shape_does_not_fit():
@@ -286,9 +332,10 @@ def test_chunk_plan_partitions_and_workspace():
     assert p.grid == min(units, 256 * 2)
     big = pa.paged_attn_chunk_plan(_shape(B=1), 512, 8192, num_cus=256)
     assert big.grid == min(1 * big.p_max * 4 * 48, 512)      # 3072 rows: 48 blocks of 64
-    assert p.ws_bytes == -(-(256 + 8 * 8 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
+    assert p.part_offset == 256 + 8 * 4160
+    assert p.ws_bytes == -(-(p.part_offset + 8 * 8 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
     d = pa.paged_attn_chunk_plan(_shape(B=1), 16, 200, num_cus=256)
-    assert d.direct == 1 and d.p_max == 1 and d.ws_bytes == 256
+    assert d.direct == 1 and d.p_max == 1 and d.ws_bytes == 256 + 4352
     f = pa.paged_attn_chunk_plan(_shape(), 4, 1000, num_cus=256, partition_tokens=64)
     assert f.psize == 64 and f.p_max == 16
 
