@@ -55,6 +55,7 @@ WORKLOADS = {
     "uniform_q4_0_128k_b8": ("uniform_q4_0", 8, 131072, "uniform Q4_0 B=8 L=131072"),
     "uniform_q4_0_32k_b8": ("uniform_q4_0", 8, 32768, "uniform Q4_0 B=8 L=32768"),
     "uniform_q8_0_4k_b8": ("uniform_q8_0", 8, 4096, "uniform Q8_0 B=8 L=4096"),
+    "uniform_f16_32k_b8": ("uniform_f16", 8, 32768, "uniform F16 B=8 L=32768"),
     "ragged_q4_0": ("ragged_q4_0", 8, 131072, "ragged Q4_0 131072+7x8192"),
     "ragged_small_q4_0": ("ragged_small_q4_0", 8, 4096, "ragged Q4_0 4096+7x256"),
     "tiny_f16": ("tiny_f16", 1, 200, "tiny F16 B=1 L=200"),

@@ -63,9 +63,10 @@ int32_t check_shape(const pa_shape* s, const char* who) {
 }
 
 // The LDS-staged kernel takes the shape: quads of kv heads, the batch prefix
-// fits its LDS budget, and one step of both sides fits a ring slot.
+// fits its LDS budget, and one step of both sides (16 or 8 token slots of
+// four heads) fits a ring slot.
 bool lds_path_ok(const pa_shape& s) {
-  return s.Hkv % 4 == 0 && s.B <= kLdsMaxB && lds_groups(s.k_type, s.v_type, s.D) > 0;
+  return s.Hkv % 4 == 0 && s.B <= kLdsMaxB && decode_group_slots(s.k_type, s.v_type, s.D) > 0;
 }
 
 // The single-launch merge runs the wide merge layout's slices; where the

@@ -84,11 +84,12 @@ template <int KT, int VT, int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArgs a) {
   using KF = KFmt<KT, D>;
   using VF = VFmt<VT, D>;
-  using LY = LdsLayout<KT, VT, D>;
+  using LY = LdsLayout<KT, VT, D, decode_group_slots(KT, VT, D)>;
   constexpr int S = D / 32;      // score MFMA steps
   constexpr int E = D / 16;      // PV d-tiles
-  constexpr int G = LY::G;       // 16-row groups per step
-  constexpr int T = 16 * G;      // tokens per step
+  constexpr int G = LY::G;       // token-slot groups per step, each one 16-row MFMA tile
+  constexpr int GS = LY::kGS;    // slots per group: 16, or 8 (tile rows 8..15 masked)
+  constexpr int T = GS * G;      // tokens per step
   constexpr int NP = 2 * G;      // V row pairs per lane (4 rows per group)
   constexpr bool kKFold = KT == kQ4_0;   // Q4_0 offsets folded into corrections
   constexpr bool kVFold = VT == kQ4_0;
@@ -129,11 +130,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
   const int cw = (LY::NI - wave + 3) / 4;              // DMA instructions this wave issues per step
   // LDS offsets (within a group) of the rows this lane reads: K row m, V rows
   // 4j+i, of the wave's head, at their rotated row positions
-  const int k_row = m * LY::SPK + ((wave + RowRot<LY::RBK>::k(m)) & 3) * LY::RBK + int(KF::lane_off(j));
+  // (with 8-slot groups, tile rows 8..15 read rows 0..7 again and are masked)
+  const int km = m & (GS - 1);
+  const int k_row = km * LY::SPK + ((wave + RowRot<LY::RBK>::k(km)) & 3) * LY::RBK + int(KF::lane_off(j));
   int v_row[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    v_row[i] = (4 * j + i) * LY::SPV + ((wave + RowRot<LY::RBV>::v(4 * j + i)) & 3) * LY::RBV;
+    v_row[i] = ((4 * j + i) & (GS - 1)) * LY::SPV + ((wave + RowRot<LY::RBV>::v((4 * j + i) & (GS - 1))) & 3) * LY::RBV;
   const uint32_t kstride = uint32_t(a.Hkv) * LY::RBK;  // pool bytes between token slots
   const uint32_t vstride = uint32_t(a.Hkv) * LY::RBV;
   const uint32_t ksh = KF::shift(j);
@@ -165,10 +168,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     for (int i = 0; i < LY::NIW; ++i) {
       const int q = wave + 4 * i;
       if (q < G * LY::NIK)
-        dvoff[i] = chunk_voff<LY::CPK, LY::RBK>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
+        dvoff[i] = chunk_voff<LY::CPK, LY::RBK, GS>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
                                                  RowRot<LY::RBK>::k);
       else
-        dvoff[i] = chunk_voff<LY::CPV, LY::RBV>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
+        dvoff[i] = chunk_voff<LY::CPV, LY::RBV, GS>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
                                                  16u * vstride, RowRot<LY::RBV>::v);
     }
 
@@ -266,11 +269,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
       auto compute = [&](int s) __attribute__((always_inline)) {
         const unsigned char* slot = ring + (s % LY::R) * LY::SLOT;
         const int t0 = seg_t0 + s * T;
-        const bool full = t0 + T <= t_end;
+        // (an 8-slot step is never full: its tile rows 8..15 are masked)
+        const bool full = GS == 16 && t0 + T <= t_end;
         // tokens of the step left before t_end (wave-uniform): the row tests
         // below compare it, less a constant, with the lane's fixed 4j or m, so
         // that they cost no per-step vector arithmetic
-        const int rem = t_end - t0;
+        const int rem = GS == 16 ? t_end - t0 : min(t_end - t0, GS);
         typename KF::Raw kr[G];
         typename VF::Raw vr[2 * NP];
 #pragma unroll
@@ -616,7 +620,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
 // starts inside a block touches kNidS+1 blocks).
 template <int KT, int VT, int D>
 size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
-  using LY = LdsLayout<KT, VT, D>;
+  using LY = LdsLayout<KT, VT, D, decode_group_slots(KT, VT, D)>;
   static_assert(size_t(LY::R) * LY::SLOT >= sizeof(MergeLds), "merge slices reuse the ring");
   static_assert(size_t(LY::R) * LY::SLOT >= 4 * 16 * 2 * D, "four waves stage up to 16 binary16 rows each");
   const size_t ring = size_t(LY::R) * LY::SLOT;
@@ -626,7 +630,7 @@ size_t lds_bytes(const DecodeArgs& a, int* ring_bytes) {
 
 template <int KT, int VT, int D>
 hipError_t launch_typed(const DecodeArgs& a0, hipStream_t stream) {
-  if constexpr (lds_groups(KT, VT, D) == 0) {
+  if constexpr (decode_group_slots(KT, VT, D) == 0) {
     return hipErrorInvalidValue;
   } else {
     DecodeArgs a = a0;

@@ -9,18 +9,23 @@
 namespace pa {
 namespace {
 
-template <int KT, int VT, int D>
+// GS: token slots per group, 16, or 8 for the decode kernel's rows too large
+// for 16 (decode_group_slots).
+template <int KT, int VT, int D, int GS = 16>
 struct LdsLayout {
+  static_assert(GS == 16 || GS == 8, "groups of 16 or 8 slots");
   static constexpr int RBK = row_bytes_of(KT, D), RBV = row_bytes_of(VT, D);
   static constexpr int SPK = 4 * RBK, SPV = 4 * RBV;   // one slot's rows of 4 heads
   static constexpr int CPK = SPK / 16, CPV = SPV / 16; // 16-byte chunks per slot
-  static constexpr int NIK = lds_dma_per_group(KT, D), NIV = lds_dma_per_group(VT, D);
-  static constexpr int G = lds_groups(KT, VT, D);
+  static constexpr int NIK = lds_dma_per_slots(KT, D, GS), NIV = lds_dma_per_slots(VT, D, GS);
+  static constexpr int G = GS == 16 ? lds_groups(KT, VT, D) : 1;
   static constexpr int VOFF = G * NIK * 1024;          // V groups follow the K groups
-  static constexpr int SLOT = lds_slot_bytes(KT, VT, D, G);
-  static constexpr int R = lds_ring_slots(KT, VT, D);   // ring slots
+  static constexpr int SLOT = G * 1024 * (NIK + NIV);
+  static constexpr int R = SLOT == 0 ? 0 : (kLdsRingBytes / SLOT > kLdsMaxSlots ? kLdsMaxSlots
+                                                                               : kLdsRingBytes / SLOT);
   static constexpr int NI = G * (NIK + NIV);           // DMA instructions per step
   static constexpr int NIW = (NI + 3) / 4;             // at most this many per wave
+  static constexpr int kGS = GS;        // token slots per group
   static_assert(SPK % 16 == 0 && SPV % 16 == 0, "4-row runs are whole 16-byte chunks");
 };
 
@@ -53,11 +58,11 @@ template <int RB> struct RowRot {
 };
 
 // Pool offset of the chunk lane l fetches in the 1 KB DMA instruction `sub`
-// of a 16-slot group: LDS chunk 64*sub + l of a group whose slots are CP
+// of a GS-slot group: LDS chunk 64*sub + l of a group whose slots are CP
 // chunks (four rows of RB bytes) long in LDS and `stride` bytes apart in the
 // pool, starting `head_off` bytes into each pool slot, rows placed by `rot`;
 // chunks past the group get `oob` (reads as 0).
-template <int CP, int RB>
+template <int CP, int RB, int GS = 16>
 __device__ __forceinline__ uint32_t chunk_voff(int sub, int lane, uint32_t stride, uint32_t head_off,
                                                uint32_t oob, int (*rot)(int)) {
   const int c = 64 * sub + lane;
@@ -68,7 +73,7 @@ __device__ __forceinline__ uint32_t chunk_voff(int sub, int lane, uint32_t strid
     const int hp = within / CPR;                       // row position in LDS
     within += (((hp - rot(slot)) & 3) - hp) * CPR;     // the pool row stored there
   }
-  return c < 16 * CP ? uint32_t(slot) * stride + head_off + 16u * within : oob;
+  return c < GS * CP ? uint32_t(slot) * stride + head_off + 16u * within : oob;
 }
 
 // One DMA instruction: every lane fetches 16 bytes at its offset and the
@@ -81,8 +86,8 @@ __device__ __forceinline__ void dma16(rsrc_t R, uint32_t dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, kDmaNonTemporal);
 }
 
-// DMA of one step into the ring slot at LDS byte `slot`: the LY::G 16-slot
-// groups of K and V of tokens t0 .. t0 + 16*LY::G - 1 of the current segment
+// DMA of one step into the ring slot at LDS byte `slot`: the LY::G groups of
+// GS token slots of K and V, tokens t0 .. t0 + GS*LY::G - 1 of the current segment
 // (block ids[] staged from block jb0; groups at or past seg_t1 get a
 // zero-size resource and read nothing). Wave W issues the instructions q
 // with q % 4 == W; W is a compile-time constant, so the selection costs no
@@ -95,14 +100,14 @@ __device__ __forceinline__ void issue_step_as(const Args& a, uint32_t slot, int 
   const int bs_mask = (1 << a.bs_shift) - 1;
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
-    const int tg = t0 + 16 * gi;
+    const int tg = t0 + LY::kGS * gi;
     const bool live = tg < seg_t1;
     const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
     const int slot0 = live ? (tg & bs_mask) : 0;
     const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBK),
-                                live ? 16u * kstride : 0u);
+                                live ? uint32_t(LY::kGS) * kstride : 0u);
     const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, 0, LY::RBV),
-                                live ? 16u * vstride : 0u);
+                                live ? uint32_t(LY::kGS) * vstride : 0u);
 #pragma unroll
     for (int sub = 0; sub < LY::NIK; ++sub) {
       const int q = gi * LY::NIK + sub;

@@ -29,7 +29,7 @@ constexpr int kMergeCols = 64;                          // output columns per sl
 constexpr int kMergeOcts = kMergeCols / 8;              // 16-byte loads of 8 binary16 columns
 constexpr int kMergeClasses = kMergeThreads / kMergeOcts;  // partition classes
 constexpr int kMergePre = 2;                            // partitions per class loaded ahead of the max
-constexpr int kMergeBatch = 8;                          // partitions per class per later batch
+constexpr int kMergeBatch = 16;                         // partitions per class per later batch
 
 // LDS the slice needs (kMergeThreads threads, four waves).
 struct MergeLds {
@@ -70,7 +70,7 @@ __device__ __forceinline__ void merge_slice(const f16* o_row, const float* ml_ro
   const int q = tid % kMergeOcts, c = tid / kMergeOcts;
 
   // Loads in flight together: the first kMergePre partitions of this thread's
-  // class with their (m, l), and m of partition tid. They go through buffer
+  // class with their (m, l), and m of partitions tid and tid + 256. They go through buffer
   // resources that end at the row's last live partition, so a load past it
   // returns 0 without touching memory and none needs a branch.
   const rsrc_t ro = make_rsrc(o_row, uint32_t(P) * uint32_t(D) * 2u);
@@ -85,9 +85,15 @@ __device__ __forceinline__ void merge_slice(const f16* o_row, const float* ml_ro
     mlp[u] = bitcast<float2>(__builtin_amdgcn_raw_buffer_load_b64(rml, pu * 8u, 0, kPolicy));
   }
   const float m0 = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(rml, uint32_t(tid) * 8u, 0, kPolicy));
+  const float m1 =
+      bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(rml, uint32_t(tid + kMergeThreads) * 8u, 0, kPolicy));
   float mx = tid < P ? m0 : -INFINITY;
   bool nan_seen = mx != mx;
-  for (int p = tid + kMergeThreads; p < P; p += kMergeThreads) {
+  if (tid + kMergeThreads < P) {
+    nan_seen |= m1 != m1;
+    mx = fmaxf(mx, m1);
+  }
+  for (int p = tid + 2 * kMergeThreads; p < P; p += kMergeThreads) {
     const float mp = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(rml, uint32_t(p) * 8u, 0, kPolicy));
     nan_seen |= mp != mp;
     mx = fmaxf(mx, mp);

@@ -92,6 +92,19 @@ constexpr int lds_ring_slots(int kt, int vt, int D) {
                     ? kLdsMaxSlots
                     : kLdsRingBytes / lds_slot_bytes(kt, vt, D, lds_groups(kt, vt, D)));
 }
+// The decode kernel also takes rows too large for a 16-slot group (an F16
+// side at D = 256: 32 KB of K or V per group of four heads): its steps are
+// then one group of 8 slots, still computed as 16-row MFMA tiles whose last
+// 8 rows are masked. 1 KB DMA instructions for GS slots x 4 heads of a side:
+constexpr int lds_dma_per_slots(int type, int D, int GS) {
+  return (GS * 4 * lds_row_bytes(type, D) + 1023) / 1024;
+}
+// Slots per group of the decode kernel: 16 where lds_groups() admits the
+// shape, else 8 when a two-slot ring of 8-slot steps fits, else 0.
+constexpr int decode_group_slots(int kt, int vt, int D) {
+  return lds_groups(kt, vt, D) > 0 ? 16
+         : (2 * 1024 * (lds_dma_per_slots(kt, D, 8) + lds_dma_per_slots(vt, D, 8)) <= kLdsRingBytes ? 8 : 0);
+}
 
 // Arguments of one chunk launch (multi-token queries), validated on the host.
 struct ChunkArgs {

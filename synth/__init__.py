@@ -329,6 +329,7 @@ def workload(name: str, *, B: int = 8, L: int = 4096, seed: int = 1000, device="
     tiny_f16     : B=1, L=200 (last block partly filled), 32-block pool, F16.
     uniform_q8_0 : B sequences of L tokens, Q8_0 K/V (L=4096 in the pages' 4K row).
     uniform_q4_0 : B sequences of L tokens, Q4_0 K/V (L in {32768, 131072}).
+    uniform_f16  : B sequences of L tokens, F16 K/V (D=256, Hq=24, Hkv=4).
     ragged_q4_0  : 131072 + 7 x 8192 tokens, blocks interleaved in one pool.
     ragged_small_q4_0 : 4096 + 7 x 256 tokens.
     slab_f16     : D=128, Hq=32, Hkv=8, blocks of 32, 139,264-block pool
@@ -342,6 +343,8 @@ def workload(name: str, *, B: int = 8, L: int = 4096, seed: int = 1000, device="
         return make_case([L] * B, k_fmt="q8_0", v_fmt="q8_0", seed=seed, device=device, junk=junk)
     if name == "uniform_q4_0":
         return make_case([L] * B, k_fmt="q4_0", v_fmt="q4_0", seed=seed, device=device, junk=junk)
+    if name == "uniform_f16":
+        return make_case([L] * B, k_fmt="f16", v_fmt="f16", seed=seed, device=device, junk=junk)
     if name == "ragged_q4_0":
         return make_case([131072] + [8192] * 7, k_fmt="q4_0", v_fmt="q4_0", seed=seed,
                          device=device, junk=junk)

@@ -26,11 +26,12 @@ def shape_for(case):
 
 def lds_path_ok(case):
     """Whether the LDS-staged decode kernel (plan path 2) takes the case's shape:
-    quads of kv heads, B <= 256, and one 16-slot group of K and V of four heads
-    in a 36 KB ring slot (so no F16 side at D=256)."""
+    quads of kv heads, B <= 256, and one group of 16 (else 8) token slots of K
+    and V of four heads in a 36 KB ring slot."""
     rb = {"f16": 2 * case.D, "q8_0": 34 * case.D // 32, "q4_0": 18 * case.D // 32}
-    per_group = sum(-(-16 * 4 * rb[f] // 1024) for f in (case.k_fmt, case.v_fmt)) * 1024
-    return case.Hkv % 4 == 0 and case.B <= 256 and per_group <= 36864
+    fits = any(sum(-(-gs * 4 * rb[f] // 1024) for f in (case.k_fmt, case.v_fmt)) * 1024 <= 36864
+               for gs in (16, 8))
+    return case.Hkv % 4 == 0 and case.B <= 256 and fits
 
 
 def plan_for(case, path=None, **kw):

@@ -92,3 +92,14 @@ def test_slab_past_2pow32_elements_gather_and_decode():
     sampled_parity(case, out, all_groups(case))
     del case, out
     _free()
+
+
+def test_uniform_f16_d256_32k_on_eight_slot_groups():
+    """F16 K and V at D=256 (the lucebox page's head size): 16 slots of four
+    heads' rows do not fit a ring slot, so the LDS-staged kernel streams
+    8-slot groups; every (sequence, kv head) group is checked at 8 x 32K."""
+    case = synth.workload("uniform_f16", B=8, L=32768, seed=1500, device=DEV)
+    out, plan = _run_auto(case)
+    assert plan.path == 2 and plan.p_max > 1
+    sampled_parity(case, out, all_groups(case))
+    _free()

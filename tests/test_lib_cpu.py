@@ -125,8 +125,8 @@ def test_plan_lds_path_fills_two_workgroups_per_cu():
 @pytest.mark.parametrize("kw,path", [
     (dict(), 2),                                   # Q4_0/Q4_0, D=256, Hkv=4
     (dict(k_type="q8_0", v_type="q8_0"), 2),
-    (dict(k_type="f16", v_type="f16"), 1),         # a 16-slot group of 4 F16 rows of D=256 is too big
-    (dict(k_type="f16", v_type="q4_0"), 1),
+    (dict(k_type="f16", v_type="f16"), 2),         # 8-slot groups: 16 slots of 4 F16 rows of D=256 are too big
+    (dict(k_type="f16", v_type="q4_0"), 2),
     (dict(k_type="f16", v_type="f16", D=128, Hq=32, Hkv=8), 2),
     (dict(Hq=12, Hkv=2), 1),                       # no quad of kv heads
     (dict(Hq=24, Hkv=8), 2),
@@ -182,7 +182,7 @@ def test_plan_single_launch_merge_choice_and_checks():
 
 
 def test_plan_path_two_refused_where_the_shape_does_not_fit():
-    p = pa.paged_attn_plan(_shape(k_type="f16", v_type="f16"), 4096, num_cus=256)
+    p = pa.paged_attn_plan(_shape(Hq=12, Hkv=2), 4096, num_cus=256)
     p.path = 2
     fake = 0x1000
     with pytest.raises(pa.PaError) as e:
