@@ -121,8 +121,8 @@ typedef struct pa_plan {
   int32_t direct;       /* 1: p_max == 1, decode writes out, merge is a no-op */
   int32_t path;         /* decode kernel: 2 = LDS-staged (K/V blocks DMA'd into
                            LDS, one workgroup per 4 kv heads; needs Hkv % 4 == 0,
-                           B <= 256, no F16 side at D=256 and 16-byte aligned
-                           pools, else path 1 runs), 1 = register-streaming.
+                           B <= 256, and pools and q 16-byte aligned, else
+                           path 1 runs), 1 = register-streaming.
                            paged_attn_plan picks 2 where the shape allows it; a
                            caller may set 1 to force the register kernel (and
                            must then set fused = 0). The two kernels differ

@@ -260,8 +260,10 @@ extern "C" int32_t paged_attn_decode(const pa_plan* plan, const float* q, const 
   a.qscale = float(double(plan->scale) * 1.4426950408889634);   // scale * log2(e)
   a.merge_items = s.B * s.Hq * (s.D / kMergeColsHost);
   a.wait_ticks = 100000000ull;                                   // one second of the 100 MHz clock
-  // the LDS-staged kernel's DMA chunks are 16-byte aligned only on aligned pools
-  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) == 0;
+  // the LDS-staged kernel's DMA chunks are 16-byte aligned only on aligned
+  // pools, and it reads q rows with 16-byte loads
+  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
+                         reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   const bool lds = plan->path == 2 && aligned;
   a.fused = plan->fused && lds ? 1 : 0;
   // a single launch also runs the merge slices: more workgroups, up to the

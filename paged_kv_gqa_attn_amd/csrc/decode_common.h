@@ -145,7 +145,11 @@ template <int D> struct KFmt<kF16, D> {
     for (int s = 0; s < S; ++s) r.c[s] = *reinterpret_cast<const u32x4*>(p + 64 * s);
   }
   __device__ static f16x8 op(const Raw& r, int s, uint32_t, uint32_t) { return bitcast<f16x8>(r.c[s]); }
-  __host__ __device__ static int dslot(int j, int s, int i) { return 32 * s + 8 * j + i; }
+  __host__ __device__ static constexpr int dslot(int j, int s, int i) { return 32 * s + 8 * j + i; }
+  // dslot(j, s, i) = dslot(j, s, 0) + qoff(i): two aligned groups of four
+  // positions, the second kQGap past the first (load_q_slots)
+  static constexpr int kQGap = 4;
+  __host__ __device__ static constexpr int qsel(int i) { return i; }
   __device__ static uint32_t shift(int) { return 0; }
 };
 
@@ -213,9 +217,14 @@ template <int D> struct KFmt<kQ8_0, D> : KQuantBase<kQ8_0, D> {
     return pack8(i8pair_to_f16(u0, d2, mg), i8pair_to_f16(u0 >> 8, d2, mg),
                  i8pair_to_f16(u1, d2, mg), i8pair_to_f16(u1 >> 8, d2, mg));
   }
-  __host__ __device__ static int dslot(int j, int s, int i) {
-    const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+  __host__ __device__ static constexpr int dslot(int j, int s, int i) {
+    constexpr int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
     return 32 * (j * NBL + s / 4) + 8 * (s % 4) + order[i];
+  }
+  static constexpr int kQGap = 4;
+  __host__ __device__ static constexpr int qsel(int i) {
+    constexpr int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    return order[i];
   }
 };
 
@@ -246,12 +255,46 @@ template <int D> struct KFmt<kQ4_0, D> : KQuantBase<kQ4_0, D> {
     return pack8(nib_pair_to_f16(w, d2, mg), nib_pair_to_f16(w >> 4, d2, mg),
                  nib_pair_to_f16(w >> 8, d2, mg), nib_pair_to_f16(w >> 12, d2, mg));
   }
-  __host__ __device__ static int dslot(int j, int s, int i) {
-    const int c = s % 4;
-    const int order[8] = {0, 2, 16, 18, 1, 3, 17, 19};
-    return 32 * (j * NBL + s / 4) + 4 * c + order[i];
+  __host__ __device__ static constexpr int dslot(int j, int s, int i) {
+    constexpr int order[8] = {0, 2, 16, 18, 1, 3, 17, 19};
+    return 32 * (j * NBL + s / 4) + 4 * (s % 4) + order[i];
+  }
+  static constexpr int kQGap = 16;
+  __host__ __device__ static constexpr int qsel(int i) {
+    constexpr int sel[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    return sel[i];
   }
 };
+
+// The q values at dslot(j, s, 0..7) for every MFMA step s (s < S) of a K
+// format, from one fp32 row qw (16-byte aligned): the 8 positions of a step
+// are two aligned groups of four floats, at dslot(j, s, 0) and kQGap past it,
+// so two 16-byte loads per step.
+template <class KF>
+__host__ __device__ constexpr bool q_slots_ok(int S) {
+  for (int j = 0; j < 4; ++j)
+    for (int s = 0; s < S; ++s) {
+      if (KF::dslot(j, s, 0) % 4) return false;
+      for (int i = 0; i < 8; ++i) {
+        const int q = KF::qsel(i);
+        if (KF::dslot(j, s, i) != KF::dslot(j, s, 0) + (q < 4 ? q : KF::kQGap + q - 4)) return false;
+      }
+    }
+  return true;
+}
+template <class KF, int S>
+__device__ __forceinline__ void load_q_slots(const float* qw, int j, float (&qv)[S][8]) {
+  static_assert(q_slots_ok<KF>(S), "dslot is two aligned groups of four positions per step");
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float* p = qw + KF::dslot(j, s, 0);
+    const float4 A = *reinterpret_cast<const float4*>(p);
+    const float4 B = *reinterpret_cast<const float4*>(p + KF::kQGap);
+    const float v[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[s][i] = v[KF::qsel(i)];
+  }
+}
 
 // ===========================================================================
 // V formats: the A operand of the PV MFMA is V^T. Lane (m, j) holds, for

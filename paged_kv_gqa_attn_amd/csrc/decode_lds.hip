@@ -193,10 +193,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_lds_kernel(const DecodeArg
     {
       const int n = m < a.r ? m : a.r - 1;
       const float* qw = a.q + (int64_t(b) * a.Hq + int64_t(g) * a.r + n) * D;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[s][i] = qw[KF::dslot(j, s, i)];
+      load_q_slots<KF, S>(qw, j, qv);       // q is 16-byte aligned on this path
     }
     __syncthreads();                        // the previous unit is done with the ring and ids[]
     int bad = 0;
