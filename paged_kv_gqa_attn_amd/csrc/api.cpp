@@ -502,15 +502,16 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   const int64_t L = max_seq_len;
   const int64_t r = s.Hq / s.Hkv;
   // the window kernel takes short chunks (a workgroup per kv-head quad, two
-  // per CU for at most 16 query rows per kv head, else one); the
+  // per CU for at most 16 query rows per kv head, else one; with the head
+  // dimension split, a workgroup per kv-head pair, two per CU); the
   // tile-conversion kernel the rest (a workgroup per kv head and 64*nt query
   // rows, one or two per CU)
   const bool window = chunk_window_ok(int64_t(tq) * r, s.Hkv, s.k_type, s.v_type, s.D);
   const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
   const int64_t qt = window ? 1 : (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // row blocks per unit
-  const int64_t heads_per_unit = window ? 4 : 1;
-  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(int(ceil_div(int64_t(tq) * r, 16)))
-                                : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
+  const int nq = int(ceil_div(int64_t(tq) * r, 16));
+  const int64_t heads_per_unit = window ? chunk_window_heads(nq, s.D) : 1;
+  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D) : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {
@@ -604,8 +605,10 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.qscale = float(double(plan->scale) * 1.4426950408889634);
   a.nt = chunk_wave_tiles(int64_t(plan->tq) * a.r, s.D);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the window kernel's DMA chunks are 16-byte aligned only on aligned pools
-  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) == 0;
+  // the window kernel's DMA chunks are 16-byte aligned only on aligned
+  // pools, and it reads q rows with 16-byte loads
+  const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
+                         reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   hipError_t e = plan->path == 2 && aligned ? launch_chunk_lds(a, st) : launch_chunk(a, st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   if (!plan->direct) {

@@ -6,22 +6,32 @@
 // prompt-chunk attention): chunk token t of sequence b (length L) sits at position
 // L - Tq + t and attends to the keys at positions 0 .. L - Tq + t of kv head
 // g = h / r. It serves the chunks whose Tq*r query rows of a kv head fit
-// 16*NQ MFMA columns, NQ <= 2 at D = 256 and NQ <= 3 at D = 128 (what one
-// wave's registers hold next to the NQ*D/16 accumulator tiles: at r = 6 a
+// 16*NQ MFMA columns, NQ <= 2 at D = 256 and NQ <= 3 at D = 128 (at r = 6 a
 // verify window of up to 5 tokens at D = 256, 8 at D = 128), where
 // converting each K/V tile into LDS operands for four waves of 16 rows
 // (chunk.hip) costs more LDS traffic than the rows are worth.
 //
 // It is the decode kernel's LDS ring with the query rows in place of the
 // heads: a workgroup of four wave64s takes a unit (sequence b, key partition
-// p, quad of kv heads hg), the DMA brings each 16-slot group of the four
-// heads' K and V rows into LDS as 1 KB contiguous instructions, and wave w
-// serves kv head 4*hg + w with all Tq*r of its query rows: each K and V row
-// it reads from LDS is converted once into the MFMA operand and used for its
-// NQ column groups. Each lane's row has its own causal limit; only steps
-// that cross some row's limit are masked, and a row with no key in the
-// partition writes m = -inf, l = 0. Partials use the decode layout with
-// Tq*Hq rows per sequence and go through the same merge.
+// p, group hg of kv heads), the DMA brings each 16-slot group of those
+// heads' K and V rows into LDS as 1 KB contiguous instructions, and each
+// wave converts the K and V rows it reads from LDS once into MFMA operands
+// used for all of its NQ column groups. Two shapes of workgroup:
+//  * a quad of kv heads, wave w serving head 4*hg + w over the whole head
+//    dimension (one column group: two workgroups per CU, as in decode; two or
+//    three at D = 128: one workgroup per CU, whose registers hold the
+//    NQ*D/16 accumulator tiles and NQ*D/32 Q operands);
+//  * two column groups at D = 256, where those are 64 + 128 registers and one
+//    wave per SIMD leaves the step latency-bound: a pair of kv heads, two
+//    waves per head, each taking half of the head dimension (its Q operands,
+//    K and V conversion and output columns), the halves' partial scores
+//    added through LDS each step; two workgroups per CU. (Measured on the
+//    verify window Q4_0 B=8 L=32768 Tq=4: 121 us per step with the quad of
+//    whole-dimension waves, 99 us with the pairs.)
+// Each lane's row has its own causal limit; only steps that cross some row's
+// limit are masked, and a row with no key in the partition writes m = -inf,
+// l = 0. Partials use the decode layout with Tq*Hq rows per sequence and go
+// through the same merge.
 #include <type_traits>
 
 #include "decode_common.h"
@@ -30,61 +40,101 @@
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kNidS = 512;     // block ids staged per segment of a partition
-constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
+constexpr int kIdsBytes = 4 * ((kNidS + 1 + 3) & ~3);
 
-// The ring of this kernel. With one column group (at most 16 query rows per
-// kv head) the registers fit two workgroups per CU, and the ring is the
-// decode kernel's; with more, one workgroup per CU takes the registers of
-// two, so it may use twice the decode kernel's LDS.
-template <int KT, int VT, int D, int NQ>
+// The ring of this kernel. WH = 1 (a quad of kv heads, one wave each): with
+// one column group (at most 16 query rows per kv head) the registers fit two
+// workgroups per CU, and the ring is the decode kernel's; otherwise one
+// workgroup per CU holds the registers of two and may use twice the decode
+// kernel's LDS. WH = 2 (a pair of kv heads, two waves each): two workgroups
+// per CU, each with 80 KB of LDS for the ring, the block ids and XBYTES for
+// the partial scores the waves exchange; steps of two 16-slot groups where
+// that leaves two ring slots, else one.
+template <int KT, int VT, int D, int NQ, int WH>
 struct WinRing {
-  using LY = LdsLayout<KT, VT, D>;
-  static constexpr int kWgsPerCu = chunk_window_wgs_per_cu(NQ);
-  static constexpr int R = kWgsPerCu == 2 ? LY::R
-                           : ((2 * kLdsRingBytes) / LY::SLOT < 4 ? (2 * kLdsRingBytes) / LY::SLOT : 4);
+  static_assert(WH == chunk_window_split(NQ, D), "the split the plan counts units by");
+  static constexpr int NH = WH == 2 ? 2 : 4;           // kv heads per workgroup
+  static constexpr int kWgsPerCu = chunk_window_wgs_per_cu(NQ, D);
+  static constexpr int xbytes(int g) { return WH == 2 ? 4 * NQ * g * 64 * 16 : 0; }
+  static constexpr int slot(int g) {
+    return g * 1024 * (lds_dma_per_slots(KT, D, 16, NH) + lds_dma_per_slots(VT, D, 16, NH));
+  }
+  static constexpr int budget(int g) {
+    // (1 KB of the 80 is left for the static LDS the compiler may add)
+    return WH == 2 ? 79 * 1024 - kIdsBytes - xbytes(g) : (kWgsPerCu == 2 ? kLdsRingBytes : 2 * kLdsRingBytes);
+  }
+  using LY = LdsLayout<KT, VT, D, 16, NH, WH == 2 ? (2 * slot(2) <= budget(2) ? 2 : 1) : 0>;
+  static constexpr int XBYTES = xbytes(LY::G);
+  static constexpr int R = budget(LY::G) / LY::SLOT < 4 ? budget(LY::G) / LY::SLOT : 4;
   static constexpr int BYTES = R * LY::SLOT;
+  static constexpr int LDS = BYTES + kIdsBytes + XBYTES;
+  static_assert(R >= 2, "two ring slots at least");
+  static_assert(kWgsPerCu * (LDS + 1024) <= 160 * 1024, "the workgroups of a CU fit its LDS");
 };
 
-template <int KT, int VT, int D, int NQ>
-__global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_lds_kernel(const ChunkArgs a) {
-  using KF = KFmt<KT, D>;
-  using VF = VFmt<VT, D>;
-  using WR = WinRing<KT, VT, D, NQ>;
+// WH = 1: wave w serves kv head 4*hg + w with the whole head dimension.
+// WH = 2 (D = 256 with two column groups, where one wave's registers cannot
+// hold the Q operands and accumulators of 32 rows at two waves per SIMD): a
+// workgroup takes a pair of kv heads, waves w and w + 2 serving kv head
+// 2*hg + w, wave w + 2h taking head-dimension positions [128h, 128h + 128). A
+// D = 256 row of every format is two D = 128 rows back to back, so each wave
+// runs the D = 128 operand formats on its half of the row. The two halves'
+// partial scores meet through LDS once per step (both waves add them in the
+// same order and so hold the same scores, softmax state and p); each wave
+// then accumulates its half of the output columns.
+template <int KT, int VT, int D, int NQ, int WH>
+__global__ void __launch_bounds__(256, chunk_window_wgs_per_cu(NQ, D)) chunk_lds_kernel(const ChunkArgs a) {
+  static_assert(WH == 1 || (WH == 2 && D == 256), "the head dimension splits in two at D = 256 only");
+  constexpr int kThreads = 256;
+  constexpr int kWaves = 4;
+  constexpr int NH = WinRing<KT, VT, D, NQ, WH>::NH;
+  constexpr int DH = D / WH;     // head-dimension positions of a wave
+  constexpr int kIdRegs = (kNidS + 1 + kThreads - 1) / kThreads;   // ids a thread fetches
+  using KF = KFmt<KT, DH>;
+  using VF = VFmt<VT, DH>;
+  using WR = WinRing<KT, VT, D, NQ, WH>;
   using LY = typename WR::LY;
   constexpr int RS = WR::R;      // ring slots
-  constexpr int S = D / 32;      // score MFMA steps
-  constexpr int E = D / 16;      // PV d-tiles
+  constexpr int S = DH / 32;     // score MFMA steps
+  constexpr int E = DH / 16;     // PV d-tiles
   constexpr int G = LY::G;       // 16-row groups per step
   constexpr int T = 16 * G;      // tokens per step
   constexpr int NP = 2 * G;      // V row pairs per lane (4 rows per group)
+  constexpr int NIW = (LY::NI + kWaves - 1) / kWaves;   // DMA instructions per wave and step, at most
   constexpr bool kKFold = KT == kQ4_0;   // Q4_0 offsets folded into corrections
   constexpr bool kVFold = VT == kQ4_0;
-  constexpr int KF_NBL = kKFold ? D / 128 : 1;   // ggml blocks per K lane window
+  constexpr int KF_NBL = kKFold ? DH / 128 : 1;  // ggml blocks per K lane window
 
   unsigned char* const ring = g_lds;
   int32_t* ids = reinterpret_cast<int32_t*>(g_lds + WR::BYTES);
+  f32x4* xbuf = reinterpret_cast<f32x4*>(g_lds + WR::BYTES + kIdsBytes);   // WH = 2
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int hw = wave & (NH - 1);                             // kv head within the workgroup's
+  const int hf = wave / NH;                                   // half of the head dimension
   const int m = lane & 15;
   const int j = lane >> 4;
   const int R = a.Tq * a.r;                      // query rows per kv head (<= 16*NQ)
-  const int HG = a.Hkv / 4;
+  const int HG = a.Hkv / NH;
   const int n_units = a.B * a.p_max * HG;
   const int Gd = gridDim.x;
   const int logical = xcd_logical(blockIdx.x, Gd);
 
-  const int cw = (LY::NI - wave + 3) / 4;              // DMA instructions this wave issues per step
+  const int cw = (LY::NI - wave + kWaves - 1) / kWaves;   // DMA instructions this wave issues per step
   // LDS offsets (within a group) of the rows this lane reads: K row m, V rows
-  // 4j+i, of the wave's head, at their rotated row positions
-  const int k_row = m * LY::SPK + ((wave + RowRot<LY::RBK>::k(m)) & 3) * LY::RBK + int(KF::lane_off(j));
+  // 4j+i, of the wave's head, at their rotated row positions (and the wave's
+  // half of each row)
+  constexpr int kHalfK = row_bytes_of(KT, DH), kHalfV = row_bytes_of(VT, DH);
+  const int k_row = m * LY::SPK + ((hw + RowRot<LY::RBK, NH>::k(m)) & (NH - 1)) * LY::RBK + hf * kHalfK +
+                    int(KF::lane_off(j));
   int v_row[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    v_row[i] = (4 * j + i) * LY::SPV + ((wave + RowRot<LY::RBV>::v(4 * j + i)) & 3) * LY::RBV;
+    v_row[i] = (4 * j + i) * LY::SPV + ((hw + RowRot<LY::RBV, NH>::v(4 * j + i)) & (NH - 1)) * LY::RBV +
+               hf * kHalfV;
   const uint32_t kstride = uint32_t(a.Hkv) * LY::RBK;  // pool bytes between token slots
   const uint32_t vstride = uint32_t(a.Hkv) * LY::RBV;
   const uint32_t ksh = KF::shift(j);
@@ -108,7 +158,7 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
       L = 0;
     }
     L = __builtin_amdgcn_readfirstlane(L);
-    const int g = 4 * hg + wave;                        // this wave's kv head
+    const int g = NH * hg + hw;                         // this wave's kv head
     const int P = L > 0 ? (L + a.psize - 1) / a.psize : 0;
     const int t_begin = p * a.psize;
     const int t_end = min(L, t_begin + a.psize);
@@ -136,7 +186,7 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
           if (valid[k])
-            for (int d = 0; d < D; ++d) a.out[orow[k] * D + d] = 0.0f;
+            for (int d = hf * DH; d < hf * DH + DH; ++d) a.out[orow[k] * D + d] = 0.0f;
       }
       continue;
     }
@@ -145,19 +195,19 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
     for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
     lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
-    const uint32_t khead = uint32_t(4 * hg) * LY::RBK;  // first head's offset in a slot
-    const uint32_t vhead = uint32_t(4 * hg) * LY::RBV;
-    // this lane's pool offset in each DMA instruction q = wave + 4i of a step
-    uint32_t dvoff[LY::NIW];
+    const uint32_t khead = uint32_t(NH * hg) * LY::RBK;   // first head's offset in a slot
+    const uint32_t vhead = uint32_t(NH * hg) * LY::RBV;
+    // this lane's pool offset in each DMA instruction q = wave + kWaves*i of a step
+    uint32_t dvoff[NIW];
 #pragma unroll
-    for (int i = 0; i < LY::NIW; ++i) {
-      const int q = wave + 4 * i;
+    for (int i = 0; i < NIW; ++i) {
+      const int q = wave + kWaves * i;
       if (q < G * LY::NIK)
-        dvoff[i] = chunk_voff<LY::CPK, LY::RBK>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
-                                                 RowRot<LY::RBK>::k);
+        dvoff[i] = chunk_voff<LY::CPK, LY::RBK, 16, NH>(q % LY::NIK, lane, kstride, khead, 16u * kstride,
+                                                         RowRot<LY::RBK, NH>::k);
       else
-        dvoff[i] = chunk_voff<LY::CPV, LY::RBV>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
-                                                 16u * vstride, RowRot<LY::RBV>::v);
+        dvoff[i] = chunk_voff<LY::CPV, LY::RBV, 16, NH>((q - G * LY::NIK) % LY::NIV, lane, vstride, vhead,
+                                                         16u * vstride, RowRot<LY::RBV, NH>::v);
     }
 
     // ---- the first segment's block ids and the first column group's q
@@ -172,11 +222,8 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
     for (int k = 0; k < kIdRegs; ++k)
       idr[k] = block_of(a.table, b, a.max_blocks, jb0 + min(tid + k * kThreads, nb - 1));
     auto load_q = [&](int k, float (&qv)[S][8]) __attribute__((always_inline)) {
-      const float* qw = a.q + (valid[k] ? orow[k] : orow[0]) * D;   // a dead column reads a live row
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[s][i] = qw[KF::dslot(j, s, i)];
+      // a dead column reads a live row; q is 16-byte aligned on this path
+      load_q_slots<KF, S>(a.q + (valid[k] ? orow[k] : orow[0]) * D + hf * DH, j, qv);
     };
     float qv[S][8];
     load_q(0, qv);
@@ -218,7 +265,7 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           // Q4_0: the high-nibble slots meet K values in the x16 frame
-          const float hs = (kKFold && KFmtHi<KT, D>::hi(i)) ? 0.0625f : 1.0f;
+          const float hs = (kKFold && KFmtHi<KT, DH>::hi(i)) ? 0.0625f : 1.0f;
           qop[k][s][i] = f16(qv[s][i] * keep * hs);
         }
 #pragma unroll
@@ -227,7 +274,7 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
 #pragma unroll
         for (int s2 = 4 * bl; s2 < 4 * bl + 4; ++s2)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) qsum += float(qop[k][s2][i]) * (KFmtHi<KT, D>::hi(i) ? 16.0f : 1.0f);
+          for (int i = 0; i < 8; ++i) qsum += float(qop[k][s2][i]) * (KFmtHi<KT, DH>::hi(i) ? 16.0f : 1.0f);
         kcorr[k][bl] = -8.0f * qsum;
       }
     }
@@ -352,6 +399,22 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
         for (int k = 0; k < NQ; ++k) {
           if constexpr (G == 1) mfma_settle(sc[k][0]);
           else mfma_settle(sc[k][0], sc[k][1]);
+        }
+        if constexpr (WH == 2) {
+          // the two halves' partial scores: publish, barrier, add the other's
+          // (a + b = b + a exactly, so both waves hold the same sums); the
+          // next step's ring barrier keeps the buffer until both have read it
+          f32x4* mine = xbuf + wave * (NQ * G * 64) + lane;
+#pragma unroll
+          for (int k = 0; k < NQ; ++k)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) mine[(k * G + gi) * 64] = sc[k][gi];
+          lds_barrier();
+          const f32x4* other = xbuf + (wave ^ NH) * (NQ * G * 64) + lane;
+#pragma unroll
+          for (int k = 0; k < NQ; ++k)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) sc[k][gi] += other[(k * G + gi) * 64];
         }
         // causal and end-of-partition mask, only where some row's limit falls
         // inside the step (lim <= t_end - 1 covers the slots past the end)
@@ -497,7 +560,7 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
         const float f = __builtin_ldexpf(1.0f, vshift);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float fe = VFmtHi<VT, D>::hi(e) ? f * 0.0625f : f;
+          const float fe = VFmtHi<VT, DH>::hi(e) ? f * 0.0625f : f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[k][e][i] = acc[k][e][i] * fe - 8.0f * vcorr[k][i];
         }
@@ -505,15 +568,15 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
       if (!valid[k]) continue;
       const float inv = bad ? __builtin_nanf("") : (l_run > 0.0f ? 1.0f / l_run : 0.0f);
       if (a.direct) {
-        float* dst = a.out + orow[k] * D;
+        float* dst = a.out + orow[k] * D + hf * DH;
 #pragma unroll
         for (int e = 0; e < E; ++e)
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[VF::dv(4 * j + i, e)] = acc[k][e][i] * inv;
       } else {
         const int64_t prow = orow[k] * a.p_max + p;
-        f16* dst = reinterpret_cast<f16*>(a.part_o) + prow * D;
-        if (j == 0) {
+        f16* dst = reinterpret_cast<f16*>(a.part_o) + prow * D + hf * DH;
+        if (j == 0 && hf == 0) {
           a.part_ml[2 * prow] = bad ? __builtin_nanf("") : (l_run > 0.0f ? m_run[k] : -INFINITY);
           a.part_ml[2 * prow + 1] = l_run;
         }
@@ -527,14 +590,14 @@ __global__ void __launch_bounds__(kThreads, chunk_window_wgs_per_cu(NQ)) chunk_l
   }
 }
 
-template <int KT, int VT, int D, int NQ>
+template <int KT, int VT, int D, int NQ, int WH = 1>
 hipError_t launch_nq(const ChunkArgs& a, hipStream_t stream) {
-  constexpr size_t lds = size_t(WinRing<KT, VT, D, NQ>::BYTES) + 4 * size_t((kNidS + 1 + 3) & ~3);
+  constexpr size_t lds = size_t(WinRing<KT, VT, D, NQ, WH>::LDS);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&chunk_lds_kernel<KT, VT, D, NQ>),
+      reinterpret_cast<const void*>(&chunk_lds_kernel<KT, VT, D, NQ, WH>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((chunk_lds_kernel<KT, VT, D, NQ>), dim3(a.grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((chunk_lds_kernel<KT, VT, D, NQ, WH>), dim3(a.grid), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -545,7 +608,7 @@ hipError_t launch_typed(const ChunkArgs& a, hipStream_t stream) {
   } else {
     const int nq = (a.Tq * a.r + 15) / 16;
     if (nq == 1) return launch_nq<KT, VT, D, 1>(a, stream);
-    if (nq == 2) return launch_nq<KT, VT, D, 2>(a, stream);
+    if (nq == 2) return launch_nq<KT, VT, D, 2, chunk_window_split(2, D)>(a, stream);
     if constexpr (D == 128) {
       if (nq == 3) return launch_nq<KT, VT, D, 3>(a, stream);
     }
@@ -572,7 +635,7 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_lds(const ChunkArgs& a, hipStream_t stream) {
-  if (a.Hkv % 4) return hipErrorInvalidValue;
+  if (a.Hkv % 4) return hipErrorInvalidValue;   // (pairs of heads too: the plan counts units by quads or pairs)
   if (a.D == 256) return launch_d<256>(a, stream);
   if (a.D == 128) return launch_d<128>(a, stream);
   return hipErrorInvalidValue;

@@ -96,8 +96,8 @@ constexpr int lds_ring_slots(int kt, int vt, int D) {
 // side at D = 256: 32 KB of K or V per group of four heads): its steps are
 // then one group of 8 slots, still computed as 16-row MFMA tiles whose last
 // 8 rows are masked. 1 KB DMA instructions for GS slots x 4 heads of a side:
-constexpr int lds_dma_per_slots(int type, int D, int GS) {
-  return (GS * 4 * lds_row_bytes(type, D) + 1023) / 1024;
+constexpr int lds_dma_per_slots(int type, int D, int GS, int NH = 4) {
+  return (GS * NH * lds_row_bytes(type, D) + 1023) / 1024;
 }
 // Slots per group of the decode kernel: 16 where lds_groups() admits the
 // shape, else 8 when a two-slot ring of 8-slot steps fits, else 0.
@@ -126,10 +126,19 @@ struct ChunkArgs {
   float qscale;            // scale * log2(e)
   int32_t nt;              // 16-row query tiles per wave (chunk_wave_tiles)
 };
-// Workgroups per CU of the window chunk kernel with NQ column groups of 16
-// query rows: two when one group fits (the decode kernel's register and LDS
-// budget), else one.
-constexpr int chunk_window_wgs_per_cu(int nq) { return nq == 1 ? 2 : 1; }
+// Waves per kv head of the window kernel with NQ column groups of 16 query
+// rows: 2 (each half of the head dimension) for two column groups at
+// D = 256, else 1.
+constexpr int chunk_window_split(int nq, int D) { return nq == 2 && D == 256 ? 2 : 1; }
+// kv heads per workgroup of the window kernel: a pair with two waves per
+// head, else a quad.
+constexpr int chunk_window_heads(int nq, int D) { return chunk_window_split(nq, D) == 2 ? 2 : 4; }
+// Workgroups per CU of the window kernel: two when one column group fits
+// (the decode kernel's register and LDS budget) or the head dimension is
+// split, else one.
+constexpr int chunk_window_wgs_per_cu(int nq, int D) {
+  return nq == 1 || chunk_window_split(nq, D) == 2 ? 2 : 1;
+}
 // Whether the window kernel takes a chunk with `rows` query rows per kv head
 // (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
 // registers hold with their accumulators; Hkv % 4 == 0; the shapes

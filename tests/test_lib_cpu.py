@@ -343,13 +343,15 @@ def test_chunk_plan_partitions_and_workspace():
 def test_chunk_plan_kernel_choice():
     """The window kernel (path 2) for at most 32 query rows per kv head at
     D=256 (48 at D=128): a workgroup per (sequence, partition, kv-head quad),
-    two per compute unit for at most 16 rows, else one; the tile-conversion
-    kernel (path 1) otherwise. A plan forced to path 2 where it does not apply
-    is refused before launch."""
+    two per compute unit for at most 16 rows, else one, except 17..32 rows at
+    D=256, where the head dimension is split over two waves and a workgroup
+    takes a kv-head pair, two per compute unit; the tile-conversion kernel
+    (path 1) otherwise. A plan forced to path 2 where it does not apply is
+    refused before launch."""
     p = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.path == 1                                   # 48 rows at D=256
     w = pa.paged_attn_chunk_plan(_shape(), 4, 32768, total_tokens=8 * 32768, num_cus=256)
-    assert w.path == 2 and w.grid == min(8 * w.p_max * 1, 256)     # 24 rows
+    assert w.path == 2 and w.grid == min(8 * w.p_max * 2, 512)     # 24 rows: kv-head pairs
     w2 = pa.paged_attn_chunk_plan(_shape(), 2, 32768, total_tokens=8 * 32768, num_cus=256)
     assert w2.path == 2 and w2.grid == min(8 * w2.p_max * 1, 512)  # 12 rows
     w128 = pa.paged_attn_chunk_plan(_shape(D=128), 8, 32768, total_tokens=8 * 32768, num_cus=256)
