@@ -511,8 +511,8 @@ def run_chunk(args):
 
 
 def run_metadata(args):
-    """Paging-metadata maintenance (lucebox PR #555, Summary: 4 bytes per fresh
-    block instead of the whole table; Roadmap item 6: copy-on-write). Prints
+    """Paging-metadata maintenance (lucebox PR #555, Summary: only new blocks'
+    ids are sent, not the table; Roadmap item 6: copy-on-write). Prints
     one JSON line:
       * table: paged_table_update of one fresh block per sequence plus its
         seq_len (the per-step upload at B=8, 16-token blocks, 128K-token

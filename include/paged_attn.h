@@ -7,8 +7,8 @@
  * token per sequence, Hq query heads sharing Hkv K/V heads, K/V rows reached
  * through a per-sequence table of fixed-size blocks, F16, Q8_0 or Q4_0 K and V
  * (chosen independently), the context of each sequence split into partitions
- * whose partial results are recombined by a numerically stable split-softmax
- * merge. For each sequence b and query head h, with r = Hq/Hkv, kv head
+ * whose partial results are recombined by a max-shifted merge of their
+ * softmax sums. For each sequence b and query head h, with r = Hq/Hkv, kv head
  * g = h / r and L = seq_len[b]:
  *
  *     out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K[b,g,t,:]) V[b,g,t,:]
@@ -28,9 +28,10 @@
  *     refused launch reports the entry point instead of computing garbage).
  *   - Pools are addressed with 64-bit byte offsets everywhere, so a pool side
  *     may hold more than 2^32 elements (mlxcel issue #2153, Problem and
- *     Proposed Solution: the offset (row*block_size + slot)*stride +
- *     kv_head*dim is widened before multiplying; a pool of exactly 2^32
- *     elements addresses its last element). There is no size refusal for
+ *     Proposed Solution: a row's offset, block id times block size plus
+ *     slot, times the token stride, plus the head's offset, is formed in
+ *     64-bit arithmetic before any product; a pool of exactly 2^32 elements
+ *     addresses its last element). There is no size refusal for
  *     large pools.
  *
  * Layouts (row-major, little endian)
@@ -131,8 +132,8 @@ typedef struct pa_plan {
                            merges the partials (its last workgroups to finish
                            take the merge slices once their partitions are in,
                            counted by atomic completion counters in ws:
-                           llama.cpp PR #13 HRX, Changes: the reduction inside
-                           the same self-synchronising launch; lucebox PR #555,
+                           llama.cpp PR #13 HRX, Changes: the partials reduced
+                           by the decode launch itself; lucebox PR #555,
                            Roadmap item 4) and paged_attn_merge is a no-op.
                            Allowed on path 2 when not direct and the merge is
                            of the wide layout (not the row-per-thread one).
@@ -219,8 +220,9 @@ int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t tota
  * Computes, for every live (sequence, K/V head, partition), the partial
  * softmax statistics and normalised partial output of all r query heads of the
  * group from one pass over the partition's K/V rows (lucebox PR #555, Summary:
- * all GQA heads of a K/V group per K/V row loaded, exp2 softmax, partials
- * stored normalised; mlxcel issue #2153: 64-bit pool offsets). In direct mode
+ * each K/V row read once serves every query head that shares it, base-2
+ * softmax, partials kept normalised; mlxcel issue #2153: 64-bit pool
+ * offsets). In direct mode
  * writes out[] instead of partials.
  *   q, k_pool, v_pool, seq_len, out: as in the layout table above
  *   block_table  NULL selects the contiguous layout: sequence b's logical
@@ -240,7 +242,7 @@ int32_t paged_attn_decode(const pa_plan* plan, const float* q, const void* k_poo
                           void* stream);
 
 /*
- * paged_attn_merge - stable split-softmax merge of the partials in ws.
+ * paged_attn_merge - max-shifted merge of the partition partials in ws.
  *
  * For each (b, h) over its live partitions p < ceil(seq_len[b]/psize):
  *   M = max_p m_p;  w_p = 2^(m_p - M) * l_p;  out = sum_p w_p o_p / sum_p w_p
@@ -326,7 +328,7 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * gives zero rows; 0 < L < Tq also gives zero rows and sets
  * PA_STATUS_BAD_SEQ_LEN. The key range is cut into partitions whose
  * partials (the decode layout with Tq*Hq rows per sequence) are reduced by
- * the same stable split-softmax merge; one partition writes out directly.
+ * the same max-shifted merge; one partition writes out directly.
  * Two kernels compute it: path 1 converts each key/value tile once per
  * workgroup into LDS for four waves of query rows (any Tq); path 2, for
  * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128) with Hkv
@@ -369,9 +371,9 @@ int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, const void* 
 
 /*
  * paged_table_update - write a few entries of the device-resident block table
- * and seq_len (lucebox PR #555, Summary: the paging metadata stays resident on
- * the device next to the pool, and a decode step uploads 4 bytes per fresh
- * 16-token block instead of the whole live table).
+ * and seq_len (lucebox PR #555, Summary: the table and lengths live on the
+ * device beside the pool, so a step sends only the ids of newly allocated
+ * blocks rather than re-sending the table).
  *   table       device int32 [B][max_blocks]; seq_len device int32 [B]
  *   updates     HOST int32 [n][3] triples (b, slot, value): slot >= 0 sets
  *               table[b][slot] = value, slot == -1 sets seq_len[b] = value.
@@ -407,9 +409,10 @@ int32_t paged_kv_copy_blocks(void* pool, uint64_t block_bytes, int32_t nblocks,
 
 /*
  * Fixed-block allocator over the block ids [0, nblocks) of a caller-owned
- * pool (lucebox PR #555, Summary and Validation: exact fixed-block allocator,
- * transactional allocation, stale-handle detection, immediate release, pool
- * reset across requests). Host only; thread-safe per pool object.
+ * pool (lucebox PR #555, Summary and Validation: an allocation either gets all
+ * of its blocks or none, a freed or reset handle is refused when used again,
+ * blocks return to the pool at once, and the pool resets between requests).
+ * Host only; thread-safe per pool object.
  *
  * An allocation is a list of block ids, in the order they were handed out,
  * named by a 64-bit handle (slot index and generation; 0 is never a valid

@@ -20,15 +20,16 @@ float64 with no blocking, fusion or reordering:
 
 Sources (page titles and sections):
   * lucebox PR #555 "paged-attention monolithic decode-only AR foundation",
-    Summary: decode-only paged attention over a fixed-block K/V pool, D=256 GQA,
-    F16/Q4_0/Q8_0 K/V, all GQA heads of a K/V group, split-softmax merge;
-    Validation: a float64 oracle in partitioned and direct modes, empty
-    sequences, page boundaries, shuffled blocks, bounds guards on corrupt
-    block tables.
+    Summary: single-query paged attention over a pool of fixed-size blocks,
+    D=256 with grouped query heads, K/V stored as F16, Q4_0 or Q8_0, one pass
+    over a K/V row serving every query head that shares it, partitions
+    recombined by a max-shifted merge; Validation: checked against a float64
+    reference with and without partitions, on zero-length sequences, block
+    edges, permuted block order and tables with out-of-range entries.
   * mlxcel issue #2153 "use 64-bit pool offsets in the fused decode kernels",
-    Current Behavior and Proposed Solution: the pool offset
-    (row*block_size + slot)*stride + kv_head*dim, widened to 64 bits before
-    multiplying; Scope: the gather path (gather through the table, then dense
+    Current Behavior and Proposed Solution: a row's pool offset (block id
+    times block size plus slot, times the token stride, plus the head's
+    offset) must be formed in 64-bit arithmetic before any product; Scope: the gather path (gather through the table, then dense
     attention) is the reference the fused kernels are checked against.
   * TensorFold PR #1418, Kernel contract: a float64 attention reference and
     shuffled pages with spare junk pages.

@@ -6,9 +6,9 @@ with it.
 
 Sources (page titles and sections):
   * lucebox PR #555 "paged-attention monolithic decode-only AR foundation",
-    Summary: the block table and sequence lengths stay resident on the device
-    next to the K/V pool; a decode step uploads only the entries of fresh
-    blocks (4 bytes each) instead of the whole live table.
+    Summary: the table and lengths live on the device beside the pool, so a
+    step sends only the ids of newly allocated blocks rather than re-sending
+    the table.
   * the same page, Roadmap item 6: prefix caching, where blocks of a common
     prefix are shared under reference counts and copied before a write.
 

@@ -31,9 +31,9 @@
 //   * No cross-wave combine: a wave owns all tokens of its head group, so it
 //     writes its partial (or output) rows directly.
 //   * Single launch (plan->fused): the merge runs in the same launch (the
-//     llama.cpp PR #13 HRX page, Changes: the reduction inside the same
-//     self-synchronising launch with an atomic completion counter, no second
-//     dispatch). Workgroups claim items from a counter in the workspace:
+//     llama.cpp PR #13 HRX page, Changes: the partials reduced by the decode
+//     launch itself, ordered by an atomic count of finished work, with no
+//     second dispatch). Workgroups claim items from a counter in the workspace:
 //     every decode unit; a workgroup whose claim comes after the last unit
 //     turns to its share of the merge slices (a query-head row and 64 output
 //     columns, the separate merge's workgroup, same code). A unit stores its

@@ -1,9 +1,9 @@
-// Stable split-softmax merge of partition partials.
+// Max-shifted merge of the partitions' softmax partials.
 //
 // For each (sequence b, query head h) over its live partitions
 // p < ceil(seq_len[b]/psize), with per-partition base-2 reference m_p, sum
 // l_p and normalised output o_p (lucebox PR #555, Summary: partials stored
-// normalised in f16, stable split-softmax merge; llama.cpp PR #13 HRX,
+// normalised in f16, merged across partitions without overflow; llama.cpp PR #13 HRX,
 // Changes: per-block normalisation scale):
 //     M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p
 // The rows are (b, h) for decode and (b, t, h) for chunks (Hq then counts

@@ -7,8 +7,8 @@
 //     allocator; the shared block's bytes are copied there first.
 //   * table_update_kernel: scatters a few (sequence, slot, value) entries
 //     into the device-resident block table and seq_len (lucebox PR #555,
-//     Summary: paging metadata stays resident next to the pool and a decode
-//     step uploads 4 bytes per fresh 16-token block, not the whole table).
+//     Summary: the table and lengths live on the device beside the pool, so
+//     a step sends only the ids of newly allocated blocks).
 //
 // Both take their short lists by value in the kernel arguments: the host
 // validated them, nothing is allocated or copied beforehand, and the call

@@ -12,7 +12,7 @@ seconds). Randomness comes from explicitly seeded torch.Generator objects.
 Workload facts used here (all from the lucebox PR #555 page, "Benchmark
 results" and "K/V capacity" sections, and the mlxcel issue #2153 page,
 "Problem / Background"):
-  * Qwen attention dims D=256, Hq=24, Hkv=4 with 16-token blocks;
+  * the pages' model attention shape: D=256, Hq=24, Hkv=4, blocks of 16 tokens;
   * K/V in F16, Q8_0 or Q4_0, K and V types independent;
   * ragged batches 128K + 7x8K with the blocks of all sequences interleaved
     randomly in one pool;

@@ -1,7 +1,7 @@
 """The single-launch decode (plan.fused: the LDS-staged kernel also merges,
 its workgroups claiming decode units and then merge slices from a counter in
-the workspace; llama.cpp PR #13 HRX, Changes: the reduction inside the same
-self-synchronising launch; lucebox PR #555, Roadmap item 4) against the
+the workspace; llama.cpp PR #13 HRX, Changes: the partials reduced by the
+decode launch itself; lucebox PR #555, Roadmap item 4) against the
 two-launch step (decode, then the merge kernel) on the same plan: the same
 bits, always. Also: the workspace counters are zero after every call, a
 counter left non-zero is detected (status bit, NaN columns) and cleared, and

@@ -1,9 +1,9 @@
 """The library's host C++ under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 api.cpp (planner, argument checks, error messages, the packing of launch
-arguments) and kv_pool.cpp (the block allocator: transactional allocation,
-stale-handle detection, prefix sharing; lucebox PR #555, Summary and
-Validation) are compiled with g++ -fsanitize=address,undefined into a
+arguments) and kv_pool.cpp (the block allocator: all-or-nothing
+allocation, refusal of freed handles, prefix sharing; lucebox PR #555, Summary
+and Validation) are compiled with g++ -fsanitize=address,undefined into a
 host-only build of the same C ABI, whose kernel launchers all refuse
 (tests/host/launch_stubs.cpp). The library's CPU suites - the allocator's
 model-based fuzz, the planner and refusal tests - and the calls that reach a
