@@ -337,8 +337,8 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * D = 256 with 17..32 rows, two waves per kv head, each over half of the head
  * dimension, adding their partial scores through LDS). The
  * plan picks path 2 where it applies; a caller may set path = 1 on such a
- * plan to force the general kernel. Pools that are not 16-byte aligned run
- * path 1.
+ * plan to force the general kernel. Pools or q that are not 16-byte aligned
+ * run path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;
