@@ -257,6 +257,30 @@ def test_unaligned_pools_run_the_tile_kernel():
     _check(c, qc, outs[0])
 
 
+def test_unaligned_q_runs_the_tile_kernel():
+    """A q that is not 16-byte aligned runs the tile-conversion kernel even
+    under a window plan (whose kernel reads q with 16-byte loads): the result
+    equals a path-1 run bit for bit."""
+    c, qc = _case([500, 77], 4, seed=237, k_fmt="q4_0", v_fmt="q4_0")
+    g = c.to(DEV)
+    raw = torch.empty(qc.numel() + 1, dtype=torch.float32, device=DEV)
+    qu = raw[1:].view(qc.shape)
+    qu.copy_(qc.to(DEV))
+    assert qu.data_ptr() % 16 == 4
+    plan2 = _plan(c, 4, path=2, partition_tokens=128)
+    plan1 = _plan(c, 4, path=1, partition_tokens=128)
+    pa = pa_mod()
+    outs = []
+    for plan, q in ((plan2, qu), (plan1, qc.to(DEV))):
+        ws = pa.workspace(plan, DEV)
+        out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
+        pa.paged_attn_chunk(plan, q, g.k_pool, g.v_pool, g.table, g.seq_len, ws, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    _check(c, qc, outs[0])
+
+
 @pytest.mark.parametrize("Tq", [2, 4, 8])
 def test_verify_windows_at_full_size(Tq):
     """Verify windows of 2, 4 and 8 tokens over Q4_0 K/V, B=8 x 32768 tokens

@@ -85,6 +85,25 @@ def test_unaligned_pools_fall_back_to_the_register_kernel():
     check_parity(case, out_u)
 
 
+def test_unaligned_q_falls_back_to_the_register_kernel():
+    """A q that is not 16-byte aligned (the LDS-staged kernel reads it with
+    16-byte loads) is decoded by the register kernel even under a path-2
+    plan: the result equals a path-1 run bit for bit."""
+    case = _case([500, 77], k_fmt="q4_0", v_fmt="q8_0", seed=229)
+    g = case.to(DEV)
+    gu = case.to(DEV)
+    raw = torch.empty(g.q.numel() + 1, dtype=torch.float32, device=DEV)
+    gu.q = raw[1:].view(g.q.shape)
+    gu.q.copy_(g.q)
+    assert gu.q.data_ptr() % 16 == 4
+    plan2 = plan_for(case, path=2, force_partitions=3)
+    plan1 = plan_for(case, path=1, force_partitions=3)
+    out_u, _ = run(gu, plan2)
+    out_1, _ = run(g, plan1)
+    assert torch.equal(out_u, out_1)
+    check_parity(case, out_u)
+
+
 def test_both_kernels_agree_within_tolerance():
     """Same inputs, same partitioning: the two kernels differ only in the
     order of fp32 accumulation."""
