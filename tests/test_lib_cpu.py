@@ -384,3 +384,19 @@ def test_chunk_refusals_before_any_launch():
         pa.paged_attn_chunk(p, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
                             stream=0, ws_bytes=int(p.ws_bytes) - 1)
     assert e.value.code == pa.PA_ERR_INVALID and "workspace" in str(e.value)
+
+
+def test_smoke_cases_take_the_kernels_smoke_expects():
+    """__graft_entry__.smoke() checks that each of its decode cases is planned
+    on a given kernel; the planner (host code) must agree, for every
+    partitioning smoke runs."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_graft_entry", os.path.join(ROOT, "__graft_entry__.py"))
+    ge = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(ge)
+    for label, case, _, path in ge.smoke_cases():
+        shape = pa.shape_of(case.B, case.Hq, case.Hkv, case.D, case.block_size, case.nblocks,
+                            case.max_blocks, case.k_fmt, case.v_fmt)
+        for force in (0, 1, 3):
+            plan = pa.paged_attn_plan(shape, max(case.seq_lens), num_cus=256, force_partitions=force)
+            assert plan.path == path, (label, force, plan.path)
