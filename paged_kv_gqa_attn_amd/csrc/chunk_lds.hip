@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(256, chunk_window_wgs_per_cu(NQ, D)) chunk_lds
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int hw = wave & (NH - 1);                             // kv head within the workgroup's
+  const int hw = wave & (NH - 1);                             // the wave's kv head within the quad or pair
   const int hf = wave / NH;                                   // half of the head dimension
   const int m = lane & 15;
   const int j = lane >> 4;
