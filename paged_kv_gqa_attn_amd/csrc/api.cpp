@@ -511,7 +511,8 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   const int64_t qt = window ? 1 : (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // row blocks per unit
   const int nq = int(ceil_div(int64_t(tq) * r, 16));
   const int64_t heads_per_unit = window ? chunk_window_heads(nq, s.D) : 1;
-  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D) : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
+  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D, s.k_type, s.v_type)
+                                : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {

@@ -18,9 +18,11 @@
 // wave converts the K and V rows it reads from LDS once into MFMA operands
 // used for all of its NQ column groups. Two shapes of workgroup:
 //  * a quad of kv heads, wave w serving head 4*hg + w over the whole head
-//    dimension (one column group: two workgroups per CU, as in decode; two or
-//    three at D = 128: one workgroup per CU, whose registers hold the
-//    NQ*D/16 accumulator tiles and NQ*D/32 Q operands);
+//    dimension (one column group: two workgroups per CU, as in decode; two
+//    at D = 128 with K or V quantised: two per CU as well (Q4_0 B=8 x 32K,
+//    Tq=8 at r=4: 145 -> 94 us per step against one); otherwise one
+//    workgroup per CU, whose registers hold the NQ*D/16 accumulator tiles
+//    and NQ*D/32 Q operands);
 //  * two column groups at D = 256, where those are 64 + 128 registers and one
 //    wave per SIMD leaves the step latency-bound: a pair of kv heads, two
 //    waves per head, each taking half of the head dimension (its Q operands,
@@ -43,11 +45,10 @@ namespace {
 constexpr int kNidS = 512;     // block ids staged per segment of a partition
 constexpr int kIdsBytes = 4 * ((kNidS + 1 + 3) & ~3);
 
-// The ring of this kernel. WH = 1 (a quad of kv heads, one wave each): with
-// one column group (at most 16 query rows per kv head) the registers fit two
-// workgroups per CU, and the ring is the decode kernel's; otherwise one
-// workgroup per CU holds the registers of two and may use twice the decode
-// kernel's LDS. WH = 2 (a pair of kv heads, two waves each): two workgroups
+// The ring of this kernel. WH = 1 (a quad of kv heads, one wave each): where
+// the registers fit two workgroups per CU (chunk_window_wgs_per_cu) the ring
+// is the decode kernel's; otherwise one workgroup per CU holds the registers
+// of two and may use twice the decode kernel's LDS. WH = 2 (a pair of kv heads, two waves each): two workgroups
 // per CU, each with 80 KB of LDS for the ring, the block ids and XBYTES for
 // the partial scores the waves exchange; steps of two 16-slot groups where
 // that leaves two ring slots, else one.
@@ -55,7 +56,7 @@ template <int KT, int VT, int D, int NQ, int WH>
 struct WinRing {
   static_assert(WH == chunk_window_split(NQ, D), "the split the plan counts units by");
   static constexpr int NH = WH == 2 ? 2 : 4;           // kv heads per workgroup
-  static constexpr int kWgsPerCu = chunk_window_wgs_per_cu(NQ, D);
+  static constexpr int kWgsPerCu = chunk_window_wgs_per_cu(NQ, D, KT, VT);
   static constexpr int xbytes(int g) { return WH == 2 ? 4 * NQ * g * 64 * 16 : 0; }
   static constexpr int slot(int g) {
     return g * 1024 * (lds_dma_per_slots(KT, D, 16, NH) + lds_dma_per_slots(VT, D, 16, NH));
@@ -84,7 +85,7 @@ struct WinRing {
 // same order and so hold the same scores, softmax state and p); each wave
 // then accumulates its half of the output columns.
 template <int KT, int VT, int D, int NQ, int WH>
-__global__ void __launch_bounds__(256, chunk_window_wgs_per_cu(NQ, D)) chunk_lds_kernel(const ChunkArgs a) {
+__global__ void __launch_bounds__(256, chunk_window_wgs_per_cu(NQ, D, KT, VT)) chunk_lds_kernel(const ChunkArgs a) {
   static_assert(WH == 1 || (WH == 2 && D == 256), "the head dimension splits in two at D = 256 only");
   constexpr int kThreads = 256;
   constexpr int kWaves = 4;

@@ -134,10 +134,15 @@ constexpr int chunk_window_split(int nq, int D) { return nq == 2 && D == 256 ? 2
 // head, else a quad.
 constexpr int chunk_window_heads(int nq, int D) { return chunk_window_split(nq, D) == 2 ? 2 : 4; }
 // Workgroups per CU of the window kernel: two when one column group fits
-// (the decode kernel's register and LDS budget) or the head dimension is
-// split, else one.
-constexpr int chunk_window_wgs_per_cu(int nq, int D) {
-  return nq == 1 || chunk_window_split(nq, D) == 2 ? 2 : 1;
+// (the decode kernel's register and LDS budget), for two groups at D = 128
+// where K or V is quantised (their registers fit twice; F16/F16 there is
+// HBM-bound either way and keeps the larger ring of one per CU), or when the
+// head dimension is split; else one.
+constexpr int chunk_window_wgs_per_cu(int nq, int D, int kt, int vt) {
+  return nq == 1 || (nq == 2 && D == 128 && !(kt == PA_F16 && vt == PA_F16)) ||
+                 chunk_window_split(nq, D) == 2
+             ? 2
+             : 1;
 }
 // Whether the window kernel takes a chunk with `rows` query rows per kv head
 // (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
