@@ -417,6 +417,8 @@ CHUNKS = {
     "verify_q4_0_32k_b8_t4": ("uniform_q4_0", 8, 32768, 4, "verify window Q4_0 B=8 L=32768 Tq=4"),
     "verify_q4_0_32k_b8_t2": ("uniform_q4_0", 8, 32768, 2, "verify window Q4_0 B=8 L=32768 Tq=2"),
     "prefill_q4_0_8k_t512": ("uniform_q4_0", 1, 8192, 512, "prefill chunk Q4_0 B=1 L=8192 Tq=512"),
+    "verify_q4_0_d128_32k_b8_t8": ("uniform_q4_0_d128", 8, 32768, 8,
+                                   "verify window Q4_0 D=128 Hq=32 Hkv=8 B=8 L=32768 Tq=8"),
 }
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 MFMA, public figure
 

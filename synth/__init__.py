@@ -332,6 +332,8 @@ def workload(name: str, *, B: int = 8, L: int = 4096, seed: int = 1000, device="
     uniform_f16  : B sequences of L tokens, F16 K/V (D=256, Hq=24, Hkv=4).
     ragged_q4_0  : 131072 + 7 x 8192 tokens, blocks interleaved in one pool.
     ragged_small_q4_0 : 4096 + 7 x 256 tokens.
+    uniform_q4_0_d128 : B sequences of L tokens, Q4_0 K/V in the D=128 shape
+                   of slab_f16 (Hq=32, Hkv=8, blocks of 32).
     slab_f16     : D=128, Hq=32, Hkv=8, blocks of 32, 139,264-block pool
                    (more than 2^32 elements per side), B=8 x 65536 tokens with
                    half of each sequence's blocks past element 2^32.
@@ -343,6 +345,9 @@ def workload(name: str, *, B: int = 8, L: int = 4096, seed: int = 1000, device="
         return make_case([L] * B, k_fmt="q8_0", v_fmt="q8_0", seed=seed, device=device, junk=junk)
     if name == "uniform_q4_0":
         return make_case([L] * B, k_fmt="q4_0", v_fmt="q4_0", seed=seed, device=device, junk=junk)
+    if name == "uniform_q4_0_d128":
+        return make_case([L] * B, Hq=32, Hkv=8, D=128, block_size=32, k_fmt="q4_0", v_fmt="q4_0",
+                         seed=seed, device=device, junk=junk)
     if name == "uniform_f16":
         return make_case([L] * B, k_fmt="f16", v_fmt="f16", seed=seed, device=device, junk=junk)
     if name == "ragged_q4_0":
