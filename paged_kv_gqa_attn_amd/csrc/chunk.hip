@@ -55,11 +55,13 @@ template <typename KF, typename VF, bool VJ> struct JobRaw { typename KF::Raw k;
 template <typename KF, typename VF> struct JobRaw<KF, VF, true> { typename VF::Raw v[4]; };
 
 // Workgroups per CU the register allocation is held to: two (two waves per
-// SIMD, 256 registers) for one query tile per wave where that fits without
-// spilling, else one.
+// SIMD, 256 registers) for one query tile per wave, else one. (F16 K at
+// D = 256 spills 6 registers at two, and still measured 2-28% faster than at
+// one: B=8 x 32K F16/Q4_0 Tq=8 222 -> 160 us, an F16 prefill chunk of 512
+// tokens over 8K 308 -> 226 us.)
 template <int KT, int VT, int D, int NTW>
 struct CMinBlocks {
-  static constexpr int value = NTW == 1 && !(KT == kF16 && D == 256) ? 2 : 1;
+  static constexpr int value = NTW == 1 ? 2 : 1;
 };
 
 template <int KT, int VT, int D, int NTW>

@@ -161,11 +161,9 @@ hipError_t launch_chunk_lds(const ChunkArgs& a, hipStream_t stream);
 // Query tiles per wave of the chunk kernel for R = Tq*r rows per kv head (a
 // workgroup of four waves takes 64*nt rows; two tiles per wave fit the
 // registers at D = 128 only), and its workgroups per CU (two waves per SIMD
-// at nt = 1 except F16 K at D = 256, one otherwise).
+// at nt = 1, one otherwise).
 constexpr int chunk_wave_tiles(int64_t rows, int D) { return rows > 64 && D == 128 ? 2 : 1; }
-constexpr int chunk_wgs_per_cu(int nt, int kt, int vt, int D) {
-  return nt == 1 && !(kt == PA_F16 && D == 256) && vt >= 0 ? 2 : 1;
-}
+constexpr int chunk_wgs_per_cu(int nt, int /*kt*/, int /*vt*/, int /*D*/) { return nt == 1 ? 2 : 1; }
 
 // Whole-block copies inside one pool (copy-on-write); up to kCopyPairs pairs
 // per launch travel in the kernel arguments.
