@@ -19,10 +19,10 @@
 // used for all of its NQ column groups. Two shapes of workgroup:
 //  * a quad of kv heads, wave w serving head 4*hg + w over the whole head
 //    dimension (one column group: two workgroups per CU, as in decode; two
-//    at D = 128 with K or V quantised: two per CU as well (Q4_0 B=8 x 32K,
-//    Tq=8 at r=4: 145 -> 94 us per step against one); otherwise one
-//    workgroup per CU, whose registers hold the NQ*D/16 accumulator tiles
-//    and NQ*D/32 Q operands);
+//    or three at D = 128 with K or V quantised: mostly two per CU as well,
+//    chunk_window_wgs_per_cu (Q4_0 B=8 x 32K, Tq=8 at r=4: 145 -> 94 us per
+//    step against one); otherwise one workgroup per CU, whose registers
+//    hold the NQ*D/16 accumulator tiles and NQ*D/32 Q operands);
 //  * two column groups at D = 256, where those are 64 + 128 registers and one
 //    wave per SIMD leaves the step latency-bound: a pair of kv heads, two
 //    waves per head, each taking half of the head dimension (its Q operands,

@@ -134,15 +134,16 @@ constexpr int chunk_window_split(int nq, int D) { return nq == 2 && D == 256 ? 2
 // head, else a quad.
 constexpr int chunk_window_heads(int nq, int D) { return chunk_window_split(nq, D) == 2 ? 2 : 4; }
 // Workgroups per CU of the window kernel: two when one column group fits
-// (the decode kernel's register and LDS budget), for two groups at D = 128
-// where K or V is quantised (their registers fit twice; F16/F16 there is
-// HBM-bound either way and keeps the larger ring of one per CU), or when the
-// head dimension is split; else one.
+// (the decode kernel's register and LDS budget), when the head dimension is
+// split, and for two or three groups at D = 128 where K or V is quantised:
+// two groups fit the registers twice, three spill 2-53 registers at two per
+// CU and still measured 20-45% faster than one, except Q4_0 K with Q8_0 V
+// (97 spilled, 16-18% slower), which keeps one; F16/F16, HBM-bound either
+// way, keeps the larger ring of one per CU. Else one.
 constexpr int chunk_window_wgs_per_cu(int nq, int D, int kt, int vt) {
-  return nq == 1 || (nq == 2 && D == 128 && !(kt == PA_F16 && vt == PA_F16)) ||
-                 chunk_window_split(nq, D) == 2
-             ? 2
-             : 1;
+  const bool d128_twice = D == 128 && (nq == 2 || nq == 3) && !(kt == PA_F16 && vt == PA_F16) &&
+                          !(nq == 3 && kt == PA_Q4_0 && vt == PA_Q8_0);
+  return nq == 1 || d128_twice || chunk_window_split(nq, D) == 2 ? 2 : 1;
 }
 // Whether the window kernel takes a chunk with `rows` query rows per kv head
 // (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
