@@ -400,3 +400,21 @@ def test_smoke_cases_take_the_kernels_smoke_expects():
         for force in (0, 1, 3):
             plan = pa.paged_attn_plan(shape, max(case.seq_lens), num_cus=256, force_partitions=force)
             assert plan.path == path, (label, force, plan.path)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,Tq,kt,vt,per_cu,heads", [
+    (24, 4, 256, 2, "q4_0", "q4_0", 2, 4),    # 12 rows: one column group
+    (24, 4, 256, 4, "q4_0", "q4_0", 2, 2),    # 24 rows at D=256: the head dimension split over kv-head pairs
+    (32, 8, 128, 8, "q4_0", "q4_0", 2, 4),    # 32 rows at D=128, quantised: registers fit twice
+    (32, 8, 128, 8, "f16", "f16", 1, 4),      # F16/F16 keeps the larger ring
+    (32, 8, 128, 12, "q8_0", "q4_0", 2, 4),   # 48 rows at D=128: two per CU where measured faster
+    (32, 8, 128, 12, "q4_0", "q8_0", 1, 4),   # ... but not Q4_0 K with Q8_0 V
+])
+def test_window_kernel_occupancy(Hq, Hkv, D, Tq, kt, vt, per_cu, heads):
+    """The window chunk kernel's workgroups per CU and kv heads per workgroup
+    for each shape class: the plan's grid is min(units, per_cu * num_cus) with
+    units = B * p_max * Hkv / heads."""
+    s = _shape(Hq=Hq, Hkv=Hkv, D=D, k_type=kt, v_type=vt, max_blocks=4096)
+    p = pa.paged_attn_chunk_plan(s, Tq, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.path == 2
+    assert p.grid == min(8 * p.p_max * Hkv // heads, per_cu * 256), (p.grid, p.p_max)
