@@ -1,6 +1,7 @@
 // The LDS ring shared by the LDS-staged kernels: geometry of a step's slot,
-// placement of the four head rows in LDS, the per-lane pool offsets of the
-// 1 KB DMA instructions that fill it, and the per-step wait + barrier.
+// placement of the head rows (a quad or a pair of kv heads) in LDS, the
+// per-lane pool offsets of the 1 KB DMA instructions that fill it, and the
+// per-step wait + barrier.
 // (Included by one translation unit each; everything is internal.)
 #pragma once
 
@@ -81,10 +82,13 @@ __device__ __forceinline__ uint32_t chunk_voff(int sub, int lane, uint32_t strid
 }
 
 // One DMA instruction: every lane fetches 16 bytes at its offset and the
-// wave lands them as 1 KB at LDS byte dst + 16*lane. Every pool line is read
-// exactly once here (a workgroup owns whole blocks of its head quad), so the
-// loads carry the non-temporal hint: it raised the streaming rate of this
-// pattern from ~5.9 to ~6.7 TB/s when measured on its own.
+// wave lands them as 1 KB at LDS byte dst + 16*lane. With quads of kv heads
+// every pool line is read once here (a workgroup owns whole token rows of its
+// quad), so the loads carry the non-temporal hint: it raised the streaming
+// rate of this pattern from ~5.9 to ~6.7 TB/s when measured on its own. (The
+// window kernel's pairs share the line where one pair's rows end and the
+// next begin: +10% fetched at Q4_0 D=256; without the hint that kernel ran
+// 1% faster and every quad kernel 6-9% slower, so the hint stays.)
 constexpr int kDmaNonTemporal = 2;
 __device__ __forceinline__ void dma16(rsrc_t R, uint32_t dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, kDmaNonTemporal);
