@@ -331,11 +331,12 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * the same max-shifted merge; one partition writes out directly.
  * Two kernels compute it: path 1 converts each key/value tile once per
  * workgroup into LDS for four waves of query rows (any Tq); path 2, for
- * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128) with Hkv
- * a multiple of 4 (verify windows), streams the pool through the decode
- * kernel's LDS ring, each wave serving one kv head with all of its rows (at
- * D = 256 with 17..32 rows, two waves per kv head, each over half of the head
- * dimension, adding their partial scores through LDS). The
+ * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128, and at
+ * D = 256 with Q4_0 K and V) with Hkv a multiple of 4 (verify windows),
+ * streams the pool through the decode kernel's LDS ring, each wave serving
+ * one kv head with all of its rows (at D = 256 with more than 16 rows, two
+ * waves per kv head, each over half of the head dimension, adding their
+ * partial scores through LDS). The
  * plan picks path 2 where it applies; a caller may set path = 1 on such a
  * plan to force the general kernel. Pools or q that are not 16-byte aligned
  * run path 1.

@@ -6,8 +6,9 @@
 // prompt-chunk attention): chunk token t of sequence b (length L) sits at position
 // L - Tq + t and attends to the keys at positions 0 .. L - Tq + t of kv head
 // g = h / r. It serves the chunks whose Tq*r query rows of a kv head fit
-// 16*NQ MFMA columns, NQ <= 2 at D = 256 and NQ <= 3 at D = 128 (at r = 6 a
-// verify window of up to 5 tokens at D = 256, 8 at D = 128), where
+// 16*NQ MFMA columns, NQ <= 3 at D = 128, and at D = 256 NQ <= 2, or 3 with
+// Q4_0 K and V (at r = 6 a verify window of up to 5 tokens at D = 256, 8 for
+// Q4_0 or at D = 128), where
 // converting each K/V tile into LDS operands for four waves of 16 rows
 // (chunk.hip) costs more LDS traffic than the rows are worth.
 //
@@ -23,13 +24,16 @@
 //    chunk_window_wgs_per_cu (Q4_0 B=8 x 32K, Tq=8 at r=4: 145 -> 94 us per
 //    step against one); otherwise one workgroup per CU, whose registers
 //    hold the NQ*D/16 accumulator tiles and NQ*D/32 Q operands);
-//  * two column groups at D = 256, where those are 64 + 128 registers and one
-//    wave per SIMD leaves the step latency-bound: a pair of kv heads, two
-//    waves per head, each taking half of the head dimension (its Q operands,
-//    K and V conversion and output columns), the halves' partial scores
-//    added through LDS each step; two workgroups per CU. (Measured on the
-//    verify window Q4_0 B=8 L=32768 Tq=4: 121 us per step with the quad of
-//    whole-dimension waves, 99 us with the pairs.)
+//  * two or three column groups at D = 256, where two are already 64 + 128
+//    registers and one wave per SIMD leaves the step latency-bound: a pair
+//    of kv heads, two waves per head, each taking half of the head
+//    dimension (its Q operands, K and V conversion and output columns), the
+//    halves' partial scores added through LDS each step; two workgroups per
+//    CU. (Measured on the verify window Q4_0 B=8 L=32768 Tq=4: 121 us per
+//    step with the quad of whole-dimension waves, 99 us with the pairs;
+//    Tq=8, three groups: 120 us against 140 us on the tile kernel. With a
+//    Q8_0 side the three-group split measured no faster than the tile
+//    kernel, which keeps those.)
 // Each lane's row has its own causal limit; only steps that cross some row's
 // limit are masked, and a row with no key in the partition writes m = -inf,
 // l = 0. Partials use the decode layout with Tq*Hq rows per sequence and go
@@ -610,9 +614,7 @@ hipError_t launch_typed(const ChunkArgs& a, hipStream_t stream) {
     const int nq = (a.Tq * a.r + 15) / 16;
     if (nq == 1) return launch_nq<KT, VT, D, 1>(a, stream);
     if (nq == 2) return launch_nq<KT, VT, D, 2, chunk_window_split(2, D)>(a, stream);
-    if constexpr (D == 128) {
-      if (nq == 3) return launch_nq<KT, VT, D, 3>(a, stream);
-    }
+    if (nq == 3) return launch_nq<KT, VT, D, 3, chunk_window_split(3, D)>(a, stream);
     return hipErrorInvalidValue;
   }
 }

@@ -127,9 +127,9 @@ struct ChunkArgs {
   int32_t nt;              // 16-row query tiles per wave (chunk_wave_tiles)
 };
 // Waves per kv head of the window kernel with NQ column groups of 16 query
-// rows: 2 (each half of the head dimension) for two column groups at
-// D = 256, else 1.
-constexpr int chunk_window_split(int nq, int D) { return nq == 2 && D == 256 ? 2 : 1; }
+// rows: 2 (each half of the head dimension) for two or three column groups
+// at D = 256, else 1.
+constexpr int chunk_window_split(int nq, int D) { return nq >= 2 && D == 256 ? 2 : 1; }
 // kv heads per workgroup of the window kernel: a pair with two waves per
 // head, else a quad.
 constexpr int chunk_window_heads(int nq, int D) { return chunk_window_split(nq, D) == 2 ? 2 : 4; }
@@ -146,13 +146,16 @@ constexpr int chunk_window_wgs_per_cu(int nq, int D, int kt, int vt) {
   return nq == 1 || d128_twice || chunk_window_split(nq, D) == 2 ? 2 : 1;
 }
 // Whether the window kernel takes a chunk with `rows` query rows per kv head
-// (pools aside): 32 rows at D = 256 and 48 at D = 128 are what one wave's
-// registers hold with their accumulators; Hkv % 4 == 0; the shapes
-// lds_groups() admits.
-constexpr int chunk_window_rows(int D) { return D == 256 ? 32 : 48; }
+// (pools aside): Hkv % 4 == 0, the shapes lds_groups() admits, and up to 48
+// rows (three column groups; at D = 256 over half of the head dimension per
+// wave), except that at D = 256 33..48 rows go to the window kernel only for
+// Q4_0 K and V, whose pair ring holds steps of two 16-slot groups: with a
+// Q8_0 side the steps are single groups and the tile kernel measured as
+// fast or faster (B=8 x 32K, Tq=8 at r=6: Q4_0 120 against 140 us, Q8_0 /
+// Q4_0 147 against 148, Q4_0 / Q8_0 149 against 146).
 constexpr bool chunk_window_ok(int64_t rows, int hkv, int kt, int vt, int D) {
-  return (D == 128 || D == 256) && rows <= chunk_window_rows(D) && hkv % 4 == 0 &&
-         lds_groups(kt, vt, D) > 0;
+  return (D == 128 || D == 256) && hkv % 4 == 0 && lds_groups(kt, vt, D) > 0 &&
+         (rows <= 32 || (rows <= 48 && (D == 128 || (kt == PA_Q4_0 && vt == PA_Q4_0))));
 }
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
 // The window kernel (chunk_lds.hip): the decode kernel's LDS ring, each wave

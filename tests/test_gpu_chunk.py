@@ -34,12 +34,15 @@ def _case(lens, Tq, seed, **kw):
 def window_ok(c, Tq):
     """Whether the window kernel (plan path 2) takes the chunk: quads of kv
     heads, one 16-slot group of K and V of four heads in a 36 KB ring slot
-    (no F16 side at D=256), and Tq*r query rows per kv head that fit one wave
-    (32 at D=256, 48 at D=128)."""
+    (no F16 side at D=256), and at most 48 query rows (Tq*r) per kv head
+    (three column groups of 16, over half of the head dimension per wave at
+    D=256, where 33..48 rows take it for Q4_0 K and V only)."""
     rb = {"f16": 2 * c.D, "q8_0": 34 * c.D // 32, "q4_0": 18 * c.D // 32}
     per_group = sum(-(-16 * 4 * rb[f] // 1024) for f in (c.k_fmt, c.v_fmt)) * 1024
     rows = Tq * (c.Hq // c.Hkv)
-    return c.Hkv % 4 == 0 and per_group <= 36864 and rows <= (32 if c.D == 256 else 48)
+    q4 = c.k_fmt == "q4_0" and c.v_fmt == "q4_0"
+    return (c.Hkv % 4 == 0 and per_group <= 36864
+            and (rows <= 32 or (rows <= 48 and (c.D == 128 or q4))))
 
 
 def _plan(c, Tq, path=None, **kw):
@@ -206,17 +209,18 @@ def test_bad_block_id_sets_status_and_nans_only_that_sequence(path):
     assert float(rel_err_rows(o[:1].double().numpy(), _ref(good, qc[:1])).max()) <= tol_for(c)
 
 
+@pytest.mark.parametrize("rows", [32, 48])
 @pytest.mark.parametrize("heads", [(24, 4), (32, 8)], ids=["r6", "r4-two-quads"])
 @pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "q4_0"), ("f16", "q8_0")])
 @pytest.mark.parametrize("D", [256, 128])
-def test_both_kernels_agree(pair, D, heads):
+def test_both_kernels_agree(pair, D, heads, rows):
     """The same chunk on both kernels with the same partitioning, to the
     format tolerance: besides the order of fp32 accumulation they round the
     quantised values differently (the window kernel folds the Q4_0 offset
     into correction MFMAs as the decode kernel does; the tile kernel converts
     (n - 8) * d directly). Hkv = 8 gives two kv-head quads per sequence."""
     Hq, Hkv = heads
-    Tq = (32 if D == 256 else 48) // (Hq // Hkv)
+    Tq = rows // (Hq // Hkv)
     c, qc = _case([2000, 700, 33], Tq, seed=101 + D + Hkv, k_fmt=pair[0], v_fmt=pair[1], D=D,
                   Hq=Hq, Hkv=Hkv)
     if not window_ok(c, Tq):
@@ -285,9 +289,10 @@ def test_unaligned_q_runs_the_tile_kernel():
 def test_verify_windows_at_full_size(Tq):
     """Verify windows of 2, 4 and 8 tokens over Q4_0 K/V, B=8 x 32768 tokens
     (the chunk benchmark's workloads), on the automatic plan: the window
-    kernel at two workgroups per CU for 12 query rows per kv head, at one
-    for 24, the tile kernel for 48. One sequence per case (2, 4, 0) is
-    checked against the oracle, which reads host copies of just its blocks."""
+    kernel, a kv-head quad per workgroup for 12 query rows per kv head, a
+    kv-head pair with the head dimension split over two waves for 24 and 48.
+    One sequence per case (2, 4, 0) is checked against the oracle, which
+    reads host copies of just its blocks."""
     from gpu_util import BlockSubset
     pa = pa_mod()
     case = synth.workload("uniform_q4_0", B=8, L=32768, seed=1500 + Tq, device=DEV)
@@ -296,7 +301,7 @@ def test_verify_windows_at_full_size(Tq):
                         case.max_blocks, case.k_fmt, case.v_fmt)
     plan = pa.paged_attn_chunk_plan(shape, Tq, max(case.seq_lens), total_tokens=sum(case.seq_lens),
                                     scale=case.scale)
-    assert plan.path == (2 if Tq * case.Hq // case.Hkv <= 32 else 1)
+    assert plan.path == 2
     ws = pa.workspace(plan, DEV)
     out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
     pa.paged_attn_chunk(plan, qc.to(DEV), case.k_pool, case.v_pool, case.table, case.seq_len, ws, out)

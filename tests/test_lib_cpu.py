@@ -325,15 +325,15 @@ def test_chunk_plan_partitions_and_workspace():
     """paged_attn_chunk_plan: a four-wave workgroup per (sequence, partition,
     kv head, 64 query rows at D=256), two per compute unit; partials of 2D+8
     bytes per query row and partition."""
-    p = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
-    assert p.tq == 8 and p.psize % 32 == 0 and p.direct == 0
+    p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.tq == 9 and p.psize % 32 == 0 and p.direct == 0 and p.path == 1
     assert p.p_max == -(-32768 // p.psize)
-    units = 8 * p.p_max * 4 * 1                      # 8*6 = 48 rows per kv head: one block
+    units = 8 * p.p_max * 4 * 1                      # 9*6 = 54 rows per kv head: one block
     assert p.grid == min(units, 256 * 2)
     big = pa.paged_attn_chunk_plan(_shape(B=1), 512, 8192, num_cus=256)
     assert big.grid == min(1 * big.p_max * 4 * 48, 512)      # 3072 rows: 48 blocks of 64
     assert p.part_offset == 256 + 8 * 4160
-    assert p.ws_bytes == -(-(p.part_offset + 8 * 8 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
+    assert p.ws_bytes == -(-(p.part_offset + 8 * 9 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
     d = pa.paged_attn_chunk_plan(_shape(B=1), 16, 200, num_cus=256)
     assert d.direct == 1 and d.p_max == 1 and d.ws_bytes == 256 + 4352
     f = pa.paged_attn_chunk_plan(_shape(), 4, 1000, num_cus=256, partition_tokens=64)
@@ -341,15 +341,18 @@ def test_chunk_plan_partitions_and_workspace():
 
 
 def test_chunk_plan_kernel_choice():
-    """The window kernel (path 2) for at most 32 query rows per kv head at
-    D=256 (48 at D=128): a workgroup per (sequence, partition, kv-head quad),
-    two per compute unit for at most 16 rows, else one, except 17..32 rows at
+    """The window kernel (path 2) for at most 48 query rows per kv head: a
+    workgroup per (sequence, partition, kv-head quad), except 17..48 rows at
     D=256, where the head dimension is split over two waves and a workgroup
     takes a kv-head pair, two per compute unit; the tile-conversion kernel
     (path 1) otherwise. A plan forced to path 2 where it does not apply is
     refused before launch."""
-    p = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
-    assert p.path == 1                                   # 48 rows at D=256
+    p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert p.path == 1                                   # 54 rows
+    w8 = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert w8.path == 2 and w8.grid == min(8 * w8.p_max * 2, 512)  # 48 rows: kv-head pairs
+    q8 = pa.paged_attn_chunk_plan(_shape(k_type="q8_0"), 8, 32768, total_tokens=8 * 32768, num_cus=256)
+    assert q8.path == 1                                  # 48 rows at D=256 with a Q8_0 side
     w = pa.paged_attn_chunk_plan(_shape(), 4, 32768, total_tokens=8 * 32768, num_cus=256)
     assert w.path == 2 and w.grid == min(8 * w.p_max * 2, 512)     # 24 rows: kv-head pairs
     w2 = pa.paged_attn_chunk_plan(_shape(), 2, 32768, total_tokens=8 * 32768, num_cus=256)
@@ -405,6 +408,7 @@ def test_smoke_cases_take_the_kernels_smoke_expects():
 @pytest.mark.parametrize("Hq,Hkv,D,Tq,kt,vt,per_cu,heads", [
     (24, 4, 256, 2, "q4_0", "q4_0", 2, 4),    # 12 rows: one column group
     (24, 4, 256, 4, "q4_0", "q4_0", 2, 2),    # 24 rows at D=256: the head dimension split over kv-head pairs
+    (24, 4, 256, 8, "q4_0", "q4_0", 2, 2),    # 48 rows at D=256: the same
     (32, 8, 128, 8, "q4_0", "q4_0", 2, 4),    # 32 rows at D=128, quantised: registers fit twice
     (32, 8, 128, 8, "f16", "f16", 1, 4),      # F16/F16 keeps the larger ring
     (32, 8, 128, 12, "q8_0", "q4_0", 2, 4),   # 48 rows at D=128: two per CU where measured faster
