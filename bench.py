@@ -501,7 +501,7 @@ def run_chunk(args):
         "config": {"workload": desc, "name": args.chunk, "B": B, "L": L, "Tq": Tq, "Hq": c0.Hq,
                    "Hkv": c0.Hkv, "D": c0.D, "k_type": c0.k_fmt, "v_type": c0.v_fmt,
                    "psize": plan.psize, "p_max": plan.p_max, "grid": plan.grid,
-                   "kernel": "window" if plan.path == 2 else "tile conversion",
+                   "kernel": {1: "tile conversion", 2: "window", 3: "wide tile"}[plan.path],
                    "pool_copies": len(cases), "gpu_us_events": round(gpu_us, 2)},
         "roofline": {"bound": bound,
                      "hbm": {"achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -617,8 +617,8 @@ def main():
     ap.add_argument("--stem", default=None, help="profiles/ file stem (default decode_LABEL)")
     ap.add_argument("--chunk", default=None, choices=sorted(CHUNKS),
                     help="measure paged_attn_chunk on this workload instead of the decode step")
-    ap.add_argument("--chunk-path", type=int, default=0, choices=[0, 1, 2],
-                    help="with --chunk: force the chunk kernel (1 tile conversion, 2 window)")
+    ap.add_argument("--chunk-path", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="with --chunk: force the chunk kernel (1 tile conversion, 2 window, 3 wide tile)")
     ap.add_argument("--metadata", action="store_true",
                     help="measure the paging-metadata entry points instead of the decode step")
     ap.add_argument("--sweep", action="store_true",

@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-SOURCES = ["api.cpp", "kv_pool.cpp", "decode.hip", "decode_lds.hip", "merge.hip", "gather.hip", "chunk.hip", "chunk_lds.hip",
+SOURCES = ["api.cpp", "kv_pool.cpp", "decode.hip", "decode_lds.hip", "merge.hip", "gather.hip", "chunk.hip", "chunk_lds.hip", "chunk_wide.hip",
            "table.hip", "step_noalloc.hip"]
 # Packed fp32 VALU ops are kept off: the compiler must not form them.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-slp-vectorize",

@@ -467,7 +467,7 @@ int32_t check_chunk_plan(const pa_chunk_plan* p, const char* who) {
   if (rc) return rc;
   if (p->tq < 1 || p->tq > kMaxChunk || p->psize < kTileTokens || p->psize % kTileTokens ||
       p->p_max < 1 || p->grid < 1 || !(p->scale == p->scale) || p->direct != (p->p_max == 1) ||
-      (p->path != 1 && p->path != 2) || p->part_offset != ws_part_offset(p->shape.B, p->shape.Hkv))
+      p->path < 1 || p->path > 3 || p->part_offset != ws_part_offset(p->shape.B, p->shape.Hkv))
     return fail(PA_ERR_INVALID, "%s: plan was not produced by paged_attn_chunk_plan", who);
   const pa_shape& s = p->shape;
   if (p->path == 2 && !chunk_window_ok(int64_t(p->tq) * (s.Hq / s.Hkv), s.Hkv, s.k_type, s.v_type, s.D))
@@ -503,16 +503,19 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   const int64_t r = s.Hq / s.Hkv;
   // the window kernel takes short chunks (a workgroup per kv-head quad, two
   // per CU for at most 16 query rows per kv head, else one; with the head
-  // dimension split, a workgroup per kv-head pair, two per CU); the
-  // tile-conversion kernel the rest (a workgroup per kv head and 64*nt query
-  // rows, one or two per CU)
+  // dimension split, a workgroup per kv-head pair, two per CU); the wide-tile
+  // kernel long ones (a workgroup per kv head and 128 query rows, one per
+  // CU); the tile-conversion kernel the rest (a workgroup per kv head and
+  // 64*nt query rows, one or two per CU)
   const bool window = chunk_window_ok(int64_t(tq) * r, s.Hkv, s.k_type, s.v_type, s.D);
+  const bool wide = !window && chunk_wide_pick(int64_t(tq) * r, s.D);
   const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
-  const int64_t qt = window ? 1 : (int64_t(tq) * r + 64 * nt - 1) / (64 * nt);   // row blocks per unit
+  const int64_t block_rows = wide ? kWideRows : 64 * nt;
+  const int64_t qt = window ? 1 : (int64_t(tq) * r + block_rows - 1) / block_rows;   // row blocks per unit
   const int nq = int(ceil_div(int64_t(tq) * r, 16));
   const int64_t heads_per_unit = window ? chunk_window_heads(nq, s.D) : 1;
   const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D, s.k_type, s.v_type)
-                                : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D);
+                                : (wide ? 1 : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D));
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
   int64_t psize;
   if (partition_tokens > 0) {
@@ -565,7 +568,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   plan->grid = int32_t(grid);
   plan->num_cus = num_cus;
   plan->direct = direct ? 1 : 0;
-  plan->path = window ? 2 : 1;
+  plan->path = window ? 2 : (wide ? 3 : 1);
   plan->ws_bytes = ws;
   plan->part_offset = ws_part_offset(s.B, s.Hkv);
   clear_error();
@@ -607,10 +610,13 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.nt = chunk_wave_tiles(int64_t(plan->tq) * a.r, s.D);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the window kernel's DMA chunks are 16-byte aligned only on aligned
-  // pools, and it reads q rows with 16-byte loads
+  // pools, and the window and wide-tile kernels read q rows with 16-byte
+  // loads; otherwise the tile kernel runs
   const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
                          reinterpret_cast<uintptr_t>(q)) & 15) == 0;
-  hipError_t e = plan->path == 2 && aligned ? launch_chunk_lds(a, st) : launch_chunk(a, st);
+  hipError_t e = !aligned || plan->path == 1 ? launch_chunk(a, st)
+                 : plan->path == 2         ? launch_chunk_lds(a, st)
+                                           : launch_chunk_wide(a, st);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   if (!plan->direct) {
     MergeArgs mg{};

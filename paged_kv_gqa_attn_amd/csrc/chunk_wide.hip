@@ -1,0 +1,881 @@
+// Multi-token queries with many query rows per kv head (prefill chunks): the
+// wide-tile kernel.
+//
+// What it computes is what chunk.hip computes (lucebox PR #555, Roadmap item
+// 3: several query tokens per sequence attend over the K/V already in the
+// pool, causally inside the chunk; TensorFold PR #1418, What: paged
+// prompt-chunk attention): chunk token t of sequence b (length L) sits at
+// position L - Tq + t and attends to the keys at positions 0 .. L - Tq + t of
+// kv head g = h / r, with the Tq*r query rows of a kv head (row n = t*r +
+// h - g*r) sharing every converted K/V tile.
+//
+// How it maps onto gfx950 (a prefill chunk is MFMA-bound: 4*D flops per
+// visible query row and key):
+//   * 32x32x16 f16 MFMAs. Scores come as S^T = K Q^T, 32 keys by 32 query
+//     rows per MFMA, with the rows' Q^T held in registers as the B operand;
+//     the S^T accumulators are, lane for lane, the B operand P^T of
+//     O^T += V^T P^T once converted to f16 (the V^T operand lists its keys
+//     in the accumulators' order), so P never moves between lanes. Each lane
+//     holds one query row (lanes l and l+32 split its keys), so the row max
+//     is 15 in-lane max operations and one lane swap.
+//   * A workgroup of four wave64s takes a unit (sequence b, key partition p,
+//     kv head g, 128 query rows), wave w owning rows 32w .. 32w+31. A wave
+//     holds its rows' Q operands (D/4 registers) and O^T accumulators (D/2),
+//     so the kernel runs one workgroup per CU with 512 registers per lane.
+//     Every operand the MFMAs read from LDS serves 32 rows: 1 KB per
+//     32x32x16 MFMA, twice the rows per operand byte of the 16x16 tiles of
+//     chunk.hip.
+//   * Every 32-key tile is converted to f16 once per workgroup, into LDS in
+//     MFMA operand order: waves 0 and 1 convert K of 16-key groups 0 and 1,
+//     waves 2 and 3 V of the same groups, each loading its raw rows straight
+//     from the pool through the block table (64-bit row addresses, mlxcel
+//     issue #2153).
+//   * One barrier per tile, in a software pipeline: while the softmax and PV
+//     of tile kt run, the scores of tile kt+1 are computed and tile kt+2 is
+//     converted, and the raw rows of tile kt+4 are loaded. K operands are
+//     double-buffered and V operands triple-buffered (V of tile kt is read
+//     one iteration later than K), 80 KB at D = 256.
+//   * Causal limit per row; tiles past the workgroup's last row are not
+//     read and only tiles that cross some row's limit are masked. Partials
+//     (normalised binary16 o, fp32 m and l) use the decode layout with Tq*Hq
+//     rows per sequence and go through the same merge.
+#include <type_traits>
+
+#include "decode_common.h"
+#include "lds_ring.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWThreads = 256;
+constexpr int kWRows = 128;     // query rows per workgroup (32 per wave)
+constexpr int kWNid = 512;      // block ids staged per segment of a partition
+constexpr int kWTile = 32;      // keys per tile
+// Order of a tile step's work (see the pipeline below).
+constexpr int kStepOrder = 0;
+
+// 32x32x16 f16 -> f32: A lane l (row l%32, k 8*(l/32)+i), B lane l (col l%32,
+// k 8*(l/32)+i), C lane l register r (row 8*(r/4) + 4*(l/32) + r%4, col l%32).
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// Wait states after the last MFMAs of a loop, before a block after it reads
+// their results (see mfma_settle), kept in place by a scheduling barrier.
+// Inside the loop every MFMA result is read an iteration after the MFMA.
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling of N MFMAs that each read one operand from LDS: two reads ahead,
+// then one read per MFMA, so at most three operands wait in registers.
+template <int N>
+__device__ __forceinline__ void lds_mfma_stream() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < N - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+// Key of register r of an S^T accumulator, within its 32-key tile, for lane half h.
+__host__ __device__ constexpr int skey(int r, int h) { return 8 * (r / 4) + 4 * h + r % 4; }
+// Key of slot e of a P^T (and V^T) operand half of k-step t: the accumulator
+// registers 8t .. 8t+7 in order.
+__host__ __device__ constexpr int pkey(int t, int h, int e) { return skey(8 * t + e, h); }
+
+// Byte-pair conversion order (bytes 0, 2 then 1, 3 of each dword).
+__host__ __device__ constexpr int word_order(int s) { return (s & 4) + ((s & 1) << 1) + ((s >> 1) & 1); }
+
+// v_perm_b32 selector for bytes [s, s+4) of {hi:lo}, s in 0..4.
+__device__ __forceinline__ uint32_t shift_sel(uint32_t s) { return 0x03020100u + s * 0x01010101u; }
+
+// ===========================================================================
+// K formats: the A operand of S^T = K Q^T. Lane l holds key l%32 of the tile
+// and, for step c (0 .. D/16-1), head positions kd(c, l/32, 0..7). Every wave
+// converts a quarter of a tile's K: 8 keys, its lane kk + 8q the operand
+// slots of key kk for half h = q & 1 and the CQ = D/64 steps of quarter
+// cq = q >> 1 (c = cq*CQ + cc). `load` reads the lane's bytes of its staged
+// row into kWords dwords, `op` converts step cc.
+// ===========================================================================
+template <int KT, int D> struct WK;
+
+template <int D> struct WK<kF16, D> {
+  static constexpr int CQ = D / 64;
+  static constexpr int kWords = 4 * CQ;
+  __host__ __device__ static constexpr int kd(int c, int h, int s) { return 16 * c + 8 * h + s; }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+#pragma unroll
+    for (int cc = 0; cc < CQ; ++cc) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(row + 32 * (cq * CQ + cc) + 16 * h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[4 * cc + k] = a[k];
+    }
+  }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int, uint32_t) {
+    return bitcast<f16x8>(u32x4{w[4 * cc], w[4 * cc + 1], w[4 * cc + 2], w[4 * cc + 3]});
+  }
+};
+
+// Quantised K: step c = 2*bk + x covers ggml block bk, quant bytes [16x + 8h,
+// +8) for Q8_0, nibble x of quant bytes [8h, +8) for Q4_0, in word_order.
+// The 8 bytes start 2 bytes into a dword for even bk: three dwords from the
+// 4-aligned base below them are read and realigned (v_alignbyte).
+template <int D> struct WK<kQ4_0, D> {
+  static constexpr int CQ = D / 64, NBQ = CQ / 2;   // steps, blocks per lane
+  static constexpr int kWords = 4 * NBQ;            // block j: w[3j..3j+2], scale w[3NBQ + j]
+  __host__ __device__ static constexpr int kd(int c, int h, int s) {
+    return 32 * (c / 2) + 16 * (c % 2) + 8 * h + word_order(s);
+  }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+#pragma unroll
+    for (int j = 0; j < NBQ; ++j) {
+      const int bk = cq * NBQ + j;
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(row + ((18 * bk + 2 + 8 * h) & ~3));
+      w[3 * j] = q[0];
+      w[3 * j + 1] = q[1];
+      w[3 * j + 2] = q[2];
+      w[3 * NBQ + j] = *reinterpret_cast<const uint16_t*>(row + 18 * bk);
+    }
+  }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) {
+    const int j = cc / 2, x = cc % 2;
+    const uint32_t sh = ((cq * NBQ + j) & 1) ? 0u : 2u;
+    uint32_t w0 = align_bytes(w[3 * j + 1], w[3 * j], sh);
+    uint32_t w1 = align_bytes(w[3 * j + 2], w[3 * j + 1], sh);
+    if (x) { w0 >>= 4; w1 >>= 4; }
+    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[3 * NBQ + j])));
+    return pack8(nib_pair_to_f16(w0, d2, mg), nib_pair_to_f16(w0 >> 8, d2, mg),
+                 nib_pair_to_f16(w1, d2, mg), nib_pair_to_f16(w1 >> 8, d2, mg));
+  }
+};
+
+template <int D> struct WK<kQ8_0, D> {
+  static constexpr int CQ = D / 64, NBQ = CQ / 2;
+  static constexpr int kWords = 7 * NBQ;            // chunk x of block j: w[6j + 3x ..], scale w[6NBQ + j]
+  __host__ __device__ static constexpr int kd(int c, int h, int s) {
+    return 32 * (c / 2) + 16 * (c % 2) + 8 * h + word_order(s);
+  }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+#pragma unroll
+    for (int j = 0; j < NBQ; ++j) {
+      const int bk = cq * NBQ + j;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(row + ((34 * bk + 2 + 16 * x + 8 * h) & ~3));
+        w[6 * j + 3 * x] = q[0];
+        w[6 * j + 3 * x + 1] = q[1];
+        w[6 * j + 3 * x + 2] = q[2];
+      }
+      w[6 * NBQ + j] = *reinterpret_cast<const uint16_t*>(row + 34 * bk);
+    }
+  }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) {
+    const int j = cc / 2, o = 6 * j + 3 * (cc % 2);
+    const uint32_t sh = ((cq * NBQ + j) & 1) ? 0u : 2u;
+    const uint32_t u0 = align_bytes(w[o + 1], w[o], sh);
+    const uint32_t u1 = align_bytes(w[o + 2], w[o + 1], sh);
+    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[6 * NBQ + j])));
+    const uint32_t a = u0 ^ 0x80808080u, b = u1 ^ 0x80808080u;
+    return pack8(i8pair_to_f16(a, d2, mg), i8pair_to_f16(a >> 8, d2, mg), i8pair_to_f16(b, d2, mg),
+                 i8pair_to_f16(b >> 8, d2, mg));
+  }
+};
+
+// ===========================================================================
+// V formats: the A operand of O^T += V^T P^T. Lane l = i + 32h holds, for
+// k-step t (16-key group t of the tile) and d-tile dt (0 .. D/32-1), head
+// position vd(dt, i) of keys pkey(t, h, 0..7). Every wave converts a quarter
+// of a tile's V: of one 16-key group, the keys pkey(t, h, 4k .. 4k+3) of
+// every operand lane (k = 0 or 1), written as the f16x4 half k of the lane's
+// f16x8. `load` reads those 4 keys' bytes from the staged rows (r0: the row
+// of the first, pkey(t, h, 4k); the others pkey(0, 0, e) rows on) into
+// kWords dwords, `prep` realigns them in place, `op` converts d-tile dt.
+// dnext(dt) is the d-tile holding position vd(dt, i) + 1 (for every i), or
+// -1: the pairs of adjacent positions the binary16 partial rows are stored by.
+// ===========================================================================
+template <int VT, int D> struct WV;
+
+template <int D> struct WV<kF16, D> {
+  static constexpr int NDT = D / 32;
+  static constexpr int NW = NDT / 2;          // dwords of a key the lane reads
+  static constexpr int kWords = 4 * NW;
+  struct Lane { uint32_t voff; };
+  __host__ __device__ static constexpr int vd(int dt, int i) { return NDT * i + dt; }
+  __host__ __device__ static constexpr int dnext(int dt) { return dt % 2 ? -1 : dt + 1; }
+  __device__ static Lane lane(int i) { return Lane{2u * NDT * i}; }
+  __device__ static void load(uint32_t* w, const unsigned char* r0, const Lane& L) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned char* p = r0 + pkey(0, 0, e) * (2 * D) + L.voff;
+      if constexpr (NW == 4) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[4 * e + k] = a[k];
+      } else {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+        w[2 * e] = a[0];
+        w[2 * e + 1] = a[1];
+      }
+    }
+  }
+  __device__ static void kill(uint32_t* w, int e) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[NW * e + k] = 0;
+  }
+  __device__ static void prep(uint32_t*, const Lane&) {}
+  __device__ static f16x4 op(const uint32_t* w, const Lane&, int dt, uint32_t) {
+    const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+    u32x2 o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) o[q] = perm_bytes(w[NW * (2 * q + 1) + dt / 2], w[NW * (2 * q) + dt / 2], sel);
+    return bitcast<f16x4>(o);
+  }
+};
+
+// Q4_0 V. D = 256: lane row i = 4bk + c (block bk, quant dword c), d-tile
+// dt = 2b + x (byte b of the dword, nibble x): position 32bk + 16x + 4c + b.
+// D = 128: i = 16x + 4bk + c, dt = b, the same position. Key e: window
+// w[2e], w[2e+1], scale w[8 + e].
+template <int D> struct WV<kQ4_0, D> {
+  static constexpr int NDT = D / 32;
+  static constexpr int RB = 18 * (D / 32);
+  static constexpr int kWords = 12;
+  struct Lane { uint32_t voff, sel, doff, xs; };
+  __host__ __device__ static constexpr int vbk(int i) { return D == 256 ? i / 4 : (i / 4) % 4; }
+  __host__ __device__ static constexpr int vx(int dt, int i) { return D == 256 ? dt % 2 : i / 16; }
+  __host__ __device__ static constexpr int vb(int dt) { return D == 256 ? dt / 2 : dt; }
+  __host__ __device__ static constexpr int vd(int dt, int i) {
+    return 32 * vbk(i) + 16 * vx(dt, i) + 4 * (i % 4) + vb(dt);
+  }
+  __host__ __device__ static constexpr int dnext(int dt) {
+    return D == 256 ? ((dt / 2) % 2 ? -1 : dt + 2) : (dt % 2 ? -1 : dt + 1);
+  }
+  // quant dword c of block bk at o = 18bk + 2 + 4c; two dwords are read from
+  // the 4-aligned base at or below o (kept inside the row) and the dword
+  // picked out with a byte permute
+  __device__ static Lane lane(int i) {
+    const uint32_t o = 18u * vbk(i) + 2u + 4u * (i % 4);
+    const uint32_t base = min(o & ~3u, uint32_t(RB - 8));
+    return Lane{base, shift_sel(o - base), 18u * vbk(i), D == 256 ? 0u : 4u * uint32_t(i / 16)};
+  }
+  __device__ static void load(uint32_t* w, const unsigned char* r0, const Lane& L) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned char* row = r0 + pkey(0, 0, e) * RB;
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(row + L.voff);
+      w[2 * e] = q[0];
+      w[2 * e + 1] = q[1];
+      w[8 + e] = *reinterpret_cast<const uint16_t*>(row + L.doff);
+    }
+  }
+  __device__ static void kill(uint32_t* w, int e) { w[8 + e] = 0; }
+  // the quant dword of key e into w[2e]; scale pairs of keys (2k, 2k+1) into w[8 + 2k]
+  __device__ static void prep(uint32_t* w, const Lane& L) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[2 * e] = perm_bytes(w[2 * e + 1], w[2 * e], L.sel);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w[8 + 2 * k] = (w[8 + 2 * k] & 0xFFFFu) | (w[9 + 2 * k] << 16);
+  }
+  __device__ static f16x4 op(const uint32_t* w, const Lane& L, int dt, uint32_t mg) {
+    const uint32_t b = uint32_t(vb(dt));
+    const uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
+    f16x2 o[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t y = perm_bytes(w[4 * k + 2], w[4 * k], sel);
+      if constexpr (D == 256) {
+        if (dt % 2) y >>= 4;
+      } else {
+        y >>= L.xs;
+      }
+      o[k] = nib_pair_to_f16(y, bitcast<f16x2>(w[8 + 2 * k]), mg);
+    }
+    return f16x4{o[0][0], o[0][1], o[1][0], o[1][1]};
+  }
+};
+
+// Q8_0 V. D = 256: lane row i = 4bk + c, quant bytes [8c, +8) of block bk,
+// d-tile dt = byte: position 32bk + 8c + dt. D = 128: i = 8bk + c, bytes
+// [4c, +4), position 32bk + 4c + dt. Key e: window w[NWIN*e ..], scale
+// w[4*NWIN + e].
+template <int D> struct WV<kQ8_0, D> {
+  static constexpr int NDT = D / 32;
+  static constexpr int RB = 34 * (D / 32);
+  static constexpr int QB = NDT;                // quant bytes per key and lane
+  static constexpr int NWIN = QB / 4 + 1;       // window dwords
+  static constexpr int SC = 4 * NWIN;           // first scale word
+  static constexpr int kWords = 4 * NWIN + 4;
+  struct Lane { uint32_t voff, sel, doff; };
+  __host__ __device__ static constexpr int vbk(int i) { return D == 256 ? i / 4 : i / 8; }
+  __host__ __device__ static constexpr int vc(int i) { return D == 256 ? i % 4 : i % 8; }
+  __host__ __device__ static constexpr int vd(int dt, int i) { return 32 * vbk(i) + QB * vc(i) + dt; }
+  __host__ __device__ static constexpr int dnext(int dt) { return dt % 2 ? -1 : dt + 1; }
+  __device__ static Lane lane(int i) {
+    const uint32_t o = 34u * vbk(i) + 2u + uint32_t(QB) * vc(i);
+    const uint32_t base = min(o & ~3u, uint32_t(RB - 4 * NWIN));
+    return Lane{base, shift_sel(o - base), 34u * vbk(i)};
+  }
+  __device__ static void load(uint32_t* w, const unsigned char* r0, const Lane& L) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned char* row = r0 + pkey(0, 0, e) * RB;
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(row + L.voff);
+#pragma unroll
+      for (int k = 0; k < NWIN; ++k) w[NWIN * e + k] = q[k];
+      w[SC + e] = *reinterpret_cast<const uint16_t*>(row + L.doff);
+    }
+  }
+  __device__ static void kill(uint32_t* w, int e) { w[SC + e] = 0; }
+  // quant dwords of key e into w[NWIN*e + k], k < QB/4; scale pairs into w[SC + 2k]
+  __device__ static void prep(uint32_t* w, const Lane& L) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int k = 0; k < QB / 4; ++k) w[NWIN * e + k] = perm_bytes(w[NWIN * e + k + 1], w[NWIN * e + k], L.sel);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w[SC + 2 * k] = (w[SC + 2 * k] & 0xFFFFu) | (w[SC + 2 * k + 1] << 16);
+  }
+  __device__ static f16x4 op(const uint32_t* w, const Lane&, int dt, uint32_t) {
+    const uint32_t b = uint32_t(dt % 4);
+    const uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
+    f16x2 o[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t y =
+          perm_bytes(w[NWIN * (2 * k + 1) + dt / 4], w[NWIN * (2 * k) + dt / 4], sel) ^ 0x64806480u;
+      o[k] = (bitcast<f16x2>(y) - f16x2{1152.0f16, 1152.0f16}) * bitcast<f16x2>(w[SC + 2 * k]);
+    }
+    return f16x4{o[0][0], o[0][1], o[1][0], o[1][1]};
+  }
+};
+
+template <typename VF>
+__host__ __device__ constexpr bool pairs_ok() {
+  for (int dt = 0; dt < VF::NDT; ++dt) {
+    const int n = VF::dnext(dt);
+    for (int i = 0; i < 32; ++i) {
+      if (n >= 0 && (VF::vd(n, i) != VF::vd(dt, i) + 1 || VF::vd(dt, i) % 2)) return false;
+    }
+  }
+  int seen = 0;
+  for (int dt = 0; dt < VF::NDT; ++dt) seen += VF::dnext(dt) >= 0 ? 2 : 0;
+  return seen == VF::NDT;
+}
+
+// Staging of raw K/V rows: a side (K or V) of one 16-key group is DMA'd as
+// NI instructions of 64 chunks of CB bytes (16, or 4 where a row is not a
+// whole number of 16-byte chunks), the 16 rows of kv head g back to back.
+template <int T, int D> struct Stage {
+  static constexpr int RB = row_bytes_of(T, D);
+  static constexpr int CB = RB % 16 == 0 ? 16 : 4;
+  static constexpr int CPR = RB / CB;                 // chunks per row
+  static constexpr int NI = (16 * CPR + 63) / 64;     // instructions per group
+  static constexpr int GB = NI * 64 * CB;             // LDS bytes per group
+  // pool offset (from the group's first row) of chunk 64*j + lane, or past
+  // any resource (reads as 0) for the instruction's unused lanes
+  __device__ static uint32_t off(int j, int lane, uint32_t stride) {
+    const int c = 64 * j + lane;
+    const int row = c / CPR;
+    return c < 16 * CPR ? uint32_t(row) * stride + uint32_t(c - row * CPR) * CB : 0x80000000u;
+  }
+};
+
+template <int KT, int VT, int D> struct WideLds {
+  using SK = Stage<KT, D>;
+  using SV = Stage<VT, D>;
+  static constexpr int KBUF = (D / 16) * 64 * 16;          // K operands of a tile
+  static constexpr int VBUF = 2 * (D / 32) * 64 * 16;      // V operands of a tile
+  static constexpr int SLOT = 2 * (SK::GB + SV::GB);       // raw rows of a tile
+  static constexpr int IDS = 4 * (kWNid + 4);              // block ids of a segment
+  static constexpr int OPS = 2 * KBUF + 3 * VBUF;
+  // raw tiles in the ring: up to four (RR-1 in flight while one is
+  // converted), as many as fit the 160 KB of a CU
+  static constexpr int RR = OPS + 4 * SLOT + IDS <= 160 * 1024   ? 4
+                            : OPS + 3 * SLOT + IDS <= 160 * 1024 ? 3
+                                                                 : 2;
+  static constexpr int RAW = OPS;
+  static constexpr int ID0 = RAW + RR * SLOT;
+  static constexpr int BYTES = ID0 + IDS;
+  static constexpr int NT = 2 * (SK::NI + SV::NI);          // DMA instructions per tile
+  static_assert(BYTES <= 160 * 1024, "LDS of one CU");
+};
+
+// The DMA instructions of one tile (tokens t0 .. t0+31 of the segment) that
+// wave W issues: q % 4 == W of the NT, K then V of group 0, then group 1.
+// Groups at or past seg_t1 get a zero-size resource and read nothing.
+// One DMA instruction: lane l's CB bytes at pool offset voff land at LDS
+// byte dst + CB*l (cached loads: the tiles are read again by the other
+// query-row blocks of the kv head).
+template <int CB>
+__device__ __forceinline__ void dma_lds(rsrc_t R, uint32_t dst, uint32_t voff) {
+  if constexpr (CB == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 4, voff, 0, 0, 0);
+}
+
+template <class LY, int W>
+__device__ __forceinline__ void issue_tile_as(const ChunkArgs& a, uint32_t slot, int t0, int seg_t1,
+                                              const int32_t* ids, int jb0, int g, uint32_t kstride,
+                                              uint32_t vstride, int lane) {
+  using SK = typename LY::SK;
+  using SV = typename LY::SV;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int tg = t0 + 16 * gi;
+    const bool live = tg < seg_t1;
+    const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+    const int slot0 = live ? (tg & bs_mask) : 0;
+    const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SK::RB),
+                                live ? 16u * kstride : 0u);
+    const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SV::RB),
+                                live ? 16u * vstride : 0u);
+#pragma unroll
+    for (int j = 0; j < SK::NI; ++j) {
+      const int q = gi * (SK::NI + SV::NI) + j;
+      if (q % 4 == W)
+        dma_lds<SK::CB>(kr, slot + gi * SK::GB + j * 64 * SK::CB, SK::off(j, lane, kstride));
+    }
+#pragma unroll
+    for (int j = 0; j < SV::NI; ++j) {
+      const int q = gi * (SK::NI + SV::NI) + SK::NI + j;
+      if (q % 4 == W)
+        dma_lds<SV::CB>(vr, slot + 2 * SK::GB + gi * SV::GB + j * 64 * SV::CB, SV::off(j, lane, vstride));
+    }
+  }
+}
+
+template <int KT, int VT, int D>
+__global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArgs a) {
+  using KF = WK<KT, D>;
+  using VF = WV<VT, D>;
+  using LY = WideLds<KT, VT, D>;
+  using SK = typename LY::SK;
+  using SV = typename LY::SV;
+  static_assert(pairs_ok<VF>(), "d-tile pairs cover adjacent even/odd positions");
+  constexpr int C = D / 16;                       // score MFMA steps
+  constexpr int CQ = D / 64;                      // steps per converting lane
+  constexpr int NDT = D / 32;                     // PV d-tiles
+  constexpr int KBUF = LY::KBUF, VBUF = LY::VBUF, RR = LY::RR;
+  constexpr int KRB = SK::RB, VRB = SV::RB;
+
+  unsigned char* const kbuf = g_lds;
+  unsigned char* const vbuf = g_lds + 2 * KBUF;
+  int32_t* const ids = reinterpret_cast<int32_t*>(g_lds + LY::ID0);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;             // query row of the lane (column of its MFMAs)
+  const int h = lane >> 5;              // key half of its accumulators
+  // conversion: every wave converts a quarter of each tile, K of keys
+  // 8*wave .. 8*wave+7 (lane kk + 8q: half k_h = q & 1, step quarter
+  // k_cq = q >> 1) and V of 16-key group v_grp, keys pkey(v_grp, h,
+  // 4*v_half .. 4*v_half+3) of every operand lane
+  const int kk = lane & 7, k_h = (lane >> 3) & 1, k_cq = lane >> 4;
+  const int kslot = 8 * wave + kk + 32 * k_h;     // the operand lane it fills
+  const int v_grp = wave >> 1, v_half = wave & 1;
+  const int R = a.Tq * a.r;
+  const int QG = (R + kWRows - 1) / kWRows;
+  const int n_units = a.B * a.p_max * a.Hkv * QG;
+  const int Gd = gridDim.x;
+  const int logical = xcd_logical(blockIdx.x, Gd);
+
+  const uint32_t kstride = uint32_t(a.Hkv) * KRB;
+  const uint32_t vstride = uint32_t(a.Hkv) * VRB;
+  // where the lane's conversion job reads inside a staged raw tile
+  // where the lane's conversion reads inside a staged raw tile
+  const uint32_t k_row = uint32_t(((8 * wave + kk) >> 4) * SK::GB + ((8 * wave + kk) & 15) * KRB);
+  const auto vl = VF::lane(li);
+  const uint32_t v_row0 = uint32_t(2 * SK::GB + v_grp * SV::GB + pkey(0, h, 4 * v_half) * VRB);
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const int seg_tokens = kWNid << a.bs_shift;
+  // DMA instructions this wave issues per tile
+  const int n_dma = (LY::NT + 3 - wave) / 4;
+
+  for (int u = logical; u < n_units; u += Gd) {
+    // ---- locate the unit: ((b*p_max + p)*Hkv + g)*QG + qg ------------------
+    const int qg = u % QG;
+    const int g = (u / QG) % a.Hkv;
+    const int bp = u / (QG * a.Hkv);
+    const int b = bp / a.p_max;
+    const int p = bp - b * a.p_max;
+    int L = a.seq_len[b];
+    if (L < 0 || L > a.cap_tokens) {
+      if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
+      L = L < 0 ? 0 : a.cap_tokens;
+    }
+    if (L > 0 && L < a.Tq) {             // the chunk is longer than the sequence
+      if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
+      L = 0;
+    }
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int P = L > 0 ? (L + a.psize - 1) / a.psize : 0;
+    const int t_begin = p * a.psize;
+    const int t_end = min(L, t_begin + a.psize);
+    // this lane's query row
+    const int row = qg * kWRows + 32 * wave + li;
+    const bool valid = row < R;
+    const int tq = valid ? row / a.r : 0;
+    const int hq = g * a.r + (valid ? row - tq * a.r : 0);
+    const int64_t orow = (int64_t(b) * a.Tq + tq) * a.Hq + hq;   // row of out / partials
+    const int lim = valid ? min(L - a.Tq + tq, t_end - 1) : t_begin - 1;
+    if (L == 0) {
+      // an empty (or refused) sequence: zero rows in direct mode; the merge
+      // writes its zero rows otherwise
+      if (a.direct && valid && h == 0)
+        for (int d = 0; d < D; ++d) a.out[orow * D + d] = 0.0f;
+      continue;
+    }
+    if (p >= P) continue;                 // no such partition: nothing to write
+    int lim_min = valid ? lim : INT32_MAX;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+    lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+    const bool wave_rows = __any(valid);
+    // last key any row of the workgroup reads: that of its last valid row
+    const int row_hi = min(R - 1, qg * kWRows + kWRows - 1);
+    const int t_stop = min(t_end, L - a.Tq + row_hi / a.r + 1);
+
+    // ---- Q^T operands: slot s of step c holds q[row][kd(c, h, s)] ----------
+    f16x8 qop[C];
+    {
+      const float* qr = a.q + orow * D;
+      const float keep = valid ? a.qscale : 0.0f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        // kd(c, h, 0..7) is 8 consecutive positions in word_order
+        const float* q8 = qr + (KF::kd(c, h, 0) & ~7);
+        const float4 A = valid ? *reinterpret_cast<const float4*>(q8) : float4{0, 0, 0, 0};
+        const float4 B = valid ? *reinterpret_cast<const float4*>(q8 + 4) : float4{0, 0, 0, 0};
+        const float v[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qop[c][s] = f16(v[KF::kd(0, 0, s)] * keep);
+        // Q^T stays in AGPRs (the MFMAs read their B operand from there),
+        // leaving the VGPRs to the operand reads, softmax and conversion
+        asm volatile("" : "+a"(qop[c]));
+      }
+    }
+
+    // reference max: +inf for rows past R (their p are exactly 0); -inf until
+    // the row has seen a key
+    float m_run = valid ? -INFINITY : INFINITY;
+    float l_lane = 0.0f;
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+    int bad = 0;
+
+    // ---- one tile's steps (scores, softmax, PV) and the conversion job, in
+    // two regions per tile with no branch inside, so the scheduler can put
+    // VALU work between the MFMAs (a wave issues in order, and at one wave
+    // per SIMD nothing else fills the gaps) -------------------------------------
+    // the causal and end-of-partition mask of the scores of the tile at t0
+    // (a branch, taken only where some row's limit falls inside the tile)
+    auto mask = [&](f32x16& s, int t0) __attribute__((always_inline)) {
+      if (t0 + kWTile - 1 > lim_min) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t0 + skey(r, h) > lim) s[r] = -INFINITY;
+      }
+    };
+    // S^T = K Q^T over the D/16 steps, read by the softmax an iteration later
+    auto scores = [&](const unsigned char* kops, f32x16& sc) __attribute__((always_inline)) {
+      f16x8 kop[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) kop[c] = *reinterpret_cast<const f16x8*>(kops + (c * 64 + lane) * 16);
+      sc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C; ++c) sc = mfma32(kop[c], qop[c], sc);
+    };
+    auto row_max = [&](const f32x16& s) __attribute__((always_inline)) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    // lazy rescale (lucebox PR #555, Summary: skip the rescale when the max is
+    // unchanged): the reference moves only when a row's max exceeds it by more
+    // than kSlack; rows with no key yet (m = -inf) and rows past R (m = +inf)
+    // keep their sums as they are
+    auto rescale = [&](float mx) __attribute__((always_inline)) {
+      // a scalar branch around the rare rescale: taken by the whole wave or
+      // skipped (the asm keeps the compiler from running it on every tile
+      // with a factor of 1)
+      if (__builtin_amdgcn_readfirstlane(__any(mx > m_run + kSlack) ? 1 : 0)) {
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_lane *= alpha;
+        // element by element through a VGPR: the accumulators stay in AGPRs
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[dt][r]));
+            x *= alpha;
+            asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(acc[dt][r]) : "v"(x));
+          }
+        m_run = m_new;
+      }
+    };
+    // exp2 of the scores against the reference, their sum, P^T operands
+    auto probs = [&](const f32x16& s, f16x8 (&pop)[2]) __attribute__((always_inline)) {
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) ls += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+      l_lane += ls;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pop[t][e] = f16(pr[8 * t + e]);
+    };
+    // O^T += V^T P^T over the tile's two 16-key steps
+    auto pv_load = [&](const unsigned char* vops, f16x8 (&vop)[2][NDT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vop[t][dt] = *reinterpret_cast<const f16x8*>(vops + ((t * NDT + dt) * 64 + lane) * 16);
+    };
+    auto pv_mfma = [&](const f16x8 (&vop)[2][NDT], const f16x8 (&pop)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma32(vop[t][dt], pop[t], acc[dt]);
+    };
+
+    for (int seg_t0 = t_begin; seg_t0 < t_stop; seg_t0 += seg_tokens) {
+      const int seg_t1 = min(t_stop, seg_t0 + seg_tokens);
+      const int jb0 = seg_t0 >> a.bs_shift;
+      const int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // ids[] and every LDS buffer are free
+      int badl = 0;
+      for (int i = tid; i < nb; i += kWThreads) {
+        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
+      }
+      bad |= __syncthreads_or(badl);
+      const int ntiles = (seg_t1 - seg_t0 + kWTile - 1) / kWTile;
+
+      // ---- DMA of tile t's raw rows into ring slot t % RR --------------------
+      auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint32_t slot = uint32_t(LY::RAW + (t % RR) * LY::SLOT);
+        const int t0 = seg_t0 + t * kWTile;
+        switch (wave) {
+          case 0: issue_tile_as<LY, 0>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
+          case 1: issue_tile_as<LY, 1>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
+          case 2: issue_tile_as<LY, 2>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
+          default: issue_tile_as<LY, 3>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
+        }
+      };
+      // ---- this wave's quarter of the conversion of tile kt: staged raw rows
+      // into f16 operands in LDS (a tile past the segment converts whatever
+      // the ring holds into buffers nothing reads) -----------------------------
+      struct ConvRaw { uint32_t kw[KF::kWords], vw[VF::kWords]; };
+      auto conv_load = [&](int kt, ConvRaw& cr) __attribute__((always_inline)) {
+        const unsigned char* raw = g_lds + LY::RAW + (kt % RR) * LY::SLOT;
+        KF::load(cr.kw, raw + k_row, k_h, k_cq);
+        VF::load(cr.vw, raw + v_row0, vl);
+      };
+      auto conv_store = [&](int kt, ConvRaw& cr) __attribute__((always_inline)) {
+        // keys past the segment (junk slots, maybe NaN) are zeroed: their p
+        // is 0, and 0 * NaN would not be
+        const int t0 = seg_t0 + kt * kWTile + 16 * v_grp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (t0 + pkey(0, h, 4 * v_half + e) >= seg_t1) VF::kill(cr.vw, e);
+        VF::prep(cr.vw, vl);
+        unsigned char* kops = kbuf + (kt & 1) * KBUF;
+#pragma unroll
+        for (int cc = 0; cc < CQ; ++cc)
+          *reinterpret_cast<f16x8*>(kops + ((k_cq * CQ + cc) * 64 + kslot) * 16) = KF::op(cr.kw, cc, k_cq, mg);
+        unsigned char* vops = vbuf + (kt % 3) * VBUF;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f16x4*>(vops + ((v_grp * NDT + dt) * 64 + lane) * 16 + 8 * v_half) =
+              VF::op(cr.vw, vl, dt, mg);
+      };
+      auto convert = [&](int kt) __attribute__((always_inline)) {
+        ConvRaw cr;
+        conv_load(kt, cr);
+        conv_store(kt, cr);
+      };
+
+      // ---- the pipeline: one barrier per tile. Iteration kt issues the DMA
+      // of tile kt+RR+1, computes the scores of kt+1, converts kt+2 and runs
+      // the softmax and PV of kt; before its barrier the DMA of kt+3 has
+      // landed (RR-2 tiles of DMA stay in flight). ---------------------------
+      f32x16 s0, s1;
+#pragma unroll
+      for (int t = 0; t < RR; ++t) issue(t);
+      wait_dma_then_barrier((RR - 1) * n_dma);
+      convert(0);
+      wait_dma_then_barrier((RR - 2) * n_dma);
+      issue(RR);
+      scores(kbuf, s0);
+      convert(1);
+      wait_dma_then_barrier((RR - 2) * n_dma);
+      auto step = [&](int kt, f32x16& s_cur, f32x16& s_next) __attribute__((always_inline)) {
+        issue(kt + RR + 1);
+        mask(s_cur, seg_t0 + kt * kWTile);
+        ConvRaw cr;
+        f16x8 vop[2][NDT];
+        if constexpr (kStepOrder == 0) {
+          // region 1: scores of kt+1, the row max of kt, conversion of kt+2
+          // (its staged-row reads first: LDS returns in order)
+          conv_load(kt + 2, cr);
+          __builtin_amdgcn_sched_barrier(0);
+          scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
+          const float mx = row_max(s_cur);
+          conv_store(kt + 2, cr);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          }
+          rescale(mx);
+          // region 2: probabilities and PV of kt
+          pv_load(vbuf + (kt % 3) * VBUF, vop);
+          f16x8 pop[2];
+          probs(s_cur, pop);
+          pv_mfma(vop, pop);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+#pragma unroll
+          for (int i = 0; i < 2 * NDT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+          }
+        } else {
+          // region 1: scores of kt+1 and the row max of kt
+          scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
+          const float mx = row_max(s_cur);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+          rescale(mx);
+          // region 2: probabilities and PV of kt beside the conversion of
+          // kt+2 (its staged-row reads and the V operand reads first)
+          conv_load(kt + 2, cr);
+          pv_load(vbuf + (kt % 3) * VBUF, vop);
+          __builtin_amdgcn_sched_barrier(0);
+          f16x8 pop[2];
+          probs(s_cur, pop);
+          pv_mfma(vop, pop);
+          conv_store(kt + 2, cr);
+          __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+#pragma unroll
+          for (int i = 0; i < 2 * NDT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
+          }
+        }
+        // the accumulators are carried from tile to tile in AGPRs (without
+        // this the compiler moves all of them to VGPRs and back every tile)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
+        wait_dma_then_barrier((RR - 2) * n_dma);
+      };
+      for (int kt = 0; kt < ntiles; kt += 2) {
+        step(kt, s0, s1);
+        if (kt + 1 >= ntiles) break;
+        step(kt + 1, s1, s0);
+      }
+      // the DMA of tiles past the segment (zeros) lands before the ring is reused
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // ---- partial (or final) rows -------------------------------------------
+    mfma_drain();                          // the last tile's PV MFMAs wrote acc
+    if (bad && tid == 0) atomicOr(a.status, 1u);
+    float l_run;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+      l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (!valid) continue;
+    const float inv = bad ? __builtin_nanf("") : (l_run > 0.0f ? 1.0f / l_run : 0.0f);
+    if (a.direct) {
+      float* dst = a.out + orow * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[VF::vd(dt, skey(r, h))] = acc[dt][r] * inv;
+    } else {
+      const int64_t prow = orow * a.p_max + p;
+      f16* dst = reinterpret_cast<f16*>(a.part_o) + prow * D;
+      if (h == 0) {
+        a.part_ml[2 * prow] = bad ? __builtin_nanf("") : (l_run > 0.0f ? m_run : -INFINITY);
+        a.part_ml[2 * prow + 1] = l_run;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int dn = VF::dnext(dt);
+        if (dn < 0) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          store_f16_pair(dst, VF::vd(dt, skey(r, h)), acc[dt][r] * inv, acc[dn][r] * inv);
+      }
+    }
+  }
+}
+
+template <int KT, int VT, int D>
+hipError_t launch_wide(const ChunkArgs& a, hipStream_t stream) {
+  constexpr size_t lds = WideLds<KT, VT, D>::BYTES;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&chunk_wide_kernel<KT, VT, D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((chunk_wide_kernel<KT, VT, D>), dim3(a.grid), dim3(kWThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_wide_d(const ChunkArgs& a, hipStream_t stream) {
+  switch (a.k_type * 3 + a.v_type) {
+    case 0: return launch_wide<kF16, kF16, D>(a, stream);
+    case 1: return launch_wide<kF16, kQ8_0, D>(a, stream);
+    case 2: return launch_wide<kF16, kQ4_0, D>(a, stream);
+    case 3: return launch_wide<kQ8_0, kF16, D>(a, stream);
+    case 4: return launch_wide<kQ8_0, kQ8_0, D>(a, stream);
+    case 5: return launch_wide<kQ8_0, kQ4_0, D>(a, stream);
+    case 6: return launch_wide<kQ4_0, kF16, D>(a, stream);
+    case 7: return launch_wide<kQ4_0, kQ8_0, D>(a, stream);
+    case 8: return launch_wide<kQ4_0, kQ4_0, D>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_wide(const ChunkArgs& a, hipStream_t stream) {
+  if (a.D == 256) return launch_wide_d<256>(a, stream);
+  if (a.D == 128) return launch_wide_d<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -162,6 +162,15 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
 // one kv head with all of its Tq*r query rows (chunk_window_ok); pools
 // 16-byte aligned.
 hipError_t launch_chunk_lds(const ChunkArgs& a, hipStream_t stream);
+// The wide-tile kernel (chunk_wide.hip): 32x32 MFMA tiles, a workgroup per
+// kv head and 128 query rows, one per CU (prefill chunks); 16-byte aligned
+// pools and q.
+hipError_t launch_chunk_wide(const ChunkArgs& a, hipStream_t stream);
+constexpr int kWideRows = 128;
+// Whether the plan picks the wide-tile kernel for a chunk with `rows` query
+// rows per kv head that the window kernel does not take: from 65 rows on,
+// where the tile kernel needs a second 64-row block.
+constexpr bool chunk_wide_pick(int64_t rows, int D) { return (D == 128 || D == 256) && rows > 64; }
 // Query tiles per wave of the chunk kernel for R = Tq*r rows per kv head (a
 // workgroup of four waves takes 64*nt rows; two tiles per wave fit the
 // registers at D = 128 only), and its workgroups per CU (two waves per SIMD

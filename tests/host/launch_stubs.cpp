@@ -15,6 +15,7 @@ hipError_t launch_decode_regs(const DecodeArgs&, hipStream_t) { return hipErrorN
 hipError_t launch_decode_lds(const DecodeArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_chunk(const ChunkArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_chunk_lds(const ChunkArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
+hipError_t launch_chunk_wide(const ChunkArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_copy_blocks(const CopyBlocksArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_table_update(const TableUpdateArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { return hipErrorNoBinaryForGpu; }

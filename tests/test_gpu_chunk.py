@@ -4,9 +4,10 @@ paged equals contiguous bit for bit) against oracle.chunk, through the C ABI.
 
 Tolerance as for decode (per-row max-abs error relative to the row's
 max-abs output): 2e-3 when K and V are F16, 5e-3 when either is quantised.
-Two kernels compute a chunk (plan path 1: tile conversion for any Tq; path
-2: the window kernel for few query rows per kv head); the tests marked with
-a `path` parameter run each on the same inputs."""
+Three kernels compute a chunk (plan path 1: tile conversion for any Tq;
+path 2: the window kernel for few query rows per kv head; path 3: the
+wide-tile kernel for many); the tests marked with a `path` parameter run
+each on the same inputs."""
 import dataclasses
 
 import numpy as np
@@ -45,15 +46,22 @@ def window_ok(c, Tq):
             and (rows <= 32 or (rows <= 48 and (c.D == 128 or q4))))
 
 
+def wide_ok(c, Tq):
+    """Whether the plan picks the wide-tile kernel (plan path 3): a chunk the
+    window kernel does not take with more than 64 query rows per kv head."""
+    return not window_ok(c, Tq) and Tq * (c.Hq // c.Hkv) > 64
+
+
 def _plan(c, Tq, path=None, **kw):
-    """paged_attn_chunk_plan for the case; path=1/2 forces the kernel (a chunk
-    the window kernel does not take is skipped for path 2)."""
+    """paged_attn_chunk_plan for the case; path=1/2/3 forces the kernel (a
+    chunk the window kernel does not take is skipped for path 2; the tile and
+    wide-tile kernels take any)."""
     pa = pa_mod()
     shape = pa.shape_of(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.nblocks, c.max_blocks, c.k_fmt,
                         c.v_fmt)
     plan = pa.paged_attn_chunk_plan(shape, Tq, max(c.seq_lens), total_tokens=sum(c.seq_lens),
                                     scale=c.scale, **kw)
-    assert plan.path == (2 if window_ok(c, Tq) else 1)
+    assert plan.path == (2 if window_ok(c, Tq) else 3 if wide_ok(c, Tq) else 1)
     if path is not None:
         if path == 2 and not window_ok(c, Tq):
             pytest.skip("the window kernel does not take this chunk")
@@ -61,7 +69,7 @@ def _plan(c, Tq, path=None, **kw):
     return plan
 
 
-PATHS = [1, 2]
+PATHS = [1, 2, 3]
 
 
 def _run(c, qc, plan, table="case"):
@@ -98,6 +106,22 @@ def test_nine_type_pairs(pair, D):
     c, qc = _case([300, 77, 16], 9, seed=seed, k_fmt=pair[0], v_fmt=pair[1], D=D)
     for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 64}):
         out, ws = _run(c, qc, _plan(c, 9, **kw))
+        _check(c, qc, out)
+        assert pa_mod().paged_attn_status(ws) == 0
+
+
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("pair", PAIRS, ids=[f"{k}-{v}" for k, v in PAIRS])
+def test_nine_type_pairs_wide(pair, D):
+    """A 24-token chunk (144 query rows per kv head: a full and a partial
+    128-row block) on the plan's wide-tile kernel, with one and several
+    partitions."""
+    seed = 3 * synth.FORMATS.index(pair[0]) + synth.FORMATS.index(pair[1]) + D + 301
+    c, qc = _case([300, 77, 40], 24, seed=seed, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    for kw in ({}, {"force_partitions": 1}, {"partition_tokens": 64}):
+        plan = _plan(c, 24, **kw)
+        assert plan.path == 3
+        out, ws = _run(c, qc, plan)
         _check(c, qc, out)
         assert pa_mod().paged_attn_status(ws) == 0
 
@@ -157,7 +181,7 @@ def test_tq_one_is_a_decode_step(path):
 def test_paged_equals_contiguous_bitwise_and_deterministic(pair, path):
     """TensorFold PR #1418, What: the paged chunk equals the contiguous one bit
     for bit (same tiles in the same order); repeated runs agree bit for bit."""
-    Tq = 12 if path == 1 else 4
+    Tq = {1: 12, 2: 4, 3: 24}[path]
     c, qc = _case([333, 64, 190], Tq, seed=7, k_fmt=pair[0], v_fmt=pair[1])
     cc = synth.contiguous_copy(c)
     for kw in ({}, {"partition_tokens": 64}):
@@ -234,9 +258,29 @@ def test_both_kernels_agree(pair, D, heads, rows):
         _check(c, qc, o2)
 
 
-def test_unaligned_pools_run_the_tile_kernel():
+@pytest.mark.parametrize("rows", [72, 144, 384])
+@pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "q4_0"), ("f16", "q8_0")])
+@pytest.mark.parametrize("D", [256, 128])
+def test_wide_and_tile_kernels_agree(pair, D, rows):
+    """The same chunk on the tile and wide-tile kernels with the same
+    partitioning, to the format tolerance (they convert the quantised values
+    alike but accumulate in a different order)."""
+    Tq = rows // 6
+    c, qc = _case([2000, 700, 90], Tq, seed=131 + D + rows, k_fmt=pair[0], v_fmt=pair[1], D=D)
+    for kw in ({}, {"partition_tokens": 256}):
+        o1, _ = _run(c, qc, _plan(c, Tq, path=1, **kw))
+        o3, _ = _run(c, qc, _plan(c, Tq, path=3, **kw))
+        g1, g3 = o1.cpu().double().numpy(), o3.cpu().double().numpy()
+        assert np.isfinite(g3).all()
+        assert float(rel_err_rows(g3, g1).max()) <= tol_for(c)
+        _check(c, qc, o3)
+
+
+@pytest.mark.parametrize("path", [2, 3])
+def test_unaligned_pools_run_the_tile_kernel(path):
     """Pools that are not 16-byte aligned run the tile-conversion kernel even
-    under a window plan: the result equals a path-1 run bit for bit."""
+    under a window or wide-tile plan: the result equals a path-1 run bit for
+    bit."""
     c, qc = _case([500, 77], 4, seed=231, k_fmt="q4_0", v_fmt="q8_0")
     g = c.to(DEV)
 
@@ -247,7 +291,7 @@ def test_unaligned_pools_run_the_tile_kernel():
         assert view.data_ptr() % 16 == 4
         return view
 
-    plan2 = _plan(c, 4, path=2, partition_tokens=128)
+    plan2 = _plan(c, 4, path=path, partition_tokens=128)
     plan1 = _plan(c, 4, path=1, partition_tokens=128)
     pa = pa_mod()
     outs = []
@@ -261,17 +305,18 @@ def test_unaligned_pools_run_the_tile_kernel():
     _check(c, qc, outs[0])
 
 
-def test_unaligned_q_runs_the_tile_kernel():
+@pytest.mark.parametrize("path", [2, 3])
+def test_unaligned_q_runs_the_tile_kernel(path):
     """A q that is not 16-byte aligned runs the tile-conversion kernel even
-    under a window plan (whose kernel reads q with 16-byte loads): the result
-    equals a path-1 run bit for bit."""
+    under a window or wide-tile plan (whose kernels read q with 16-byte
+    loads): the result equals a path-1 run bit for bit."""
     c, qc = _case([500, 77], 4, seed=237, k_fmt="q4_0", v_fmt="q4_0")
     g = c.to(DEV)
     raw = torch.empty(qc.numel() + 1, dtype=torch.float32, device=DEV)
     qu = raw[1:].view(qc.shape)
     qu.copy_(qc.to(DEV))
     assert qu.data_ptr() % 16 == 4
-    plan2 = _plan(c, 4, path=2, partition_tokens=128)
+    plan2 = _plan(c, 4, path=path, partition_tokens=128)
     plan1 = _plan(c, 4, path=1, partition_tokens=128)
     pa = pa_mod()
     outs = []
@@ -319,6 +364,54 @@ def test_verify_windows_at_full_size(Tq):
         assert np.isfinite(got).all(), f"sequence {b}: non-finite output"
         worst = float(rel_err_rows(got, ref).max())
         assert worst <= tol_for(case), f"sequence {b}: max row error {worst:.3e}"
+    del case, ws, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pair", [("q4_0", "q4_0"), ("q8_0", "f16")])
+def test_wide_partition_longer_than_a_segment(pair):
+    """One partition of 9000 keys: the wide-tile kernel stages 512 block ids
+    (8192 tokens at 16 per block) at a time and restarts its tile pipeline
+    for the second segment."""
+    c, qc = _case([9000, 300], 16, seed=88, k_fmt=pair[0], v_fmt=pair[1])
+    plan = _plan(c, 16, force_partitions=1)
+    assert plan.path == 3 and plan.direct
+    out, ws = _run(c, qc, plan)
+    _check(c, qc, out)
+    assert pa_mod().paged_attn_status(ws) == 0
+
+
+def test_prefill_chunk_at_full_size():
+    """The chunk benchmark's prefill chunk: 512 tokens over a Q4_0 sequence
+    of 8192 (3072 query rows per kv head) on the plan's wide-tile kernel. Its
+    last 6 tokens are checked against the oracle as a 6-token chunk of the
+    same sequence, and its first 6 as a 6-token chunk of the sequence cut
+    after them (the keys each token sees are the same)."""
+    pa = pa_mod()
+    Tq, L = 512, 8192
+    case = synth.workload("uniform_q4_0", B=1, L=L, seed=1700, device=DEV)
+    qc = torch.randn((1, Tq, case.Hq, case.D), generator=torch.Generator().manual_seed(1701))
+    shape = pa.shape_of(case.B, case.Hq, case.Hkv, case.D, case.block_size, case.nblocks,
+                        case.max_blocks, case.k_fmt, case.v_fmt)
+    plan = pa.paged_attn_chunk_plan(shape, Tq, L, total_tokens=L, scale=case.scale)
+    assert plan.path == 3
+    ws = pa.workspace(plan, DEV)
+    out = torch.full(tuple(qc.shape), float("nan"), dtype=torch.float32, device=DEV)
+    pa.paged_attn_chunk(plan, qc.to(DEV), case.k_pool, case.v_pool, case.table, case.seq_len, ws, out)
+    torch.cuda.synchronize()
+    assert pa.paged_attn_status(ws) == 0
+    got = out.cpu()
+    assert torch.isfinite(got).all()
+    kp, vp = case.k_pool.cpu().numpy().reshape(-1), case.v_pool.cpu().numpy().reshape(-1)
+    tab = case.table.cpu()
+    for first in (False, True):
+        toks = slice(0, 6) if first else slice(Tq - 6, Tq)
+        n = L - Tq + 6 if first else L
+        ref = oracle.chunk(qc[:, toks], kp, vp, tab, torch.tensor([n], dtype=torch.int32), Hkv=case.Hkv,
+                           D=case.D, block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
+                           nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
+        worst = float(rel_err_rows(got[:, toks].double().numpy(), ref).max())
+        assert worst <= tol_for(case), f"tokens {toks}: max row error {worst:.3e}"
     del case, ws, out
     torch.cuda.empty_cache()
 

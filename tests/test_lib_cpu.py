@@ -323,7 +323,8 @@ def test_copy_blocks_refusals_before_any_launch():
 
 def test_chunk_plan_partitions_and_workspace():
     """paged_attn_chunk_plan: a four-wave workgroup per (sequence, partition,
-    kv head, 64 query rows at D=256), two per compute unit; partials of 2D+8
+    kv head, 64 query rows at D=256), two per compute unit, or per 128 query
+    rows on the wide-tile kernel, one per compute unit; partials of 2D+8
     bytes per query row and partition."""
     p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.tq == 9 and p.psize % 32 == 0 and p.direct == 0 and p.path == 1
@@ -331,7 +332,7 @@ def test_chunk_plan_partitions_and_workspace():
     units = 8 * p.p_max * 4 * 1                      # 9*6 = 54 rows per kv head: one block
     assert p.grid == min(units, 256 * 2)
     big = pa.paged_attn_chunk_plan(_shape(B=1), 512, 8192, num_cus=256)
-    assert big.grid == min(1 * big.p_max * 4 * 48, 512)      # 3072 rows: 48 blocks of 64
+    assert big.path == 3 and big.grid == min(1 * big.p_max * 4 * 24, 256)   # 3072 rows: 24 blocks of 128
     assert p.part_offset == 256 + 8 * 4160
     assert p.ws_bytes == -(-(p.part_offset + 8 * 9 * 24 * p.p_max * (2 * 256 + 8)) // 256) * 256
     d = pa.paged_attn_chunk_plan(_shape(B=1), 16, 200, num_cus=256)
@@ -344,9 +345,11 @@ def test_chunk_plan_kernel_choice():
     """The window kernel (path 2) for at most 48 query rows per kv head: a
     workgroup per (sequence, partition, kv-head quad), except 17..48 rows at
     D=256, where the head dimension is split over two waves and a workgroup
-    takes a kv-head pair, two per compute unit; the tile-conversion kernel
-    (path 1) otherwise. A plan forced to path 2 where it does not apply is
-    refused before launch."""
+    takes a kv-head pair, two per compute unit; the wide-tile kernel (path 3)
+    for more than 64 rows, a workgroup per (sequence, partition, kv head, 128
+    rows), one per compute unit; the tile-conversion kernel (path 1)
+    otherwise. A plan forced to path 2 where it does not apply, or to a path
+    that does not exist, is refused before launch."""
     p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.path == 1                                   # 54 rows
     w8 = pa.paged_attn_chunk_plan(_shape(), 8, 32768, total_tokens=8 * 32768, num_cus=256)
@@ -360,12 +363,17 @@ def test_chunk_plan_kernel_choice():
     w128 = pa.paged_attn_chunk_plan(_shape(D=128), 8, 32768, total_tokens=8 * 32768, num_cus=256)
     assert w128.path == 2                                # 48 rows at D=128
     assert pa.paged_attn_chunk_plan(_shape(D=128), 9, 32768, num_cus=256).path == 1
+    for D in (256, 128):
+        wide = pa.paged_attn_chunk_plan(_shape(D=D), 12, 32768, total_tokens=8 * 32768, num_cus=256)
+        assert wide.path == 3 and wide.grid == min(8 * wide.p_max * 4 * 1, 256)    # 72 rows
+        pre = pa.paged_attn_chunk_plan(_shape(D=D, B=1), 512, 8192, total_tokens=8192, num_cus=256)
+        assert pre.path == 3 and pre.grid == min(pre.p_max * 4 * 24, 256)         # 3072 rows
     p.path = 2
     with pytest.raises(pa.PaError) as e:
         pa.paged_attn_chunk(p, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
                             stream=0, ws_bytes=int(p.ws_bytes))
     assert e.value.code == pa.PA_ERR_UNSUPPORTED and "window" in str(e.value)
-    w.path = 3
+    w.path = 4
     with pytest.raises(pa.PaError) as e:
         pa.paged_attn_chunk(w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
                             stream=0, ws_bytes=int(w.ws_bytes))
