@@ -329,17 +329,20 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * PA_STATUS_BAD_SEQ_LEN. The key range is cut into partitions whose
  * partials (the decode layout with Tq*Hq rows per sequence) are reduced by
  * the same max-shifted merge; one partition writes out directly.
- * Two kernels compute it: path 1 converts each key/value tile once per
- * workgroup into LDS for four waves of query rows (any Tq); path 2, for
+ * Three kernels compute it: path 1 converts each key/value tile once per
+ * workgroup into LDS for four waves of 16 query rows (any Tq); path 2, for
  * Tq*Hq/Hkv <= 32 query rows per kv head at D = 256 (48 at D = 128, and at
  * D = 256 with Q4_0 K and V) with Hkv a multiple of 4 (verify windows),
  * streams the pool through the decode kernel's LDS ring, each wave serving
  * one kv head with all of its rows (at D = 256 with more than 16 rows, two
  * waves per kv head, each over half of the head dimension, adding their
- * partial scores through LDS). The
- * plan picks path 2 where it applies; a caller may set path = 1 on such a
- * plan to force the general kernel. Pools or q that are not 16-byte aligned
- * run path 1.
+ * partial scores through LDS); path 3, for more than 64 query rows per kv
+ * head (prefill chunks), converts each tile once per workgroup for four
+ * waves of 32 rows on 32x32 MFMAs (at D = 256 the plan takes it only where
+ * its 128-row blocks are as full as 64-row ones and its units fill the
+ * compute units). The plan picks path 2 or 3 where it applies; a caller may
+ * set path = 1 on any plan, or 3 on one for path 1, to force that kernel.
+ * Pools or q that are not 16-byte aligned run path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;
@@ -351,7 +354,8 @@ typedef struct pa_chunk_plan {
   int32_t grid;         /* workgroups (four wave64s each) */
   int32_t num_cus;
   int32_t direct;       /* 1: one partition, no merge */
-  int32_t path;         /* 1: tile-conversion kernel, 2: window kernel */
+  int32_t path;         /* 1: tile-conversion kernel, 2: window kernel,
+                           3: wide-tile kernel */
   uint64_t ws_bytes;    /* workspace: header + partials (part_offset +
                            B*Tq*Hq*p_max*(2D+8) bytes when direct == 0) */
   uint64_t part_offset; /* byte offset of the partials in ws: the decode

@@ -501,28 +501,15 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   if (num_cus < 1) return fail(PA_ERR_INVALID, "%s: num_cus must be >= 1", who);
   const int64_t L = max_seq_len;
   const int64_t r = s.Hq / s.Hkv;
-  // the window kernel takes short chunks (a workgroup per kv-head quad, two
-  // per CU for at most 16 query rows per kv head, else one; with the head
-  // dimension split, a workgroup per kv-head pair, two per CU); the wide-tile
-  // kernel long ones (a workgroup per kv head and 128 query rows, one per
-  // CU); the tile-conversion kernel the rest (a workgroup per kv head and
-  // 64*nt query rows, one or two per CU)
   const bool window = chunk_window_ok(int64_t(tq) * r, s.Hkv, s.k_type, s.v_type, s.D);
-  const bool wide = !window && chunk_wide_pick(int64_t(tq) * r, s.D);
   const int nt = chunk_wave_tiles(int64_t(tq) * r, s.D);
-  const int64_t block_rows = wide ? kWideRows : 64 * nt;
-  const int64_t qt = window ? 1 : (int64_t(tq) * r + block_rows - 1) / block_rows;   // row blocks per unit
   const int nq = int(ceil_div(int64_t(tq) * r, 16));
-  const int64_t heads_per_unit = window ? chunk_window_heads(nq, s.D) : 1;
-  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D, s.k_type, s.v_type)
-                                : (wide ? 1 : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D));
   const int64_t tok = total_tokens > 0 ? total_tokens : int64_t(s.B) * L;
-  int64_t psize;
-  if (partition_tokens > 0) {
-    psize = round_up(partition_tokens, kTileTokens);
-  } else if (force_partitions >= 1) {
-    psize = round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
-  } else {
+  // Partition size for units of qt row blocks of heads_per_unit kv heads,
+  // wgs_per_cu workgroups per compute unit.
+  auto size_partitions = [&](int64_t qt, int64_t heads_per_unit, int wgs_per_cu) {
+    if (partition_tokens > 0) return round_up(partition_tokens, kTileTokens);
+    if (force_partitions >= 1) return round_up(std::max<int64_t>(1, ceil_div(L, force_partitions)), kTileTokens);
     // Occupancy-aware partitioning (lucebox PR #555, Summary), counting the
     // workgroups a compute unit holds. Partials cost 2D+8 bytes per query row
     // and partition, written and read once; a partition is never so short
@@ -540,7 +527,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
     const double floor_mfma = part * kFlopsPerByte / (0.25 * double(tq) * s.Hq * 4.0 * s.D);
     const int64_t floor_tok = std::max<int64_t>(
         round_up(int64_t(std::ceil(std::min(floor_hbm, floor_mfma))), kTileTokens), 128);
-    psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
+    int64_t ps_best = round_up(std::max<int64_t>(L, 1), kTileTokens);
     int64_t best = -1;
     for (int64_t parts = 1; parts <= 64; ++parts) {
       const int64_t ps = round_up(std::max<int64_t>(1, ceil_div(L, parts)), kTileTokens);
@@ -548,9 +535,41 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
       const int64_t bp = std::min<int64_t>(int64_t(s.B) * ceil_div(std::max<int64_t>(L, 1), ps),
                                            ceil_div(tok, ps) + s.B);
       const int64_t cost = ceil_div(std::max<int64_t>(1, bp * (s.Hkv / heads_per_unit) * qt), slots) * ps;
-      if (best < 0 || cost < best) { best = cost; psize = ps; }
+      if (best < 0 || cost < best) { best = cost; ps_best = ps; }
+    }
+    return ps_best;
+  };
+  // The wide-tile kernel takes chunks of more than 64 query rows per kv head.
+  // At D = 256 it does where its 128-row blocks are no emptier than the tile
+  // kernel's 64-row ones and its units fill the compute units (one
+  // workgroup each); otherwise the tile kernel, two per compute unit, was
+  // measured faster (B=8 x 32K Q4_0: 192 rows 483 against 438 us; a 64-token
+  // chunk over 8K, 72 units: 96 against 85 us).
+  const int64_t rows = int64_t(tq) * r;
+  bool wide = !window && chunk_wide_pick(rows, s.D);
+  int64_t psize = 0;
+  if (wide) {
+    const int64_t qt_w = ceil_div(rows, int64_t(kWideRows));
+    psize = size_partitions(qt_w, 1, 1);
+    if (s.D == 256) {
+      const int64_t qt_t = ceil_div(rows, int64_t(64 * nt));
+      const int64_t units_w =
+          int64_t(s.B) * std::max<int64_t>(1, ceil_div(std::max<int64_t>(L, 1), psize)) * s.Hkv * qt_w;
+      if (qt_w * kWideRows > qt_t * 64 * nt || units_w < num_cus) wide = false;
     }
   }
+  // the window kernel takes short chunks (a workgroup per kv-head quad, two
+  // per CU for at most 16 query rows per kv head, else one; with the head
+  // dimension split, a workgroup per kv-head pair, two per CU); the wide-tile
+  // kernel long ones (a workgroup per kv head and 128 query rows, one per
+  // CU); the tile-conversion kernel the rest (a workgroup per kv head and
+  // 64*nt query rows, one or two per CU)
+  const int64_t block_rows = wide ? kWideRows : 64 * nt;
+  const int64_t qt = window ? 1 : (rows + block_rows - 1) / block_rows;   // row blocks per unit
+  const int64_t heads_per_unit = window ? chunk_window_heads(nq, s.D) : 1;
+  const int wgs_per_cu = window ? chunk_window_wgs_per_cu(nq, s.D, s.k_type, s.v_type)
+                                : (wide ? 1 : chunk_wgs_per_cu(nt, s.k_type, s.v_type, s.D));
+  if (!wide) psize = size_partitions(qt, heads_per_unit, wgs_per_cu);
   if (psize >= L) psize = round_up(std::max<int64_t>(L, 1), kTileTokens);
   if (psize > INT32_MAX - kTileTokens) return fail(PA_ERR_INVALID, "%s: partition size overflows", who);
   const int64_t p_max = std::max<int64_t>(1, ceil_div(L, psize));

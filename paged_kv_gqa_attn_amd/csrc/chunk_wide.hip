@@ -21,20 +21,23 @@
 //   * A workgroup of four wave64s takes a unit (sequence b, key partition p,
 //     kv head g, 128 query rows), wave w owning rows 32w .. 32w+31. A wave
 //     holds its rows' Q operands (D/4 registers) and O^T accumulators (D/2),
-//     so the kernel runs one workgroup per CU with 512 registers per lane.
-//     Every operand the MFMAs read from LDS serves 32 rows: 1 KB per
-//     32x32x16 MFMA, twice the rows per operand byte of the 16x16 tiles of
-//     chunk.hip.
-//   * Every 32-key tile is converted to f16 once per workgroup, into LDS in
-//     MFMA operand order: waves 0 and 1 convert K of 16-key groups 0 and 1,
-//     waves 2 and 3 V of the same groups, each loading its raw rows straight
-//     from the pool through the block table (64-bit row addresses, mlxcel
-//     issue #2153).
+//     so the kernel runs one workgroup per CU with 512 registers per lane:
+//     Q^T and O^T in AGPRs, where the MFMAs read and write them. Every
+//     operand the MFMAs read from LDS serves 32 rows: 1 KB per 32x32x16
+//     MFMA, twice the rows per operand byte of the 16x16 tiles of chunk.hip.
+//   * The raw K/V rows of each 32-key tile arrive by DMA in an LDS ring of
+//     3-4 tiles, the 16 rows of a group of kv head g back to back, through
+//     the block table (64-bit row addresses, mlxcel issue #2153); every tile
+//     is converted to f16 once per workgroup into LDS in MFMA operand order,
+//     each wave a quarter of it (8 keys of K, and 4 keys of every V^T
+//     operand lane of one 16-key group).
 //   * One barrier per tile, in a software pipeline: while the softmax and PV
 //     of tile kt run, the scores of tile kt+1 are computed and tile kt+2 is
-//     converted, and the raw rows of tile kt+4 are loaded. K operands are
-//     double-buffered and V operands triple-buffered (V of tile kt is read
-//     one iteration later than K), 80 KB at D = 256.
+//     converted; the DMA runs RR-1 tiles ahead. K operands are double- and
+//     V operands triple-buffered (V of tile kt is read one iteration later
+//     than K). At one wave per SIMD a tile's parts overlap only as far as
+//     the instruction order interleaves them, so each tile is two branch-
+//     free regions with scheduling groups.
 //   * Causal limit per row; tiles past the workgroup's last row are not
 //     read and only tiles that cross some row's limit are masked. Partials
 //     (normalised binary16 o, fp32 m and l) use the decode layout with Tq*Hq
@@ -53,8 +56,6 @@ constexpr int kWThreads = 256;
 constexpr int kWRows = 128;     // query rows per workgroup (32 per wave)
 constexpr int kWNid = 512;      // block ids staged per segment of a partition
 constexpr int kWTile = 32;      // keys per tile
-// Order of a tile step's work (see the pipeline below).
-constexpr int kStepOrder = 0;
 
 // 32x32x16 f16 -> f32: A lane l (row l%32, k 8*(l/32)+i), B lane l (col l%32,
 // k 8*(l/32)+i), C lane l register r (row 8*(r/4) + 4*(l/32) + r%4, col l%32).
@@ -734,64 +735,33 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
         mask(s_cur, seg_t0 + kt * kWTile);
         ConvRaw cr;
         f16x8 vop[2][NDT];
-        if constexpr (kStepOrder == 0) {
-          // region 1: scores of kt+1, the row max of kt, conversion of kt+2
-          // (its staged-row reads first: LDS returns in order)
-          conv_load(kt + 2, cr);
-          __builtin_amdgcn_sched_barrier(0);
-          scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
-          const float mx = row_max(s_cur);
-          conv_store(kt + 2, cr);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // region 1: scores of kt+1 and the row max of kt
+        scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
+        const float mx = row_max(s_cur);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-          for (int i = 0; i < C; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          }
-          rescale(mx);
-          // region 2: probabilities and PV of kt
-          pv_load(vbuf + (kt % 3) * VBUF, vop);
-          f16x8 pop[2];
-          probs(s_cur, pop);
-          pv_mfma(vop, pop);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+        for (int i = 0; i < C; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        rescale(mx);
+        // region 2: probabilities and PV of kt beside the conversion of kt+2
+        // (its staged-row reads and the V operand reads first: LDS returns
+        // in order)
+        conv_load(kt + 2, cr);
+        pv_load(vbuf + (kt % 3) * VBUF, vop);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 pop[2];
+        probs(s_cur, pop);
+        pv_mfma(vop, pop);
+        conv_store(kt + 2, cr);
+        __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
 #pragma unroll
-          for (int i = 0; i < 2 * NDT; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
-          }
-        } else {
-          // region 1: scores of kt+1 and the row max of kt
-          scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
-          const float mx = row_max(s_cur);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-          for (int i = 0; i < C; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          }
-          rescale(mx);
-          // region 2: probabilities and PV of kt beside the conversion of
-          // kt+2 (its staged-row reads and the V operand reads first)
-          conv_load(kt + 2, cr);
-          pv_load(vbuf + (kt % 3) * VBUF, vop);
-          __builtin_amdgcn_sched_barrier(0);
-          f16x8 pop[2];
-          probs(s_cur, pop);
-          pv_mfma(vop, pop);
-          conv_store(kt + 2, cr);
-          __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
-#pragma unroll
-          for (int i = 0; i < 2 * NDT; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
-          }
+        for (int i = 0; i < 2 * NDT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
         }
         // the accumulators are carried from tile to tile in AGPRs (without
         // this the compiler moves all of them to VGPRs and back every tile)

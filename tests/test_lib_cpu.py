@@ -347,8 +347,9 @@ def test_chunk_plan_kernel_choice():
     D=256, where the head dimension is split over two waves and a workgroup
     takes a kv-head pair, two per compute unit; the wide-tile kernel (path 3)
     for more than 64 rows, a workgroup per (sequence, partition, kv head, 128
-    rows), one per compute unit; the tile-conversion kernel (path 1)
-    otherwise. A plan forced to path 2 where it does not apply, or to a path
+    rows), one per compute unit (at D=256 only where 128-row blocks are as
+    full as 64-row ones and the units fill the CUs); the tile-conversion
+    kernel (path 1) otherwise. A plan forced to path 2 where it does not apply, or to a path
     that does not exist, is refused before launch."""
     p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
     assert p.path == 1                                   # 54 rows
@@ -368,6 +369,11 @@ def test_chunk_plan_kernel_choice():
         assert wide.path == 3 and wide.grid == min(8 * wide.p_max * 4 * 1, 256)    # 72 rows
         pre = pa.paged_attn_chunk_plan(_shape(D=D, B=1), 512, 8192, total_tokens=8192, num_cus=256)
         assert pre.path == 3 and pre.grid == min(pre.p_max * 4 * 24, 256)         # 3072 rows
+    # at D=256: 192 rows fill two 128-row blocks to 75% and three 64-row
+    # blocks whole; a 64-token chunk over 8K makes fewer wide units than CUs
+    assert pa.paged_attn_chunk_plan(_shape(), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 1
+    assert pa.paged_attn_chunk_plan(_shape(B=1), 64, 8192, total_tokens=8192, num_cus=256).path == 1
+    assert pa.paged_attn_chunk_plan(_shape(D=128), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 3
     p.path = 2
     with pytest.raises(pa.PaError) as e:
         pa.paged_attn_chunk(p, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
