@@ -404,9 +404,9 @@ def test_chunk_refusals_before_any_launch():
 
 
 def test_smoke_cases_take_the_kernels_smoke_expects():
-    """__graft_entry__.smoke() checks that each of its decode cases is planned
-    on a given kernel; the planner (host code) must agree, for every
-    partitioning smoke runs."""
+    """__graft_entry__.smoke() checks that each of its decode and chunk cases
+    is planned on a given kernel; the planner (host code) must agree, for
+    every partitioning smoke runs."""
     import importlib.util
     spec = importlib.util.spec_from_file_location("_graft_entry", os.path.join(ROOT, "__graft_entry__.py"))
     ge = importlib.util.module_from_spec(spec)
@@ -417,6 +417,12 @@ def test_smoke_cases_take_the_kernels_smoke_expects():
         for force in (0, 1, 3):
             plan = pa.paged_attn_plan(shape, max(case.seq_lens), num_cus=256, force_partitions=force)
             assert plan.path == path, (label, force, plan.path)
+    for label, case, Tq, path in ge.smoke_chunk_cases():
+        shape = pa.shape_of(case.B, case.Hq, case.Hkv, case.D, case.block_size, case.nblocks,
+                            case.max_blocks, case.k_fmt, case.v_fmt)
+        plan = pa.paged_attn_chunk_plan(shape, Tq, max(case.seq_lens), total_tokens=sum(case.seq_lens),
+                                        num_cus=256, partition_tokens=256, scale=case.scale)
+        assert plan.path == path, (label, plan.path)
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,Tq,kt,vt,per_cu,heads", [
