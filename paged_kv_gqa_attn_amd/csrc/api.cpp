@@ -541,10 +541,11 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
   };
   // The wide-tile kernel takes chunks of more than 64 query rows per kv head.
   // At D = 256 it does where its 128-row blocks are no emptier than the tile
-  // kernel's 64-row ones and its units fill the compute units (one
-  // workgroup each); otherwise the tile kernel, two per compute unit, was
-  // measured faster (B=8 x 32K Q4_0: 192 rows 483 against 438 us; a 64-token
-  // chunk over 8K, 72 units: 96 against 85 us).
+  // kernel's 64-row ones and its units fill at least half the compute units
+  // (one workgroup each); otherwise the tile kernel, two per compute unit,
+  // was measured as fast or faster (B=8 x 32K Q4_0/Q8_0: 144 rows 468
+  // against 412 us; a 64-token chunk over 8K, 72 units: F16 89 against 78
+  // us, while 144 units at 128 tokens take 92 against 97).
   const int64_t rows = int64_t(tq) * r;
   bool wide = !window && chunk_wide_pick(rows, s.D);
   int64_t psize = 0;
@@ -555,7 +556,7 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
       const int64_t qt_t = ceil_div(rows, int64_t(64 * nt));
       const int64_t units_w =
           int64_t(s.B) * std::max<int64_t>(1, ceil_div(std::max<int64_t>(L, 1), psize)) * s.Hkv * qt_w;
-      if (qt_w * kWideRows > qt_t * 64 * nt || units_w < num_cus) wide = false;
+      if (qt_w * kWideRows > qt_t * 64 * nt || 2 * units_w < num_cus) wide = false;
     }
   }
   // the window kernel takes short chunks (a workgroup per kv-head quad, two

@@ -406,9 +406,6 @@ template <int KT, int VT, int D> struct WideLds {
   static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
 
-// The DMA instructions of one tile (tokens t0 .. t0+31 of the segment) that
-// wave W issues: q % 4 == W of the NT, K then V of group 0, then group 1.
-// Groups at or past seg_t1 get a zero-size resource and read nothing.
 // One DMA instruction: lane l's CB bytes at pool offset voff land at LDS
 // byte dst + CB*l (cached loads: the tiles are read again by the other
 // query-row blocks of the kv head).
@@ -418,38 +415,6 @@ __device__ __forceinline__ void dma_lds(rsrc_t R, uint32_t dst, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 16, voff, 0, 0, 0);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R, (lds_ptr_t)(g_lds + dst), 4, voff, 0, 0, 0);
-}
-
-template <class LY, int W>
-__device__ __forceinline__ void issue_tile_as(const ChunkArgs& a, uint32_t slot, int t0, int seg_t1,
-                                              const int32_t* ids, int jb0, int g, uint32_t kstride,
-                                              uint32_t vstride, int lane) {
-  using SK = typename LY::SK;
-  using SV = typename LY::SV;
-  const int bs_mask = (1 << a.bs_shift) - 1;
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int tg = t0 + 16 * gi;
-    const bool live = tg < seg_t1;
-    const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
-    const int slot0 = live ? (tg & bs_mask) : 0;
-    const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SK::RB),
-                                live ? 16u * kstride : 0u);
-    const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SV::RB),
-                                live ? 16u * vstride : 0u);
-#pragma unroll
-    for (int j = 0; j < SK::NI; ++j) {
-      const int q = gi * (SK::NI + SV::NI) + j;
-      if (q % 4 == W)
-        dma_lds<SK::CB>(kr, slot + gi * SK::GB + j * 64 * SK::CB, SK::off(j, lane, kstride));
-    }
-#pragma unroll
-    for (int j = 0; j < SV::NI; ++j) {
-      const int q = gi * (SK::NI + SV::NI) + SK::NI + j;
-      if (q % 4 == W)
-        dma_lds<SV::CB>(vr, slot + 2 * SK::GB + gi * SV::GB + j * 64 * SV::CB, SV::off(j, lane, vstride));
-    }
-  }
 }
 
 template <int KT, int VT, int D>
@@ -497,8 +462,17 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
   const uint32_t v_row0 = uint32_t(2 * SK::GB + v_grp * SV::GB + pkey(0, h, 4 * v_half) * VRB);
   const uint32_t mg = opaque_vgpr(kMagic);
   const int seg_tokens = kWNid << a.bs_shift;
-  // DMA instructions this wave issues per tile
-  const int n_dma = (LY::NT + 3 - wave) / 4;
+  // the DMA of a tile: wave w issues every instruction of one side (K for
+  // even w, V for odd) of 16-key group w >> 1, at lane offsets that do not
+  // change from tile to tile
+  const int d_grp = wave >> 1;
+  const bool d_v = (wave & 1) != 0;
+  const int n_dma = d_v ? SV::NI : SK::NI;
+  constexpr int NIM = SK::NI > SV::NI ? SK::NI : SV::NI;
+  uint32_t d_off[NIM];
+#pragma unroll
+  for (int j = 0; j < NIM; ++j)
+    d_off[j] = d_v ? (j < SV::NI ? SV::off(j, lane, vstride) : 0u) : (j < SK::NI ? SK::off(j, lane, kstride) : 0u);
 
   for (int u = logical; u < n_units; u += Gd) {
     // ---- locate the unit: ((b*p_max + p)*Hkv + g)*QG + qg ------------------
@@ -673,14 +647,25 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
       const int ntiles = (seg_t1 - seg_t0 + kWTile - 1) / kWTile;
 
       // ---- DMA of tile t's raw rows into ring slot t % RR --------------------
+      // (a group at or past seg_t1 gets a zero-size resource and reads
+      // nothing; the instruction count per wave stays the same)
       auto issue = [&](int t) __attribute__((always_inline)) {
         const uint32_t slot = uint32_t(LY::RAW + (t % RR) * LY::SLOT);
-        const int t0 = seg_t0 + t * kWTile;
-        switch (wave) {
-          case 0: issue_tile_as<LY, 0>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
-          case 1: issue_tile_as<LY, 1>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
-          case 2: issue_tile_as<LY, 2>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
-          default: issue_tile_as<LY, 3>(a, slot, t0, seg_t1, ids, jb0, g, kstride, vstride, lane); break;
+        const int tg = seg_t0 + t * kWTile + 16 * d_grp;
+        const bool live = tg < seg_t1;
+        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+        const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
+        if (!d_v) {
+          const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SK::RB),
+                                      live ? 16u * kstride : 0u);
+#pragma unroll
+          for (int j = 0; j < SK::NI; ++j) dma_lds<SK::CB>(kr, slot + d_grp * SK::GB + j * 64 * SK::CB, d_off[j]);
+        } else {
+          const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SV::RB),
+                                      live ? 16u * vstride : 0u);
+#pragma unroll
+          for (int j = 0; j < SV::NI; ++j)
+            dma_lds<SV::CB>(vr, slot + 2 * SK::GB + d_grp * SV::GB + j * 64 * SV::CB, d_off[j]);
         }
       };
       // ---- this wave's quarter of the conversion of tile kt: staged raw rows

@@ -50,7 +50,7 @@ def wide_paths(c, Tq):
     """The kernels the plan may pick besides the window kernel: the wide-tile
     kernel (plan path 3) takes more than 64 query rows per kv head, at D=256
     only where its 128-row blocks are no emptier than 64-row ones (and then
-    only if its units fill the compute units, which the test does not
+    only if its units fill half the compute units, which the test does not
     mirror); the tile kernel (path 1) the rest."""
     rows = Tq * (c.Hq // c.Hkv)
     if rows <= 64:

@@ -348,7 +348,7 @@ def test_chunk_plan_kernel_choice():
     takes a kv-head pair, two per compute unit; the wide-tile kernel (path 3)
     for more than 64 rows, a workgroup per (sequence, partition, kv head, 128
     rows), one per compute unit (at D=256 only where 128-row blocks are as
-    full as 64-row ones and the units fill the CUs); the tile-conversion
+    full as 64-row ones and the units fill at least half the CUs); the tile-conversion
     kernel (path 1) otherwise. A plan forced to path 2 where it does not apply, or to a path
     that does not exist, is refused before launch."""
     p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
@@ -370,9 +370,12 @@ def test_chunk_plan_kernel_choice():
         pre = pa.paged_attn_chunk_plan(_shape(D=D, B=1), 512, 8192, total_tokens=8192, num_cus=256)
         assert pre.path == 3 and pre.grid == min(pre.p_max * 4 * 24, 256)         # 3072 rows
     # at D=256: 192 rows fill two 128-row blocks to 75% and three 64-row
-    # blocks whole; a 64-token chunk over 8K makes fewer wide units than CUs
+    # blocks whole; a 64-token chunk over 8K makes 72 wide units, fewer than
+    # half the CUs, a 128-token one 144
     assert pa.paged_attn_chunk_plan(_shape(), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 1
     assert pa.paged_attn_chunk_plan(_shape(B=1), 64, 8192, total_tokens=8192, num_cus=256).path == 1
+    t128 = pa.paged_attn_chunk_plan(_shape(B=1), 128, 8192, total_tokens=8192, num_cus=256)
+    assert t128.path == 3 and t128.grid == 144
     assert pa.paged_attn_chunk_plan(_shape(D=128), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 3
     p.path = 2
     with pytest.raises(pa.PaError) as e:
