@@ -70,17 +70,20 @@ __device__ __forceinline__ void mfma_drain() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Scheduling of N MFMAs that each read one operand from LDS: two reads ahead,
-// then one read per MFMA, so at most three operands wait in registers.
-template <int N>
-__device__ __forceinline__ void lds_mfma_stream() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int i = 0; i < N - 2; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+// s_waitcnt vmcnt(n) lgkmcnt(0), then the workgroup barrier: the wave's DMA
+// but the last n instructions has landed and its LDS writes are done, so
+// every wave reads them after the barrier (n wave-uniform; above 15 it waits
+// for more than needed, which is safe).
+__device__ __forceinline__ void wait_all_then_barrier(int n) {
+#define PA_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  switch (n < 15 ? n : 15) {
+    PA_WAIT_CASE(0) PA_WAIT_CASE(1) PA_WAIT_CASE(2) PA_WAIT_CASE(3) PA_WAIT_CASE(4)
+    PA_WAIT_CASE(5) PA_WAIT_CASE(6) PA_WAIT_CASE(7) PA_WAIT_CASE(8) PA_WAIT_CASE(9)
+    PA_WAIT_CASE(10) PA_WAIT_CASE(11) PA_WAIT_CASE(12) PA_WAIT_CASE(13) PA_WAIT_CASE(14)
+    default: asm volatile("s_waitcnt vmcnt(15) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#undef PA_WAIT_CASE
 }
 
 // Key of register r of an S^T accumulator, within its 32-key tile, for lane half h.
@@ -710,49 +713,59 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
       for (int t = 0; t < RR; ++t) issue(t);
       wait_dma_then_barrier((RR - 1) * n_dma);
       convert(0);
-      wait_dma_then_barrier((RR - 2) * n_dma);
+      wait_all_then_barrier((RR - 2) * n_dma);
       issue(RR);
       scores(kbuf, s0);
       convert(1);
-      wait_dma_then_barrier((RR - 2) * n_dma);
+      wait_all_then_barrier((RR - 2) * n_dma);
       auto step = [&](int kt, f32x16& s_cur, f32x16& s_next) __attribute__((always_inline)) {
         issue(kt + RR + 1);
         mask(s_cur, seg_t0 + kt * kWTile);
+        // the staged rows of tile kt+2 first (LDS returns in order), the row
+        // max and the rare rescale
         ConvRaw cr;
-        f16x8 vop[2][NDT];
-        // region 1: scores of kt+1 and the row max of kt
-        scores(kbuf + ((kt + 1) & 1) * KBUF, s_next);
-        const float mx = row_max(s_cur);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
-        rescale(mx);
-        // region 2: probabilities and PV of kt beside the conversion of kt+2
-        // (its staged-row reads and the V operand reads first: LDS returns
-        // in order)
         conv_load(kt + 2, cr);
-        pv_load(vbuf + (kt % 3) * VBUF, vop);
-        __builtin_amdgcn_sched_barrier(0);
+        const float mx = row_max(s_cur);
+        rescale(mx);
+        // then the score MFMAs of kt+1 alternate with the PV MFMAs of kt, the
+        // operand reads streaming kLead reads ahead of them (the LDS counter
+        // holds at most 15) and the probabilities and the conversion of kt+2
+        // between them
+        f16x8 kop[C];
+        f16x8 vop[2][NDT];
+        {
+          const unsigned char* kops = kbuf + ((kt + 1) & 1) * KBUF;
+          const unsigned char* vops = vbuf + (kt % 3) * VBUF;
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            kop[i] = *reinterpret_cast<const f16x8*>(kops + (i * 64 + lane) * 16);
+            vop[i / NDT][i % NDT] = *reinterpret_cast<const f16x8*>(vops + (i * 64 + lane) * 16);
+          }
+        }
         f16x8 pop[2];
         probs(s_cur, pop);
-        pv_mfma(vop, pop);
-        conv_store(kt + 2, cr);
-        __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+        s_next = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 2 * NDT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
+        for (int i = 0; i < C; ++i) {
+          s_next = mfma32(kop[i], qop[i], s_next);
+          acc[i % NDT] = mfma32(vop[i / NDT][i % NDT], pop[i / NDT], acc[i % NDT]);
         }
+        conv_store(kt + 2, cr);
+        constexpr int kLead = 12;
+        __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          if (i + kLead < 2 * C) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);
         // the accumulators are carried from tile to tile in AGPRs (without
         // this the compiler moves all of them to VGPRs and back every tile)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
-        wait_dma_then_barrier((RR - 2) * n_dma);
+        wait_all_then_barrier((RR - 2) * n_dma);
       };
       for (int kt = 0; kt < ntiles; kt += 2) {
         step(kt, s0, s1);
