@@ -630,10 +630,11 @@ extern "C" int32_t paged_attn_chunk(const pa_chunk_plan* plan, const float* q, c
   a.nt = chunk_wave_tiles(int64_t(plan->tq) * a.r, s.D);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the window kernel's DMA chunks are 16-byte aligned only on aligned
-  // pools, and the window and wide-tile kernels read q rows with 16-byte
-  // loads; otherwise the tile kernel runs
+  // pools, the window and wide-tile kernels read q rows with 16-byte loads,
+  // and the wide-tile kernel writes partial rows with 16-byte stores;
+  // otherwise the tile kernel runs
   const bool aligned = ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
-                         reinterpret_cast<uintptr_t>(q)) & 15) == 0;
+                         reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(ws)) & 15) == 0;
   hipError_t e = !aligned || plan->path == 1 ? launch_chunk(a, st)
                  : plan->path == 2         ? launch_chunk_lds(a, st)
                                            : launch_chunk_wide(a, st);

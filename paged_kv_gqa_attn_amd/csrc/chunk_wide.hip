@@ -86,6 +86,22 @@ __device__ __forceinline__ void wait_all_then_barrier(int n) {
 #undef PA_WAIT_CASE
 }
 
+// s_waitcnt vmcnt(n): the wave's own vector memory operations but the last n
+// have completed (n wave-uniform; above 15 it waits for more than needed).
+__device__ __forceinline__ void wait_vm(int n) {
+#define PA_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+  switch (n < 15 ? n : 15) {
+    PA_WAIT_CASE(0) PA_WAIT_CASE(1) PA_WAIT_CASE(2) PA_WAIT_CASE(3) PA_WAIT_CASE(4)
+    PA_WAIT_CASE(5) PA_WAIT_CASE(6) PA_WAIT_CASE(7) PA_WAIT_CASE(8) PA_WAIT_CASE(9)
+    PA_WAIT_CASE(10) PA_WAIT_CASE(11) PA_WAIT_CASE(12) PA_WAIT_CASE(13) PA_WAIT_CASE(14)
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+  }
+#undef PA_WAIT_CASE
+}
+// The wave's LDS operations have completed.
+__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Key of register r of an S^T accumulator, within its 32-key tile, for lane half h.
 __host__ __device__ constexpr int skey(int r, int h) { return 8 * (r / 4) + 4 * h + r % 4; }
 // Key of slot e of a P^T (and V^T) operand half of k-step t: the accumulator
@@ -108,21 +124,28 @@ __device__ __forceinline__ uint32_t shift_sel(uint32_t s) { return 0x03020100u +
 // ===========================================================================
 template <int KT, int D> struct WK;
 
+// Every format also converts a run of NS steps c0 .. c0+NS-1 for one lane
+// (`loadn`, `opn`; c0 and NS even), the unit of the paired form's K waves.
 template <int D> struct WK<kF16, D> {
   static constexpr int CQ = D / 64;
-  static constexpr int kWords = 4 * CQ;
+  template <int NS> static constexpr int words() { return 4 * NS; }
+  static constexpr int kWords = words<CQ>();
   __host__ __device__ static constexpr int kd(int c, int h, int s) { return 16 * c + 8 * h + s; }
-  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+  template <int NS>
+  __device__ static void loadn(uint32_t* w, const unsigned char* row, int h, int c0) {
 #pragma unroll
-    for (int cc = 0; cc < CQ; ++cc) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(row + 32 * (cq * CQ + cc) + 16 * h);
+    for (int cc = 0; cc < NS; ++cc) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(row + 32 * (c0 + cc) + 16 * h);
 #pragma unroll
       for (int k = 0; k < 4; ++k) w[4 * cc + k] = a[k];
     }
   }
-  __device__ static f16x8 op(const uint32_t* w, int cc, int, uint32_t) {
+  template <int NS>
+  __device__ static f16x8 opn(const uint32_t* w, int cc, int, uint32_t) {
     return bitcast<f16x8>(u32x4{w[4 * cc], w[4 * cc + 1], w[4 * cc + 2], w[4 * cc + 3]});
   }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) { loadn<CQ>(w, row, h, cq * CQ); }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) { return opn<CQ>(w, cc, cq * CQ, mg); }
 };
 
 // Quantised K: step c = 2*bk + x covers ggml block bk, quant bytes [16x + 8h,
@@ -130,44 +153,54 @@ template <int D> struct WK<kF16, D> {
 // The 8 bytes start 2 bytes into a dword for even bk: three dwords from the
 // 4-aligned base below them are read and realigned (v_alignbyte).
 template <int D> struct WK<kQ4_0, D> {
-  static constexpr int CQ = D / 64, NBQ = CQ / 2;   // steps, blocks per lane
-  static constexpr int kWords = 4 * NBQ;            // block j: w[3j..3j+2], scale w[3NBQ + j]
+  static constexpr int CQ = D / 64;
+  template <int NS> static constexpr int words() { return 4 * (NS / 2); }   // block j: w[3j..3j+2], scale w[3NB + j]
+  static constexpr int kWords = words<CQ>();
   __host__ __device__ static constexpr int kd(int c, int h, int s) {
     return 32 * (c / 2) + 16 * (c % 2) + 8 * h + word_order(s);
   }
-  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+  template <int NS>
+  __device__ static void loadn(uint32_t* w, const unsigned char* row, int h, int c0) {
+    constexpr int NB = NS / 2;
 #pragma unroll
-    for (int j = 0; j < NBQ; ++j) {
-      const int bk = cq * NBQ + j;
+    for (int j = 0; j < NB; ++j) {
+      const int bk = c0 / 2 + j;
       const uint32_t* q = reinterpret_cast<const uint32_t*>(row + ((18 * bk + 2 + 8 * h) & ~3));
       w[3 * j] = q[0];
       w[3 * j + 1] = q[1];
       w[3 * j + 2] = q[2];
-      w[3 * NBQ + j] = *reinterpret_cast<const uint16_t*>(row + 18 * bk);
+      w[3 * NB + j] = *reinterpret_cast<const uint16_t*>(row + 18 * bk);
     }
   }
-  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) {
+  template <int NS>
+  __device__ static f16x8 opn(const uint32_t* w, int cc, int c0, uint32_t mg) {
+    constexpr int NB = NS / 2;
     const int j = cc / 2, x = cc % 2;
-    const uint32_t sh = ((cq * NBQ + j) & 1) ? 0u : 2u;
+    const uint32_t sh = ((c0 / 2 + j) & 1) ? 0u : 2u;
     uint32_t w0 = align_bytes(w[3 * j + 1], w[3 * j], sh);
     uint32_t w1 = align_bytes(w[3 * j + 2], w[3 * j + 1], sh);
     if (x) { w0 >>= 4; w1 >>= 4; }
-    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[3 * NBQ + j])));
+    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[3 * NB + j])));
     return pack8(nib_pair_to_f16(w0, d2, mg), nib_pair_to_f16(w0 >> 8, d2, mg),
                  nib_pair_to_f16(w1, d2, mg), nib_pair_to_f16(w1 >> 8, d2, mg));
   }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) { loadn<CQ>(w, row, h, cq * CQ); }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) { return opn<CQ>(w, cc, cq * CQ, mg); }
 };
 
 template <int D> struct WK<kQ8_0, D> {
-  static constexpr int CQ = D / 64, NBQ = CQ / 2;
-  static constexpr int kWords = 7 * NBQ;            // chunk x of block j: w[6j + 3x ..], scale w[6NBQ + j]
+  static constexpr int CQ = D / 64;
+  template <int NS> static constexpr int words() { return 7 * (NS / 2); }   // chunk x of block j: w[6j + 3x ..], scale w[6NB + j]
+  static constexpr int kWords = words<CQ>();
   __host__ __device__ static constexpr int kd(int c, int h, int s) {
     return 32 * (c / 2) + 16 * (c % 2) + 8 * h + word_order(s);
   }
-  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) {
+  template <int NS>
+  __device__ static void loadn(uint32_t* w, const unsigned char* row, int h, int c0) {
+    constexpr int NB = NS / 2;
 #pragma unroll
-    for (int j = 0; j < NBQ; ++j) {
-      const int bk = cq * NBQ + j;
+    for (int j = 0; j < NB; ++j) {
+      const int bk = c0 / 2 + j;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const uint32_t* q = reinterpret_cast<const uint32_t*>(row + ((34 * bk + 2 + 16 * x + 8 * h) & ~3));
@@ -175,19 +208,23 @@ template <int D> struct WK<kQ8_0, D> {
         w[6 * j + 3 * x + 1] = q[1];
         w[6 * j + 3 * x + 2] = q[2];
       }
-      w[6 * NBQ + j] = *reinterpret_cast<const uint16_t*>(row + 34 * bk);
+      w[6 * NB + j] = *reinterpret_cast<const uint16_t*>(row + 34 * bk);
     }
   }
-  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) {
+  template <int NS>
+  __device__ static f16x8 opn(const uint32_t* w, int cc, int c0, uint32_t mg) {
+    constexpr int NB = NS / 2;
     const int j = cc / 2, o = 6 * j + 3 * (cc % 2);
-    const uint32_t sh = ((cq * NBQ + j) & 1) ? 0u : 2u;
+    const uint32_t sh = ((c0 / 2 + j) & 1) ? 0u : 2u;
     const uint32_t u0 = align_bytes(w[o + 1], w[o], sh);
     const uint32_t u1 = align_bytes(w[o + 2], w[o + 1], sh);
-    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[6 * NBQ + j])));
+    const f16x2 d2 = splat2(bitcast<f16>(uint16_t(w[6 * NB + j])));
     const uint32_t a = u0 ^ 0x80808080u, b = u1 ^ 0x80808080u;
     return pack8(i8pair_to_f16(a, d2, mg), i8pair_to_f16(a >> 8, d2, mg), i8pair_to_f16(b, d2, mg),
                  i8pair_to_f16(b >> 8, d2, mg));
   }
+  __device__ static void load(uint32_t* w, const unsigned char* row, int h, int cq) { loadn<CQ>(w, row, h, cq * CQ); }
+  __device__ static f16x8 op(const uint32_t* w, int cc, int cq, uint32_t mg) { return opn<CQ>(w, cc, cq * CQ, mg); }
 };
 
 // ===========================================================================
@@ -226,10 +263,6 @@ template <int D> struct WV<kF16, D> {
         w[2 * e + 1] = a[1];
       }
     }
-  }
-  __device__ static void kill(uint32_t* w, int e) {
-#pragma unroll
-    for (int k = 0; k < NW; ++k) w[NW * e + k] = 0;
   }
   __device__ static void prep(uint32_t*, const Lane&) {}
   __device__ static f16x4 op(const uint32_t* w, const Lane&, int dt, uint32_t) {
@@ -277,7 +310,6 @@ template <int D> struct WV<kQ4_0, D> {
       w[8 + e] = *reinterpret_cast<const uint16_t*>(row + L.doff);
     }
   }
-  __device__ static void kill(uint32_t* w, int e) { w[8 + e] = 0; }
   // the quant dword of key e into w[2e]; scale pairs of keys (2k, 2k+1) into w[8 + 2k]
   __device__ static void prep(uint32_t* w, const Lane& L) {
 #pragma unroll
@@ -334,7 +366,6 @@ template <int D> struct WV<kQ8_0, D> {
       w[SC + e] = *reinterpret_cast<const uint16_t*>(row + L.doff);
     }
   }
-  __device__ static void kill(uint32_t* w, int e) { w[SC + e] = 0; }
   // quant dwords of key e into w[NWIN*e + k], k < QB/4; scale pairs into w[SC + 2k]
   __device__ static void prep(uint32_t* w, const Lane& L) {
 #pragma unroll
@@ -651,21 +682,25 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
 
       // ---- DMA of tile t's raw rows into ring slot t % RR --------------------
       // (a group at or past seg_t1 gets a zero-size resource and reads
-      // nothing; the instruction count per wave stays the same)
+      // nothing, one that crosses it a resource over its live rows; the
+      // instruction count per wave stays the same)
       auto issue = [&](int t) __attribute__((always_inline)) {
         const uint32_t slot = uint32_t(LY::RAW + (t % RR) * LY::SLOT);
         const int tg = seg_t0 + t * kWTile + 16 * d_grp;
         const bool live = tg < seg_t1;
         const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
         const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
+        // rows past seg_t1 (junk slots, maybe NaN) lie outside the resource
+        // and land as zeros: their p is 0, and 0 * NaN would not be
+        const uint32_t nlive = live ? uint32_t(min(16, seg_t1 - tg)) : 0u;
         if (!d_v) {
           const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SK::RB),
-                                      live ? 16u * kstride : 0u);
+                                      nlive * kstride);
 #pragma unroll
           for (int j = 0; j < SK::NI; ++j) dma_lds<SK::CB>(kr, slot + d_grp * SK::GB + j * 64 * SK::CB, d_off[j]);
         } else {
           const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SV::RB),
-                                      live ? 16u * vstride : 0u);
+                                      nlive * vstride);
 #pragma unroll
           for (int j = 0; j < SV::NI; ++j)
             dma_lds<SV::CB>(vr, slot + 2 * SK::GB + d_grp * SV::GB + j * 64 * SV::CB, d_off[j]);
@@ -681,12 +716,6 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
         VF::load(cr.vw, raw + v_row0, vl);
       };
       auto conv_store = [&](int kt, ConvRaw& cr) __attribute__((always_inline)) {
-        // keys past the segment (junk slots, maybe NaN) are zeroed: their p
-        // is 0, and 0 * NaN would not be
-        const int t0 = seg_t0 + kt * kWTile + 16 * v_grp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t0 + pkey(0, h, 4 * v_half + e) >= seg_t1) VF::kill(cr.vw, e);
         VF::prep(cr.vw, vl);
         unsigned char* kops = kbuf + (kt & 1) * KBUF;
 #pragma unroll
@@ -811,8 +840,570 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
   }
 }
 
+// ===========================================================================
+// The paired form: eight waves, two per SIMD. Waves w and w + 4 (on one SIMD)
+// share query rows 32w .. 32w+31: the score wave (w < 4) holds their Q^T,
+// computes the scores of tile kt+1, the softmax of tile kt and the PV of the
+// first half of the d-tiles; the conversion wave (w >= 4) issues the DMA,
+// converts tile kt+2 (a quarter of it, as in the four-wave form) and runs the
+// PV of the second half of the d-tiles for tile kt-1, with the P^T operands
+// and the rescale factors its partner left in LDS one tile earlier. Each
+// SIMD keeps the four-wave form's MFMA and vector work, but two waves issue
+// it, so one wave's LDS waits are filled with the other's instructions.
+// ===========================================================================
+constexpr int kPThreads = 512;
+
+// Whether every stored pair of d-tiles (dt, dnext(dt)) lies inside one half
+// of the d-tiles, with the same pattern in both halves.
+template <typename VF>
+__host__ __device__ constexpr bool halves_ok() {
+  constexpr int NH = VF::NDT / 2;
+  for (int j = 0; j < NH; ++j) {
+    const int a = VF::dnext(j), b = VF::dnext(NH + j);
+    if ((a < 0) != (b < 0)) return false;
+    if (a >= 0 && (a >= NH || b != NH + a)) return false;
+  }
+  return true;
+}
+constexpr int kPNid = 256;      // block ids staged per segment
+// LDS row stride of the staged Q rows and partial rows (binary16, D = 256):
+// 16 bytes of padding spread a wave's rows over the banks
+constexpr int kStageRow = 2 * 256 + 16;
+
+template <int KT, int VT, int D> struct PairLds {
+  using SK = Stage<KT, D>;
+  using SV = Stage<VT, D>;
+  static constexpr int KBUF = (D / 16) * 64 * 16;          // K operands of a tile
+  static constexpr int VBUF = 2 * (D / 32) * 64 * 16;      // V operands of a tile
+  static constexpr int PBUF = 4 * 2 * 64 * 16;             // P^T operands of the four score waves
+  static constexpr int XBUF = 4 * 256;                     // per score wave: flag, 32 row factors
+  static constexpr int SLOT = 2 * (SK::GB + SV::GB);       // raw rows of a tile
+  static constexpr int IDS = 4 * (kPNid + 4);
+  static constexpr int K0 = 0;
+  static constexpr int V0 = K0 + 2 * KBUF;                 // four V buffers (tiles kt-1 .. kt+2)
+  static constexpr int P0 = V0 + 4 * VBUF;                 // two tiles of P^T
+  static constexpr int X0 = P0 + 2 * PBUF;                 // two tiles of flags and factors
+  static constexpr int L0 = X0 + 2 * XBUF;                 // row sums for the epilogue
+  static constexpr int OPS = L0 + 4 * 32 * 4;
+  static constexpr int RR = OPS + 3 * SLOT + IDS <= 160 * 1024 ? 3 : 2;
+  static constexpr int RAW = OPS;
+  static constexpr int ID0 = RAW + RR * SLOT;
+  static constexpr int BYTES = ID0 + IDS;
+  static constexpr bool kFits = BYTES <= 160 * 1024;
+};
+
+// Roles of the paired form's waves.
+constexpr int kRoleScore = 0, kRoleConvK = 1, kRoleConvV = 2;
+
+// The whole body of one role, instantiated once per role so that no role's
+// registers stay live across another's code; every role runs the same
+// sequence of barriers. Score wave pw (waves 0-3) holds query rows 32pw ..
+// 32pw+31; conversion wave 4 + pw shares its SIMD and rows and, by pw,
+// handles one side (K for even pw, V for odd) of 16-key group pw >> 1 of
+// every tile: it DMAs those rows, waits for its own DMA only, loads the raw
+// rows of tile kt+3 into registers during tile kt, and converts tile kt+2
+// from the registers loaded during tile kt-1, so no LDS latency stands
+// between a tile's start and its conversion.
+template <int KT, int VT, int D, int ROLE>
+__device__ __forceinline__ void pair_role(const ChunkArgs& a) {
+  using KF = WK<KT, D>;
+  using VF = WV<VT, D>;
+  using LY = PairLds<KT, VT, D>;
+  using SK = typename LY::SK;
+  using SV = typename LY::SV;
+  static_assert(pairs_ok<VF>(), "d-tile pairs cover adjacent even/odd positions");
+  static_assert(LY::kFits, "LDS of one CU");
+  constexpr int C = D / 16;                       // score MFMA steps
+  constexpr int NDT = D / 32;                     // PV d-tiles
+  constexpr int NH = NDT / 2;                     // d-tiles per wave of a pair
+  constexpr int KBUF = LY::KBUF, VBUF = LY::VBUF, RR = LY::RR;
+  constexpr int KRB = SK::RB, VRB = SV::RB;
+  constexpr bool sw = ROLE == kRoleScore;
+  constexpr bool cv = ROLE == kRoleConvV;
+  static_assert(2 * NH == NDT && halves_ok<VF>(), "the d-tile pairs stay inside a half");
+  static_assert(D == 256 && kWRows * kStageRow <= LY::P0, "staged rows fit the operand buffers");
+
+  unsigned char* const kbuf = g_lds + LY::K0;
+  unsigned char* const vbuf = g_lds + LY::V0;
+  int32_t* const ids = reinterpret_cast<int32_t*>(g_lds + LY::ID0);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = wave & 3;                        // the pair: query rows 32pw .. 32pw+31
+  const int li = lane & 31;                       // query row of the lane (column of its MFMAs)
+  const int h = lane >> 5;                        // key half of its accumulators
+  const int R = a.Tq * a.r;
+  const int QG = (R + kWRows - 1) / kWRows;
+  const int n_units = a.B * a.p_max * a.Hkv * QG;
+  const int Gd = gridDim.x;
+  const int logical = xcd_logical(blockIdx.x, Gd);
+
+  const uint32_t kstride = uint32_t(a.Hkv) * KRB;
+  const uint32_t vstride = uint32_t(a.Hkv) * VRB;
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const int seg_tokens = kPNid << a.bs_shift;
+  // conversion waves: the 16-key group and its DMA (NI instructions of the
+  // side, lane offsets fixed for the kernel)
+  const int grp = pw >> 1;
+  constexpr int NI = cv ? SV::NI : SK::NI;
+  const int n_dma = sw ? 0 : NI;
+  uint32_t d_off[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) d_off[j] = cv ? SV::off(j, lane, vstride) : SK::off(j, lane, kstride);
+  // K conversion: lane = kk + 16 (k_h + 2 k_c2) converts the operand slots of
+  // key 16 grp + kk for half k_h and the C/2 steps k_c2*C/2 ..
+  constexpr int KS = C / 2;
+  const int kk = lane & 15, k_h = (lane >> 4) & 1, k_c2 = lane >> 5;
+  const int kslot = 16 * grp + kk + 32 * k_h;
+  // V conversion: every operand lane of group grp, both halves of its keys
+  const auto vl = VF::lane(li);
+  // P^T operands, flags and row factors of the pair, by tile parity
+  auto pslot = [&](int kt) __attribute__((always_inline)) {
+    return g_lds + LY::P0 + (kt & 1) * LY::PBUF + pw * 2048;
+  };
+  auto xslot = [&](int kt) __attribute__((always_inline)) {
+    return g_lds + LY::X0 + (kt & 1) * LY::XBUF + pw * 256;
+  };
+  float* const lsum = reinterpret_cast<float*>(g_lds + LY::L0) + 32 * pw;
+
+  for (int u = logical; u < n_units; u += Gd) {
+    // ---- locate the unit: ((b*p_max + p)*Hkv + g)*QG + qg ------------------
+    const int qg = u % QG;
+    const int g = (u / QG) % a.Hkv;
+    const int bp = u / (QG * a.Hkv);
+    const int b = bp / a.p_max;
+    const int p = bp - b * a.p_max;
+    int L = a.seq_len[b];
+    if (L < 0 || L > a.cap_tokens) {
+      if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
+      L = L < 0 ? 0 : a.cap_tokens;
+    }
+    if (L > 0 && L < a.Tq) {             // the chunk is longer than the sequence
+      if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
+      L = 0;
+    }
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int P = L > 0 ? (L + a.psize - 1) / a.psize : 0;
+    const int t_begin = p * a.psize;
+    const int t_end = min(L, t_begin + a.psize);
+    // this lane's query row
+    const int row = qg * kWRows + 32 * pw + li;
+    const bool valid = row < R;
+    const int tq = valid ? row / a.r : 0;
+    const int hq = g * a.r + (valid ? row - tq * a.r : 0);
+    const int64_t orow = (int64_t(b) * a.Tq + tq) * a.Hq + hq;   // row of out / partials
+    const int lim = valid ? min(L - a.Tq + tq, t_end - 1) : t_begin - 1;
+    if (L == 0) {
+      // an empty (or refused) sequence: zero rows in direct mode; the merge
+      // writes its zero rows otherwise
+      if (a.direct && sw && valid && h == 0)
+        for (int d = 0; d < D; ++d) a.out[orow * D + d] = 0.0f;
+      continue;
+    }
+    if (p >= P) continue;                 // no such partition: nothing to write
+    int lim_min = valid ? lim : INT32_MAX;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+    lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+    // last key any row of the workgroup reads: that of its last valid row
+    const int row_hi = min(R - 1, qg * kWRows + kWRows - 1);
+    const int t_stop = min(t_end, L - a.Tq + row_hi / a.r + 1);
+
+    // ---- Q^T operands (score waves): slot s of step c holds q[row][kd(c, h, s)].
+    // The workgroup's 128 rows are read whole by all its threads (16-byte
+    // loads, every row contiguous, all in flight at once), scaled, rounded to
+    // f16 into LDS and read back by the score waves in operand order; rows
+    // past R are zeros.
+    __syncthreads();                      // the LDS staging of the last unit is read
+    {
+      constexpr int CPR4 = D / 4;                       // 16-byte chunks of a row
+      constexpr int NQ = kWRows * CPR4 / kPThreads;     // per thread
+      float4 v[NQ];
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const int c = tid + k * kPThreads;
+        const int grow = qg * kWRows + c / CPR4;
+        v[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (grow < R) {
+          const int tq2 = grow / a.r;
+          const int64_t orow2 = (int64_t(b) * a.Tq + tq2) * a.Hq + g * a.r + (grow - tq2 * a.r);
+          v[k] = *reinterpret_cast<const float4*>(a.q + orow2 * D + 4 * (c % CPR4));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const int c = tid + k * kPThreads;
+        *reinterpret_cast<f16x4*>(g_lds + (c / CPR4) * kStageRow + 8 * (c % CPR4)) =
+            f16x4{f16(v[k].x * a.qscale), f16(v[k].y * a.qscale), f16(v[k].z * a.qscale), f16(v[k].w * a.qscale)};
+      }
+    }
+    __syncthreads();
+    f16x8 qop[C];
+    if (sw) {
+      const unsigned char* qs = g_lds + (32 * pw + li) * kStageRow;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const f16x8 q8 = *reinterpret_cast<const f16x8*>(qs + 2 * (KF::kd(c, h, 0) & ~7));
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qop[c][s] = q8[KF::kd(0, 0, s)];
+      }
+    }
+
+    // reference max: +inf for rows past R (their p are exactly 0); -inf until
+    // the row has seen a key (score waves)
+    float m_run = valid ? -INFINITY : INFINITY;
+    float l_lane = 0.0f;
+    f32x16 acc[NH];
+#pragma unroll
+    for (int dt = 0; dt < NH; ++dt) acc[dt] = f32x16{};
+    int bad = 0;
+
+    auto mask = [&](f32x16& s, int t0) __attribute__((always_inline)) {
+      if (t0 + kWTile - 1 > lim_min) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t0 + skey(r, h) > lim) s[r] = -INFINITY;
+      }
+    };
+    auto scores = [&](const unsigned char* kops, f32x16& sc) __attribute__((always_inline)) {
+      f16x8 kop[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) kop[c] = *reinterpret_cast<const f16x8*>(kops + (c * 64 + lane) * 16);
+      sc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C; ++c) sc = mfma32(kop[c], qop[c], sc);
+    };
+    auto row_max = [&](const f32x16& s) __attribute__((always_inline)) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      return fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+    };
+    auto scale_acc = [&](float alpha) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < NH; ++dt) acc[dt] *= alpha;
+    };
+    // lazy rescale (lucebox PR #555, Summary: skip the rescale when the max is
+    // unchanged), as in the four-wave form; the score wave also leaves the
+    // flag of tile kt (and, when set, each row's factor) for its partner
+    auto rescale = [&](float mx, int kt) __attribute__((always_inline)) {
+      unsigned char* xs = xslot(kt);
+      const int take = __builtin_amdgcn_readfirstlane(__any(mx > m_run + kSlack) ? 1 : 0);
+      if (lane == 0) *reinterpret_cast<uint32_t*>(xs) = uint32_t(take);
+      if (take) {
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_lane *= alpha;
+        scale_acc(alpha);
+        reinterpret_cast<float*>(xs + 4)[li] = alpha;
+        m_run = m_new;
+      }
+    };
+    auto probs = [&](const f32x16& s, f16x8 (&pop)[2]) __attribute__((always_inline)) {
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) ls += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+      l_lane += ls;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pop[t][e] = f16(pr[8 * t + e]);
+    };
+
+    for (int seg_t0 = t_begin; seg_t0 < t_stop; seg_t0 += seg_tokens) {
+      const int seg_t1 = min(t_stop, seg_t0 + seg_tokens);
+      const int jb0 = seg_t0 >> a.bs_shift;
+      const int nb = ((seg_t1 - 1) >> a.bs_shift) - jb0 + 1;
+      __syncthreads();                       // ids[] and every LDS buffer are free
+      int badl = 0;
+      for (int i = tid; i < nb; i += kPThreads) {
+        int32_t id = block_of(a.table, b, a.max_blocks, jb0 + i);
+        if (uint32_t(id) >= uint32_t(a.nblocks)) { badl = 1; id = 0; }
+        ids[i] = id;
+      }
+      bad |= __syncthreads_or(badl);
+      const int ntiles = (seg_t1 - seg_t0 + kWTile - 1) / kWTile;
+
+      // ---- DMA of the wave's side of group grp of tile t into ring slot
+      // t % RR (a group at or past seg_t1 gets a zero-size resource and reads
+      // nothing, one that crosses it a resource over its live rows: rows past
+      // seg_t1, junk slots maybe holding NaN, land as zeros, so their p of 0
+      // meets no NaN) -----------------------------------------------------------
+      auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint32_t slot = uint32_t(LY::RAW + (t % RR) * LY::SLOT);
+        const int tg = seg_t0 + t * kWTile + 16 * grp;
+        const bool live = tg < seg_t1;
+        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+        const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
+        const uint32_t nlive = live ? uint32_t(min(16, seg_t1 - tg)) : 0u;
+        if (!cv) {
+          const rsrc_t kr = make_rsrc(a.k_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SK::RB),
+                                      nlive * kstride);
+#pragma unroll
+          for (int j = 0; j < SK::NI; ++j) dma_lds<SK::CB>(kr, slot + grp * SK::GB + j * 64 * SK::CB, d_off[j]);
+        } else {
+          const rsrc_t vr = make_rsrc(a.v_pool + row_offset(id, slot0, a.bs_shift, a.Hkv, g, SV::RB),
+                                      nlive * vstride);
+#pragma unroll
+          for (int j = 0; j < SV::NI; ++j)
+            dma_lds<SV::CB>(vr, slot + 2 * SK::GB + grp * SV::GB + j * 64 * SV::CB, d_off[j]);
+        }
+      };
+      // ---- the raw rows of tile t in registers, and their conversion into
+      // f16 operands in LDS (a tile past the segment converts the zeros of
+      // its zero-size DMA into buffers nothing reads) ---------------------------
+      struct Raw {
+        uint32_t w[cv ? 2 * VF::kWords : KF::template words<KS>()];
+      };
+      auto raw_load = [&](int t, Raw& r) __attribute__((always_inline)) {
+        const unsigned char* raw = g_lds + LY::RAW + (t % RR) * LY::SLOT;
+        if constexpr (cv) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            VF::load(r.w + k * VF::kWords, raw + 2 * SK::GB + grp * SV::GB + pkey(0, h, 4 * k) * VRB, vl);
+        } else {
+          KF::template loadn<KS>(r.w, raw + grp * SK::GB + kk * KRB, k_h, k_c2 * KS);
+        }
+      };
+      auto raw_store = [&](int t, Raw& r) __attribute__((always_inline)) {
+        if constexpr (cv) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) VF::prep(r.w + k * VF::kWords, vl);
+          unsigned char* vops = vbuf + (t & 3) * VBUF;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const f16x4 lo = VF::op(r.w, vl, dt, mg), hi = VF::op(r.w + VF::kWords, vl, dt, mg);
+            *reinterpret_cast<f16x8*>(vops + ((grp * NDT + dt) * 64 + lane) * 16) =
+                f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        } else {
+          unsigned char* kops = kbuf + (t & 1) * KBUF;
+#pragma unroll
+          for (int cc = 0; cc < KS; ++cc)
+            *reinterpret_cast<f16x8*>(kops + ((k_c2 * KS + cc) * 64 + kslot) * 16) =
+                KF::template opn<KS>(r.w, cc, k_c2 * KS, mg);
+        }
+      };
+      // ---- PV of tile kt on the conversion wave's d-tiles: the partner's
+      // flag, P^T operands and (when it rescaled) row factors of tile kt ------
+      auto pair_pv_load = [&](int kt, f16x8 (&pop)[2], f16x8 (&vop)[2][NH]) __attribute__((always_inline)) {
+        const unsigned char* ps = pslot(kt);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pop[t] = *reinterpret_cast<const f16x8*>(ps + (t * 64 + lane) * 16);
+        const unsigned char* vops = vbuf + (kt & 3) * VBUF;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int dt = 0; dt < NH; ++dt)
+            vop[t][dt] = *reinterpret_cast<const f16x8*>(vops + ((t * NDT + NH + dt) * 64 + lane) * 16);
+      };
+      auto pair_pv_mfma = [&](int kt, const f16x8 (&pop)[2], const f16x8 (&vop)[2][NH]) __attribute__((always_inline)) {
+        const unsigned char* xs = xslot(kt);
+        if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(xs))) {
+          asm volatile("" ::: "memory");
+          scale_acc(reinterpret_cast<const float*>(xs + 4)[li]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int dt = 0; dt < NH; ++dt) acc[dt] = mfma32(vop[t][dt], pop[t], acc[dt]);
+      };
+
+      // ---- the pipeline: one barrier per tile. Iteration kt: the score waves
+      // run the softmax of kt (leaving its P^T and rescale flag), the scores
+      // of kt+1 and their half of the PV of kt; the conversion waves issue
+      // their DMA of tile kt+RR+2, load tile kt+3's raw rows into registers
+      // (their own DMA of it has landed), convert kt+2 from the registers
+      // loaded during kt-1 and run their half of the PV of kt-1. -------------
+      f32x16 s0, s1;
+      if constexpr (sw) {
+        wait_all_then_barrier(0);
+        scores(kbuf, s0);
+        wait_all_then_barrier(0);
+        auto s_step = [&](int kt, f32x16& s_cur, f32x16& s_next) __attribute__((always_inline)) {
+          mask(s_cur, seg_t0 + kt * kWTile);
+          const float mx = row_max(s_cur);
+          rescale(mx, kt);
+          // the score MFMAs of kt+1 alternate with the PV MFMAs of kt, the
+          // operand reads streaming ahead of them
+          f16x8 kop[C];
+          f16x8 vop[2][NH];
+          {
+            const unsigned char* kops = kbuf + ((kt + 1) & 1) * KBUF;
+            const unsigned char* vops = vbuf + (kt & 3) * VBUF;
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+              kop[i] = *reinterpret_cast<const f16x8*>(kops + (i * 64 + lane) * 16);
+              if (i < 2 * NH)
+                vop[i / NH][i % NH] =
+                    *reinterpret_cast<const f16x8*>(vops + (((i / NH) * NDT + i % NH) * 64 + lane) * 16);
+            }
+          }
+          f16x8 pop[2];
+          probs(s_cur, pop);
+          unsigned char* ps = pslot(kt);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) *reinterpret_cast<f16x8*>(ps + (t * 64 + lane) * 16) = pop[t];
+          s_next = f32x16{};
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            s_next = mfma32(kop[i], qop[i], s_next);
+            if (i < 2 * NH) acc[i % NH] = mfma32(vop[i / NH][i % NH], pop[i / NH], acc[i % NH]);
+          }
+          constexpr int kLead = 8, kReads = C + 2 * NH, kMfma = C + 2 * NH;
+          __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+#pragma unroll
+          for (int i = 0; i < kMfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            if (i + kLead < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        };
+        for (int kt = 0; kt < ntiles; kt += 2) {
+          s_step(kt, s0, s1);
+          wait_all_then_barrier(0);
+          if (kt + 1 >= ntiles) break;
+          s_step(kt + 1, s1, s0);
+          wait_all_then_barrier(0);
+        }
+      } else {
+        // prologue: the first RR tiles in flight; tiles 0 and 1 converted (0
+        // before the first barrier, which the score waves wait for to compute
+        // the scores of tile 0), tile 2 loaded
+        const int vm_keep = (RR - 1) * n_dma;
+#pragma unroll
+        for (int t = 0; t < RR; ++t) issue(t);
+        Raw cur, nxt;
+        wait_vm(vm_keep);
+        raw_load(0, cur);
+        raw_store(0, cur);
+        lds_drain();                          // the rows of tile 0 are read before its slot is refilled
+        issue(RR);
+        lds_barrier();
+        wait_vm(vm_keep);
+        raw_load(1, cur);
+        raw_store(1, cur);
+        lds_drain();
+        issue(RR + 1);
+        wait_vm(vm_keep);
+        raw_load(2, cur);
+        lds_barrier();
+        // (tile 0: no PV of the tile before it; every later tile's PV sits
+        // after the conversion, which needs no LDS wait)
+        auto c_step = [&](int kt, bool pv) __attribute__((always_inline)) {
+          issue(kt + RR + 2);
+          wait_vm(vm_keep);                   // own DMA of tile kt+3 has landed
+          raw_load(kt + 3, nxt);
+          f16x8 pop[2];
+          f16x8 vop[2][NH];
+          if (pv) pair_pv_load(kt - 1, pop, vop);
+          raw_store(kt + 2, cur);
+          if (pv) pair_pv_mfma(kt - 1, pop, vop);
+          cur = nxt;
+        };
+        c_step(0, false);
+        lds_barrier();
+        for (int kt = 1; kt < ntiles; ++kt) {
+          c_step(kt, true);
+          lds_barrier();
+        }
+        // the last tile's half of the PV; the DMA of tiles past the segment
+        // (zeros) lands before the ring is reused
+        {
+          f16x8 pop[2];
+          f16x8 vop[2][NH];
+          pair_pv_load(ntiles - 1, pop, vop);
+          pair_pv_mfma(ntiles - 1, pop, vop);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+
+    // ---- partial (or final) rows: each wave of a pair writes its d-tiles ---
+    mfma_drain();                          // the last PV MFMAs wrote acc
+    if (bad && tid == 0) atomicOr(a.status, 1u);
+    float l_run = 0.0f;
+    if (sw) {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+      l_run = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+      lsum[li] = l_run;
+    }
+    __syncthreads();                       // also: every LDS buffer is free
+    if (!sw) l_run = lsum[li];
+    const float inv = bad ? __builtin_nanf("") : (l_run > 0.0f ? 1.0f / l_run : 0.0f);
+    constexpr int H0 = sw ? 0 : NH;        // the wave's first d-tile
+    if (a.direct) {
+      if (valid) {
+        float* dst = a.out + orow * D;
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[VF::vd(H0 + j, skey(r, h))] = acc[j][r] * inv;
+      }
+    } else {
+      // binary16 rows staged in LDS (row stride kStageRow), then copied out
+      // 16 bytes a thread, each row's D values contiguous
+      f16* st = reinterpret_cast<f16*>(g_lds + (32 * pw + li) * kStageRow);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int dn = VF::dnext(H0 + j);
+        if (dn < 0) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          store_f16_pair(st, VF::vd(H0 + j, skey(r, h)), acc[j][r] * inv, acc[dn - H0][r] * inv);
+      }
+      if (sw && h == 0 && valid) {
+        const int64_t prow = orow * a.p_max + p;
+        a.part_ml[2 * prow] = bad ? __builtin_nanf("") : (l_run > 0.0f ? m_run : -INFINITY);
+        a.part_ml[2 * prow + 1] = l_run;
+      }
+      __syncthreads();
+      constexpr int CPR16 = D / 8;         // 16-byte chunks per row
+      for (int c = tid; c < kWRows * CPR16; c += kPThreads) {
+        const int rr = c / CPR16, col = c - rr * CPR16;
+        const int grow = qg * kWRows + rr;
+        if (grow < R) {
+          const int tq2 = grow / a.r;
+          const int64_t prow2 = ((int64_t(b) * a.Tq + tq2) * a.Hq + g * a.r + (grow - tq2 * a.r)) * a.p_max + p;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<f16*>(a.part_o) + prow2 * D + col * 8) =
+              *reinterpret_cast<const u32x4*>(g_lds + rr * kStageRow + col * 16);
+        }
+      }
+    }
+  }
+}
+
+template <int KT, int VT, int D>
+__global__ void __launch_bounds__(kPThreads, 1) chunk_pair_kernel(const ChunkArgs a) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w < 4) pair_role<KT, VT, D, kRoleScore>(a);
+  else if ((w & 1) == 0) pair_role<KT, VT, D, kRoleConvK>(a);
+  else pair_role<KT, VT, D, kRoleConvV>(a);
+}
+
+template <int KT, int VT, int D>
+hipError_t launch_pair(const ChunkArgs& a, hipStream_t stream) {
+  constexpr size_t lds = PairLds<KT, VT, D>::BYTES;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&chunk_pair_kernel<KT, VT, D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((chunk_pair_kernel<KT, VT, D>), dim3(a.grid), dim3(kPThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int KT, int VT, int D>
 hipError_t launch_wide(const ChunkArgs& a, hipStream_t stream) {
+  if constexpr (D == 256 && PairLds<KT, VT, D>::kFits) return launch_pair<KT, VT, D>(a, stream);
   constexpr size_t lds = WideLds<KT, VT, D>::BYTES;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&chunk_wide_kernel<KT, VT, D>),
