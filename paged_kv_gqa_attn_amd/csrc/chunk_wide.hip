@@ -1136,11 +1136,18 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
       // nothing, one that crosses it a resource over its live rows: rows past
       // seg_t1, junk slots maybe holding NaN, land as zeros, so their p of 0
       // meets no NaN) -----------------------------------------------------------
-      auto issue = [&](int t) __attribute__((always_inline)) {
+      // the block id of the group of tile t, read from LDS (0 past seg_t1);
+      // issue_id takes it read a tile earlier, so the DMA issue does not
+      // wait for LDS
+      auto id_load = [&](int t) __attribute__((always_inline)) {
+        const int tg = seg_t0 + t * kWTile + 16 * grp;
+        return tg < seg_t1 ? ids[(tg >> a.bs_shift) - jb0] : 0;
+      };
+      auto issue_id = [&](int t, int32_t idv) __attribute__((always_inline)) {
         const uint32_t slot = uint32_t(LY::RAW + (t % RR) * LY::SLOT);
         const int tg = seg_t0 + t * kWTile + 16 * grp;
         const bool live = tg < seg_t1;
-        const int32_t id = live ? __builtin_amdgcn_readfirstlane(ids[(tg >> a.bs_shift) - jb0]) : 0;
+        const int32_t id = __builtin_amdgcn_readfirstlane(idv);
         const int slot0 = live ? (tg & ((1 << a.bs_shift) - 1)) : 0;
         const uint32_t nlive = live ? uint32_t(min(16, seg_t1 - tg)) : 0u;
         if (!cv) {
@@ -1156,6 +1163,7 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
             dma_lds<SV::CB>(vr, slot + 2 * SK::GB + grp * SV::GB + j * 64 * SV::CB, d_off[j]);
         }
       };
+      auto issue = [&](int t) __attribute__((always_inline)) { issue_id(t, id_load(t)); };
       // ---- the raw rows of tile t in registers, and their conversion into
       // f16 operands in LDS (a tile past the segment converts the zeros of
       // its zero-size DMA into buffers nothing reads) ---------------------------
@@ -1172,13 +1180,17 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
           KF::template loadn<KS>(r.w, raw + grp * SK::GB + kk * KRB, k_h, k_c2 * KS);
         }
       };
-      auto raw_store = [&](int t, Raw& r) __attribute__((always_inline)) {
+      // (in two halves: steps or d-tiles [lo, hi) of the lane's job; the
+      // first half also realigns the raw V words)
+      auto raw_store = [&](int t, Raw& r, int lo, int hi) __attribute__((always_inline)) {
         if constexpr (cv) {
+          if (lo == 0) {
 #pragma unroll
-          for (int k = 0; k < 2; ++k) VF::prep(r.w + k * VF::kWords, vl);
+            for (int k = 0; k < 2; ++k) VF::prep(r.w + k * VF::kWords, vl);
+          }
           unsigned char* vops = vbuf + (t & 3) * VBUF;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
+          for (int dt = lo; dt < hi; ++dt) {
             const f16x4 lo = VF::op(r.w, vl, dt, mg), hi = VF::op(r.w + VF::kWords, vl, dt, mg);
             *reinterpret_cast<f16x8*>(vops + ((grp * NDT + dt) * 64 + lane) * 16) =
                 f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1186,7 +1198,7 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
         } else {
           unsigned char* kops = kbuf + (t & 1) * KBUF;
 #pragma unroll
-          for (int cc = 0; cc < KS; ++cc)
+          for (int cc = lo * KS / NDT; cc < hi * KS / NDT; ++cc)
             *reinterpret_cast<f16x8*>(kops + ((k_c2 * KS + cc) * 64 + kslot) * 16) =
                 KF::template opn<KS>(r.w, cc, k_c2 * KS, mg);
         }
@@ -1276,6 +1288,9 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
           wait_all_then_barrier(0);
         }
       } else {
+        // the conversion waves set the pace of a tile: their instructions
+        // issue before the score waves' when both are ready
+        __builtin_amdgcn_s_setprio(2);
         // prologue: the first RR tiles in flight; tiles 0 and 1 converted (0
         // before the first barrier, which the score waves wait for to compute
         // the scores of tile 0), tile 2 loaded
@@ -1285,13 +1300,13 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
         Raw cur, nxt;
         wait_vm(vm_keep);
         raw_load(0, cur);
-        raw_store(0, cur);
+        raw_store(0, cur, 0, NDT);
         lds_drain();                          // the rows of tile 0 are read before its slot is refilled
         issue(RR);
         lds_barrier();
         wait_vm(vm_keep);
         raw_load(1, cur);
-        raw_store(1, cur);
+        raw_store(1, cur, 0, NDT);
         lds_drain();
         issue(RR + 1);
         wait_vm(vm_keep);
@@ -1299,15 +1314,25 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
         lds_barrier();
         // (tile 0: no PV of the tile before it; every later tile's PV sits
         // after the conversion, which needs no LDS wait)
+        int32_t idn = id_load(RR + 2);
         auto c_step = [&](int kt, bool pv) __attribute__((always_inline)) {
-          issue(kt + RR + 2);
+          issue_id(kt + RR + 2, idn);
+          idn = id_load(kt + RR + 3);
           wait_vm(vm_keep);                   // own DMA of tile kt+3 has landed
           raw_load(kt + 3, nxt);
           f16x8 pop[2];
           f16x8 vop[2][NH];
           if (pv) pair_pv_load(kt - 1, pop, vop);
-          raw_store(kt + 2, cur);
+          raw_store(kt + 2, cur, 0, NDT / 2);
           if (pv) pair_pv_mfma(kt - 1, pop, vop);
+          raw_store(kt + 2, cur, NDT / 2, NDT);
+          if (pv) {
+#pragma unroll
+            for (int i = 0; i < 2 * NH; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+          }
           cur = nxt;
         };
         c_step(0, false);
@@ -1325,6 +1350,7 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
           pair_pv_mfma(ntiles - 1, pop, vop);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_setprio(0);
       }
     }
 
