@@ -337,12 +337,13 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * one kv head with all of its rows (at D = 256 with more than 16 rows, two
  * waves per kv head, each over half of the head dimension, adding their
  * partial scores through LDS); path 3, for more than 64 query rows per kv
- * head (prefill chunks), converts each tile once per workgroup for four
- * waves of 32 rows on 32x32 MFMAs (at D = 256 the plan takes it only where
- * its 128-row blocks are as full as 64-row ones and its units fill at least
- * half the compute units). The plan picks path 2 or 3 where it applies; a caller may
+ * head (prefill chunks), converts each tile once per workgroup for 128 query
+ * rows on 32x32 MFMAs, in eight waves (score waves and conversion waves two
+ * per SIMD) or, for F16 K and V at D = 256 and F16 with Q8_0, in four (there
+ * the plan takes it only where its units fill at least half the compute
+ * units). The plan picks path 2 or 3 where it applies; a caller may
  * set path = 1 on any plan, or 3 on one for path 1, to force that kernel.
- * Pools or q that are not 16-byte aligned run path 1.
+ * Pools, q or ws that are not 16-byte aligned run path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;

@@ -15,6 +15,7 @@
 
 #include "../../include/paged_attn.h"
 #include "pa_host.h"
+#include "wide_plan.h"
 
 namespace pa {
 
@@ -539,24 +540,24 @@ extern "C" int32_t paged_attn_chunk_plan(const pa_shape* shape, int32_t tq, int3
     }
     return ps_best;
   };
-  // The wide-tile kernel takes chunks of more than 64 query rows per kv head.
-  // At D = 256 it does where its 128-row blocks are no emptier than the tile
-  // kernel's 64-row ones and its units fill at least half the compute units
-  // (one workgroup each); otherwise the tile kernel, two per compute unit,
-  // was measured as fast or faster (B=8 x 32K Q4_0/Q8_0: 144 rows 468
-  // against 412 us; a 64-token chunk over 8K, 72 units: F16 89 against 78
-  // us, while 144 units at 128 tokens take 92 against 97).
+  // The wide-tile kernel takes chunks of more than 64 query rows per kv head:
+  // in its paired form always (measured 0.63-0.95x the tile kernel's time
+  // over B=8 x 32K chunks of 72-192 rows and 32-512-token chunks over 8K).
+  // In its four-wave form (F16 K and V at D = 256, F16 with Q8_0) it does
+  // where its units fill at least half the compute units (one workgroup
+  // each; F16/F16: 0.86-0.95x over 72-192 rows at B=8 x 32K and 128-512
+  // tokens over 8K); with fewer the tile kernel, two per compute unit, was
+  // measured faster (a 64-token chunk over 8K in 72 units: 80 against 78 us).
   const int64_t rows = int64_t(tq) * r;
   bool wide = !window && chunk_wide_pick(rows, s.D);
   int64_t psize = 0;
   if (wide) {
     const int64_t qt_w = ceil_div(rows, int64_t(kWideRows));
     psize = size_partitions(qt_w, 1, 1);
-    if (s.D == 256) {
-      const int64_t qt_t = ceil_div(rows, int64_t(64 * nt));
+    if (!chunk_wide_paired(s.k_type, s.v_type, s.D)) {
       const int64_t units_w =
           int64_t(s.B) * std::max<int64_t>(1, ceil_div(std::max<int64_t>(L, 1), psize)) * s.Hkv * qt_w;
-      if (qt_w * kWideRows > qt_t * 64 * nt || 2 * units_w < num_cus) wide = false;
+      if (2 * units_w < num_cus) wide = false;
     }
   }
   // the window kernel takes short chunks (a workgroup per kv-head quad, two

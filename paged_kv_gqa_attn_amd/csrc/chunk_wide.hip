@@ -46,6 +46,7 @@
 
 #include "decode_common.h"
 #include "lds_ring.h"
+#include "wide_plan.h"
 
 namespace pa {
 namespace {
@@ -866,9 +867,9 @@ __host__ __device__ constexpr bool halves_ok() {
   return true;
 }
 constexpr int kPNid = 256;      // block ids staged per segment
-// LDS row stride of the staged Q rows and partial rows (binary16, D = 256):
-// 16 bytes of padding spread a wave's rows over the banks
-constexpr int kStageRow = 2 * 256 + 16;
+// LDS row stride of the staged Q rows and partial rows (binary16): 16 bytes
+// of padding spread a wave's rows over the banks
+constexpr int stage_row(int D) { return 2 * D + 16; }
 
 template <int KT, int VT, int D> struct PairLds {
   using SK = Stage<KT, D>;
@@ -921,7 +922,8 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
   constexpr bool sw = ROLE == kRoleScore;
   constexpr bool cv = ROLE == kRoleConvV;
   static_assert(2 * NH == NDT && halves_ok<VF>(), "the d-tile pairs stay inside a half");
-  static_assert(D == 256 && kWRows * kStageRow <= LY::P0, "staged rows fit the operand buffers");
+  constexpr int kStageRow = stage_row(D);
+  static_assert(kWRows * kStageRow <= LY::P0, "staged rows fit the operand buffers");
 
   unsigned char* const kbuf = g_lds + LY::K0;
   unsigned char* const vbuf = g_lds + LY::V0;
@@ -1429,7 +1431,9 @@ hipError_t launch_pair(const ChunkArgs& a, hipStream_t stream) {
 
 template <int KT, int VT, int D>
 hipError_t launch_wide(const ChunkArgs& a, hipStream_t stream) {
-  if constexpr (D == 256 && PairLds<KT, VT, D>::kFits) return launch_pair<KT, VT, D>(a, stream);
+  static_assert(kF16 == PA_F16 && kQ8_0 == PA_Q8_0 && kQ4_0 == PA_Q4_0, "type codes");
+  static_assert(PairLds<KT, VT, D>::kFits == chunk_wide_paired(KT, VT, D), "the planner's form matches the LDS layout");
+  if constexpr (chunk_wide_paired(KT, VT, D)) return launch_pair<KT, VT, D>(a, stream);
   constexpr size_t lds = WideLds<KT, VT, D>::BYTES;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&chunk_wide_kernel<KT, VT, D>),

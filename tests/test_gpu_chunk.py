@@ -48,16 +48,17 @@ def window_ok(c, Tq):
 
 def wide_paths(c, Tq):
     """The kernels the plan may pick besides the window kernel: the wide-tile
-    kernel (plan path 3) takes more than 64 query rows per kv head, at D=256
-    only where its 128-row blocks are no emptier than 64-row ones (and then
-    only if its units fill half the compute units, which the test does not
-    mirror); the tile kernel (path 1) the rest."""
+    kernel (plan path 3) takes more than 64 query rows per kv head, always in
+    its paired form (every type pair at D=128; at D=256 all but F16 K and V
+    together and F16 with Q8_0), in its four-wave form only if its units fill
+    half the compute units, which the test does not mirror; the tile kernel
+    (path 1) the rest."""
     rows = Tq * (c.Hq // c.Hkv)
     if rows <= 64:
         return {1}
-    if c.D == 128:
-        return {3}
-    return {1, 3} if -(-rows // 128) * 128 <= -(-rows // 64) * 64 else {1}
+    four_wave = c.D == 256 and ((c.k_fmt == "f16" and c.v_fmt != "q4_0") or
+                                (c.v_fmt == "f16" and c.k_fmt != "q4_0"))
+    return {1, 3} if four_wave else {3}
 
 
 def _plan(c, Tq, path=None, **kw):

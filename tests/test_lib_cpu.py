@@ -347,8 +347,9 @@ def test_chunk_plan_kernel_choice():
     D=256, where the head dimension is split over two waves and a workgroup
     takes a kv-head pair, two per compute unit; the wide-tile kernel (path 3)
     for more than 64 rows, a workgroup per (sequence, partition, kv head, 128
-    rows), one per compute unit (at D=256 only where 128-row blocks are as
-    full as 64-row ones and the units fill at least half the CUs); the tile-conversion
+    rows), one per compute unit (in its four-wave form, for F16 K and V at
+    D=256 and F16 with Q8_0, only where its units fill at least half the
+    CUs); the tile-conversion
     kernel (path 1) otherwise. A plan forced to path 2 where it does not apply, or to a path
     that does not exist, is refused before launch."""
     p = pa.paged_attn_chunk_plan(_shape(), 9, 32768, total_tokens=8 * 32768, num_cus=256)
@@ -369,13 +370,17 @@ def test_chunk_plan_kernel_choice():
         assert wide.path == 3 and wide.grid == min(8 * wide.p_max * 4 * 1, 256)    # 72 rows
         pre = pa.paged_attn_chunk_plan(_shape(D=D, B=1), 512, 8192, total_tokens=8192, num_cus=256)
         assert pre.path == 3 and pre.grid == min(pre.p_max * 4 * 24, 256)         # 3072 rows
-    # at D=256: 192 rows fill two 128-row blocks to 75% and three 64-row
-    # blocks whole; a 64-token chunk over 8K makes 72 wide units, fewer than
-    # half the CUs, a 128-token one 144
-    assert pa.paged_attn_chunk_plan(_shape(), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 1
-    assert pa.paged_attn_chunk_plan(_shape(B=1), 64, 8192, total_tokens=8192, num_cus=256).path == 1
-    t128 = pa.paged_attn_chunk_plan(_shape(B=1), 128, 8192, total_tokens=8192, num_cus=256)
+    # the paired form takes every chunk of more than 64 rows: 192 rows, and a
+    # 64-token chunk over 8K (72 units)
+    assert pa.paged_attn_chunk_plan(_shape(), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 3
+    assert pa.paged_attn_chunk_plan(_shape(B=1), 64, 8192, total_tokens=8192, num_cus=256).path == 3
+    # the four-wave form (F16 K and V at D=256) needs units for half the CUs:
+    # 72 at a 64-token chunk over 8K are too few, 144 at 128 tokens enough
+    f16 = dict(k_type="f16", v_type="f16")
+    assert pa.paged_attn_chunk_plan(_shape(B=1, **f16), 64, 8192, total_tokens=8192, num_cus=256).path == 1
+    t128 = pa.paged_attn_chunk_plan(_shape(B=1, **f16), 128, 8192, total_tokens=8192, num_cus=256)
     assert t128.path == 3 and t128.grid == 144
+    assert pa.paged_attn_chunk_plan(_shape(**f16), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 3
     assert pa.paged_attn_chunk_plan(_shape(D=128), 32, 32768, total_tokens=8 * 32768, num_cus=256).path == 3
     p.path = 2
     with pytest.raises(pa.PaError) as e:
