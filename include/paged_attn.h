@@ -343,7 +343,8 @@ int32_t paged_attn_status(void* ws, void* stream, uint32_t* flags);
  * the plan takes it only where its units fill at least half the compute
  * units). The plan picks path 2 or 3 where it applies; a caller may
  * set path = 1 on any plan, or 3 on one for path 1, to force that kernel.
- * Pools, q or ws that are not 16-byte aligned run path 1.
+ * Pools or q that are not 16-byte aligned (or a ws that is not, outside
+ * the layout above) run path 1.
  */
 typedef struct pa_chunk_plan {
   pa_shape shape;
