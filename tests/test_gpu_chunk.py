@@ -284,6 +284,21 @@ def test_wide_and_tile_kernels_agree(pair, D, rows):
         _check(c, qc, o3)
 
 
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("path,Tq,D,pair", [(1, 9, 256, ("q4_0", "q8_0")), (2, 4, 256, ("q4_0", "q4_0")),
+                                            (3, 16, 256, ("q4_0", "q4_0")), (3, 16, 256, ("f16", "f16")),
+                                            (3, 24, 128, ("q8_0", "q4_0"))])
+def test_block_sizes_on_every_kernel(path, Tq, D, pair, bs):
+    """Blocks of 32 and 64 tokens on each chunk kernel (the wide-tile kernel in
+    both its forms), with sequence ends inside a block and inside a 16-key
+    group: every kernel takes its 16-row groups from inside one block."""
+    Hq, Hkv = (24, 4) if D == 256 else (32, 8)
+    c, qc = _case([bs * 3 + 17, bs - 1 + Tq, 2 * bs + 5], Tq, seed=bs + 7 * path + D, k_fmt=pair[0],
+                  v_fmt=pair[1], D=D, Hq=Hq, Hkv=Hkv, block_size=bs)
+    o, _ = _run(c, qc, _plan(c, Tq, path=path, partition_tokens=64))
+    _check(c, qc, o)
+
+
 @pytest.mark.parametrize("path", [2, 3])
 def test_unaligned_pools_run_the_tile_kernel(path):
     """Pools that are not 16-byte aligned run the tile-conversion kernel even
