@@ -548,7 +548,6 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
     lim_min = __builtin_amdgcn_readfirstlane(lim_min);
-    const bool wave_rows = __any(valid);
     // last key any row of the workgroup reads: that of its last valid row
     const int row_hi = min(R - 1, qg * kWRows + kWRows - 1);
     const int t_stop = min(t_end, L - a.Tq + row_hi / a.r + 1);
@@ -651,20 +650,6 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pop[t][e] = f16(pr[8 * t + e]);
-    };
-    // O^T += V^T P^T over the tile's two 16-key steps
-    auto pv_load = [&](const unsigned char* vops, f16x8 (&vop)[2][NDT]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          vop[t][dt] = *reinterpret_cast<const f16x8*>(vops + ((t * NDT + dt) * 64 + lane) * 16);
-    };
-    auto pv_mfma = [&](const f16x8 (&vop)[2][NDT], const f16x8 (&pop)[2]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma32(vop[t][dt], pop[t], acc[dt]);
     };
 
     for (int seg_t0 = t_begin; seg_t0 < t_stop; seg_t0 += seg_tokens) {
