@@ -17,27 +17,32 @@
 //     O^T += V^T P^T once converted to f16 (the V^T operand lists its keys
 //     in the accumulators' order), so P never moves between lanes. Each lane
 //     holds one query row (lanes l and l+32 split its keys), so the row max
-//     is 15 in-lane max operations and one lane swap.
-//   * A workgroup of four wave64s takes a unit (sequence b, key partition p,
-//     kv head g, 128 query rows), wave w owning rows 32w .. 32w+31. A wave
-//     holds its rows' Q operands (D/4 registers) and O^T accumulators (D/2),
-//     so the kernel runs one workgroup per CU with 512 registers per lane:
-//     Q^T and O^T in AGPRs, where the MFMAs read and write them. Every
-//     operand the MFMAs read from LDS serves 32 rows: 1 KB per 32x32x16
-//     MFMA, twice the rows per operand byte of the 16x16 tiles of chunk.hip.
-//   * The raw K/V rows of each 32-key tile arrive by DMA in an LDS ring of
-//     3-4 tiles, the 16 rows of a group of kv head g back to back, through
-//     the block table (64-bit row addresses, mlxcel issue #2153); every tile
-//     is converted to f16 once per workgroup into LDS in MFMA operand order,
-//     each wave a quarter of it (8 keys of K, and 4 keys of every V^T
-//     operand lane of one 16-key group).
-//   * One barrier per tile, in a software pipeline: while the softmax and PV
-//     of tile kt run, the scores of tile kt+1 are computed and tile kt+2 is
-//     converted; the DMA runs RR-1 tiles ahead. K operands are double- and
-//     V operands triple-buffered (V of tile kt is read one iteration later
-//     than K). At one wave per SIMD a tile's parts overlap only as far as
-//     the instruction order interleaves them, so each tile is two branch-
-//     free regions with scheduling groups.
+//     is 15 in-lane max operations and one lane swap. Every operand the
+//     MFMAs read from LDS serves 32 rows: 1 KB per 32x32x16 MFMA, twice the
+//     rows per operand byte of the 16x16 tiles of chunk.hip.
+//   * A workgroup takes a unit (sequence b, key partition p, kv head g, 128
+//     query rows). The raw K/V rows of each 32-key tile arrive by DMA in an
+//     LDS ring, the 16 rows of a group of kv head g back to back, through
+//     the block table (64-bit row addresses, mlxcel issue #2153); a group
+//     that crosses the end of the keys gets a buffer resource over its live
+//     rows, so junk slots land as zeros. Every tile is converted to f16 once
+//     per workgroup into LDS in MFMA operand order, one barrier per tile.
+//   * Paired form (chunk_pair_kernel; every type pair at D = 128, all but
+//     F16/F16, F16/Q8_0 and Q8_0/F16 at D = 256): eight waves, two per SIMD.
+//     Score wave w holds the Q^T of rows 32w .. 32w+31 and per tile kt runs
+//     the softmax of kt, the scores of kt+1 and the PV of the first half of
+//     the d-tiles, leaving its P^T operands and rescale flags in LDS; the
+//     conversion wave on its SIMD DMAs and converts one side (K or V) of one
+//     16-key group of every tile, from registers loaded a tile ahead, and
+//     runs the PV of the second half of the d-tiles for kt-1. No AGPRs (the
+//     compiler would split the 256 registers of two waves per SIMD evenly
+//     between VGPRs and AGPRs); one instantiation of the body per role.
+//   * Four-wave form (chunk_wide_kernel; F16/F16, F16/Q8_0 and Q8_0/F16 at
+//     D = 256, whose raw tiles leave no LDS for the paired form's ring): wave
+//     w owns rows 32w .. 32w+31, holds its Q^T (D/4 registers) and O^T
+//     (D/2) in AGPRs at one workgroup per CU with 512 registers per lane, and
+//     converts a quarter of each tile; the score MFMAs of kt+1 alternate with
+//     the PV MFMAs of kt, operand reads streaming ahead of them.
 //   * Causal limit per row; tiles past the workgroup's last row are not
 //     read and only tiles that cross some row's limit are masked. Partials
 //     (normalised binary16 o, fp32 m and l) use the decode layout with Tq*Hq
