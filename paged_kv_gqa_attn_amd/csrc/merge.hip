@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
               a.part_ml + int64_t(bh) * a.p_max * 2, P, a.D, col0, a.out + int64_t(bh) * a.D + col0, lds);
 }
 
-// NPM: the most partitions a row has (8 or 16)
+// NPM: the most partitions a row has (2 to 32)
 template <int NPM>
 __global__ void __launch_bounds__(kThreads) merge_rows_kernel(const MergeArgs a) {
   const int octs = a.D / 8;
@@ -113,12 +113,18 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     const int64_t threads = rows * (a.D / 8);
     const int64_t blocks = (threads + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (a.p_max <= 8)
-      hipLaunchKernelGGL(merge_rows_kernel<8>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
-    else if (a.p_max <= 16)
-      hipLaunchKernelGGL(merge_rows_kernel<16>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(merge_rows_kernel<32>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    // the smallest unrolled partition count that covers p_max: slots past a
+    // row's partitions re-read its last one and add 0, so a tight count saves
+    // those loads and their arithmetic
+    const dim3 g{unsigned(blocks)}, t{unsigned(kThreads)};
+    if (a.p_max <= 2) hipLaunchKernelGGL(merge_rows_kernel<2>, g, t, 0, stream, a);
+    else if (a.p_max <= 4) hipLaunchKernelGGL(merge_rows_kernel<4>, g, t, 0, stream, a);
+    else if (a.p_max <= 6) hipLaunchKernelGGL(merge_rows_kernel<6>, g, t, 0, stream, a);
+    else if (a.p_max <= 8) hipLaunchKernelGGL(merge_rows_kernel<8>, g, t, 0, stream, a);
+    else if (a.p_max <= 12) hipLaunchKernelGGL(merge_rows_kernel<12>, g, t, 0, stream, a);
+    else if (a.p_max <= 16) hipLaunchKernelGGL(merge_rows_kernel<16>, g, t, 0, stream, a);
+    else if (a.p_max <= 24) hipLaunchKernelGGL(merge_rows_kernel<24>, g, t, 0, stream, a);
+    else hipLaunchKernelGGL(merge_rows_kernel<32>, g, t, 0, stream, a);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq * (a.D / kCols)), dim3(kThreads), 0, stream, a);
   }
