@@ -190,9 +190,12 @@ MERGE_CASES = {
     # 44 sequences x 24 heads = 1056 rows of at most 5 partitions: the
     # row-per-thread merge layout
     "rows_p5": ([0, 1, 64, 65, 300, 17, 128, 129] * 5 + [0, 300, 33, 200], 24, 4),
-    # ... and of at most 16 partitions
+    # ... and of at most 12 and 16 partitions (two lanes per row and 8 columns)
+    "rows_p12": ([0, 1, 64, 65, 750, 17, 640, 129] * 5 + [0, 700, 33, 200], 24, 4),
     "rows_p16": ([0, 1, 64, 65, 1000, 17, 640, 129] * 5 + [0, 1000, 33, 200], 24, 4),
-    # 27 x 24 = 648 rows of at most 32 partitions
+    # 27 x 24 = 648 rows of at most 24 and 32 partitions (four lanes; rows of
+    # fewer partitions than lanes leave lanes with none)
+    "rows_p24": ([0, 1, 64, 65, 1500, 17, 1280, 129] * 3 + [0, 1536, 33], 24, 4),
     "rows_p32": ([0, 1, 64, 65, 2000, 17, 1280, 129] * 3 + [0, 2048, 33], 24, 4),
 }
 
@@ -204,7 +207,8 @@ def test_merge_kernel_on_oracle_partials(name):
     merge of the same values; and against the unrounded partials within what
     binary16 rounding of o can move the result (2^-11 of the largest |o_p|).
     Both merge layouts are covered: few rows (any partition count) and many
-    rows of at most 8, 16 or 32 partitions."""
+    rows of at most 6, 12, 16, 24 or 32 partitions (one, two or four lanes per
+    row and 8 columns)."""
     pa = pa_mod()
     lens, Hq, Hkv = MERGE_CASES[name]
     case = _case(lens, k_fmt="f16", v_fmt="q8_0", seed=23, Hq=Hq, Hkv=Hkv)
@@ -233,6 +237,39 @@ def test_merge_kernel_on_oracle_partials(name):
     for b, L in enumerate(lens):
         if L == 0:
             assert np.all(got[b] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["p32", "rows_p5", "rows_p16", "rows_p32"])
+def test_merge_nan_m_poisons_only_its_row(name):
+    """A NaN m (what a partition that met a bad block id leaves) makes its
+    whole row NaN on both merge layouts, whichever lane of a row's group
+    holds that partition, and leaves every other row as it was."""
+    pa = pa_mod()
+    lens, Hq, Hkv = MERGE_CASES[name]
+    case = _case(lens, k_fmt="f16", v_fmt="q8_0", seed=29, Hq=Hq, Hkv=Hkv)
+    plan = plan_for(case, partition_tokens=64)
+    plan.fused = 0
+    m, l, o, n = _oracle_partials(case, plan.psize)
+    B, Hq, P, D = o.shape
+    b_long = int(np.argmax(n))
+    bad = [(b_long, 1, int(n[b_long]) - 1), (b_long, Hq - 1, 1 % int(n[b_long]))]
+    for b, h, p in bad:
+        m[b, h, p] = np.nan
+    ml = np.stack([m, l], axis=-1).astype(np.float32)
+    ws = pa.workspace(plan, "cpu")
+    n_o = B * Hq * P * D
+    at = int(plan.part_offset)
+    ws[at:at + 2 * n_o] = torch.from_numpy(o.astype(np.float16).reshape(-1)).view(torch.uint8)
+    ws[at + 2 * n_o:at + 2 * n_o + 8 * B * Hq * P] = torch.from_numpy(ml.reshape(-1)).view(torch.uint8)
+    out = torch.zeros((B, Hq, D), device=DEV)
+    pa.paged_attn_merge(plan, ws.to(DEV), case.seq_len.to(DEV), out)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    poisoned = np.zeros((B, Hq), dtype=bool)
+    for b, h, _ in bad:
+        poisoned[b, h] = True
+    assert np.all(np.isnan(got[poisoned]))
+    assert np.all(np.isfinite(got[~poisoned]))
 
 
 @pytest.mark.parametrize("path", PATHS)
