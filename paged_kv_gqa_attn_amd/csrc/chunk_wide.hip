@@ -515,12 +515,13 @@ __global__ void __launch_bounds__(kWThreads, 1) chunk_wide_kernel(const ChunkArg
     d_off[j] = d_v ? (j < SV::NI ? SV::off(j, lane, vstride) : 0u) : (j < SK::NI ? SK::off(j, lane, kstride) : 0u);
 
   for (int u = logical; u < n_units; u += Gd) {
-    // ---- locate the unit: ((b*p_max + p)*Hkv + g)*QG + qg ------------------
-    const int qg = u % QG;
-    const int g = (u / QG) % a.Hkv;
-    const int bp = u / (QG * a.Hkv);
-    const int b = bp / a.p_max;
-    const int p = bp - b * a.p_max;
+    // ---- locate the unit: ((b*Hkv + g)*QG + qg)*p_max + p ------------------
+    // (the partition varies fastest, so the units that read one Q run side by
+    // side on one XCD, whose L2 then serves that Q once for all of them)
+    const int p = u % a.p_max;
+    const int qg = (u / a.p_max) % QG;
+    const int g = (u / (a.p_max * QG)) % a.Hkv;
+    const int b = u / (a.p_max * QG * a.Hkv);
     int L = a.seq_len[b];
     if (L < 0 || L > a.cap_tokens) {
       if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
@@ -960,12 +961,13 @@ __device__ __forceinline__ void pair_role(const ChunkArgs& a) {
   float* const lsum = reinterpret_cast<float*>(g_lds + LY::L0) + 32 * pw;
 
   for (int u = logical; u < n_units; u += Gd) {
-    // ---- locate the unit: ((b*p_max + p)*Hkv + g)*QG + qg ------------------
-    const int qg = u % QG;
-    const int g = (u / QG) % a.Hkv;
-    const int bp = u / (QG * a.Hkv);
-    const int b = bp / a.p_max;
-    const int p = bp - b * a.p_max;
+    // ---- locate the unit: ((b*Hkv + g)*QG + qg)*p_max + p ------------------
+    // (the partition varies fastest, so the units that read one Q run side by
+    // side on one XCD, whose L2 then serves that Q once for all of them)
+    const int p = u % a.p_max;
+    const int qg = (u / a.p_max) % QG;
+    const int g = (u / (a.p_max * QG)) % a.Hkv;
+    const int b = u / (a.p_max * QG * a.Hkv);
     int L = a.seq_len[b];
     if (L < 0 || L > a.cap_tokens) {
       if (tid == 0 && p == 0 && g == 0 && qg == 0) atomicOr(a.status, 2u);
