@@ -359,9 +359,8 @@ def test_verify_windows_at_full_size(Tq):
     (the chunk benchmark's workloads), on the automatic plan: the window
     kernel, a kv-head quad per workgroup for 12 query rows per kv head, a
     kv-head pair with the head dimension split over two waves for 24 and 48.
-    One sequence per case (2, 4, 0) is checked against the oracle, which
-    reads host copies of just its blocks."""
-    from gpu_util import BlockSubset
+    Every output row (all sequences, tokens and query heads) is checked
+    against the oracle."""
     pa = pa_mod()
     case = synth.workload("uniform_q4_0", B=8, L=32768, seed=1500 + Tq, device=DEV)
     qc = torch.randn((case.B, Tq, case.Hq, case.D), generator=torch.Generator().manual_seed(1600 + Tq))
@@ -375,18 +374,16 @@ def test_verify_windows_at_full_size(Tq):
     pa.paged_attn_chunk(plan, qc.to(DEV), case.k_pool, case.v_pool, case.table, case.seq_len, ws, out)
     torch.cuda.synchronize()
     assert pa.paged_attn_status(ws) == 0
-    tab = case.table.cpu()
-    for b in (Tq % case.B,):
-        n = -(-case.seq_lens[b] // case.block_size)
-        blocks = tab[b, :n].tolist()
-        ref = oracle.chunk(qc[b:b + 1], BlockSubset(case.k_pool, blocks), BlockSubset(case.v_pool, blocks),
-                           tab[b:b + 1], case.seq_len[b:b + 1].cpu(), Hkv=case.Hkv, D=case.D,
-                           block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
-                           nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
-        got = out[b:b + 1].cpu().double().numpy()
-        assert np.isfinite(got).all(), f"sequence {b}: non-finite output"
-        worst = float(rel_err_rows(got, ref).max())
-        assert worst <= tol_for(case), f"sequence {b}: max row error {worst:.3e}"
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all(), "non-finite output"
+    kp, vp = case.k_pool.cpu().numpy().reshape(-1), case.v_pool.cpu().numpy().reshape(-1)
+    ref = oracle.chunk(qc, kp, vp, case.table.cpu(), case.seq_len.cpu(), Hkv=case.Hkv, D=case.D,
+                       block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
+                       nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
+    err = rel_err_rows(got, ref)                  # [B, Tq, Hq]
+    worst = float(err.max())
+    b, t, h = np.unravel_index(int(err.argmax()), err.shape)
+    assert worst <= tol_for(case), f"max row error {worst:.3e} at sequence {b}, token {t}, head {h}"
     del case, ws, out
     torch.cuda.empty_cache()
 
@@ -406,10 +403,10 @@ def test_wide_partition_longer_than_a_segment(pair):
 
 def test_prefill_chunk_at_full_size():
     """The chunk benchmark's prefill chunk: 512 tokens over a Q4_0 sequence
-    of 8192 (3072 query rows per kv head) on the plan's wide-tile kernel. Its
-    last 6 tokens are checked against the oracle as a 6-token chunk of the
-    same sequence, and its first 6 as a 6-token chunk of the sequence cut
-    after them (the keys each token sees are the same)."""
+    of 8192 (3072 query rows per kv head) on the plan's wide-tile kernel.
+    Every output row is checked against the oracle; so are its first 6
+    tokens once more as a 6-token chunk of the sequence cut after them (the
+    keys each token sees are the same)."""
     pa = pa_mod()
     Tq, L = 512, 8192
     case = synth.workload("uniform_q4_0", B=1, L=L, seed=1700, device=DEV)
@@ -427,14 +424,14 @@ def test_prefill_chunk_at_full_size():
     assert torch.isfinite(got).all()
     kp, vp = case.k_pool.cpu().numpy().reshape(-1), case.v_pool.cpu().numpy().reshape(-1)
     tab = case.table.cpu()
-    for first in (False, True):
-        toks = slice(0, 6) if first else slice(Tq - 6, Tq)
-        n = L - Tq + 6 if first else L
+    for toks, n in ((slice(0, Tq), L), (slice(0, 6), L - Tq + 6)):
         ref = oracle.chunk(qc[:, toks], kp, vp, tab, torch.tensor([n], dtype=torch.int32), Hkv=case.Hkv,
                            D=case.D, block_size=case.block_size, k_fmt=case.k_fmt, v_fmt=case.v_fmt,
                            nblocks=case.nblocks, max_blocks=case.max_blocks, scale=case.scale)
-        worst = float(rel_err_rows(got[:, toks].double().numpy(), ref).max())
-        assert worst <= tol_for(case), f"tokens {toks}: max row error {worst:.3e}"
+        err = rel_err_rows(got[:, toks].double().numpy(), ref)
+        worst = float(err.max())
+        _, t, h = np.unravel_index(int(err.argmax()), err.shape)
+        assert worst <= tol_for(case), f"tokens {toks}: max row error {worst:.3e} at token {t}, head {h}"
     del case, ws, out
     torch.cuda.empty_cache()
 
