@@ -191,8 +191,11 @@ int32_t paged_attn_plan(const pa_shape* shape, int32_t max_seq_len, int64_t tota
  *               The counters [4, 12) and done[] must be zero before the first
  *               fused decode (the workspace is zero-filled once); every fused
  *               decode leaves them zero (its last workgroup resets them), and
- *               no other call writes them. Calls that share one workspace must
- *               not overlap in time.
+ *               no call of the same B and Hkv writes them. A plan of a smaller
+ *               B or Hkv has a smaller part_offset and writes partials there:
+ *               zero the workspace again before a fused decode that follows
+ *               such a plan on it. Calls that share one workspace must not
+ *               overlap in time.
  *   partials    only when plan->direct == 0, at offset plan->part_offset
  *               (256 + 4160*B*ceil(Hkv/4) rounded up to 256):
  *               uint16 o[B][Hq][p_max][D]  normalised output of each partition
@@ -274,9 +277,11 @@ int32_t paged_attn_step(const pa_plan* plan, const float* q, const void* k_pool,
  * still passes q, the pools, the table, seq_len and out, laid out as for
  * paged_attn_step; the call allocates nothing (no hipMalloc, hipFree or
  * allocating library routine) and enqueues nothing but the kernels.
- *   Returns PA_ERR_INVALID when plan->ws_bytes exceeds the 64 MiB scratch,
- *   PA_ERR_HIP when the scratch's device address cannot be obtained, else as
- *   paged_attn_step.
+ *   Returns PA_ERR_INVALID when plan->ws_bytes exceeds the 64 MiB scratch or
+ *   plan->fused is set (the single launch needs counters that start at zero,
+ *   and in the shared scratch a two-launch plan of a smaller batch writes its
+ *   partials where they lie), PA_ERR_HIP when the scratch's device address
+ *   cannot be obtained, else as paged_attn_step.
  *   Every call on one GPU shares that GPU's scratch: calls that overlap on one
  *   GPU (other streams, other host threads) race and must be serialised by the
  *   caller. The scratch's status word is not readable: a corrupt block table

@@ -330,6 +330,12 @@ extern "C" int32_t paged_attn_step_noalloc(const pa_plan* plan, const float* q, 
   const char* who = "paged_attn_step_noalloc";
   int32_t rc = check_plan(plan, who);
   if (rc) return rc;
+  // the single launch needs its counters at zero when it starts; in the
+  // shared scratch a two-launch plan of a smaller batch writes partials where
+  // a fused plan's counters lie, so no call here can promise that
+  if (plan->fused)
+    return fail(PA_ERR_INVALID, "%s: a fused plan needs counters that start at zero, which the shared static "
+                "scratch does not keep (set fused = 0, or use paged_attn_step with a workspace)", who);
   if (plan->ws_bytes > kNoAllocScratchBytes)
     return fail(PA_ERR_INVALID, "%s: the plan needs %llu bytes of workspace, the static scratch holds %llu",
                 who, (unsigned long long)plan->ws_bytes, (unsigned long long)kNoAllocScratchBytes);

@@ -272,6 +272,19 @@ def test_noalloc_step_refuses_plans_beyond_its_scratch_before_any_launch():
     assert "paged_attn_step_noalloc" in pa.pa_last_error() and "static scratch" in pa.pa_last_error()
 
 
+def test_noalloc_step_refuses_fused_plans_before_any_launch():
+    """A fused plan's counters must start at zero, which the shared static
+    scratch does not keep: paged_attn_step_noalloc refuses it before it
+    touches the device."""
+    plan = pa.paged_attn_plan(_shape(B=8), 32768, num_cus=256)
+    assert plan.path == 2 and plan.direct == 0
+    plan.fused = 1
+    fake = 0x1000
+    rc = pa.lib.paged_attn_step_noalloc(ctypes.byref(plan), fake, fake, fake, fake, fake, fake, 0)
+    assert rc == pa.PA_ERR_INVALID
+    assert "paged_attn_step_noalloc" in pa.pa_last_error() and "start at zero" in pa.pa_last_error()
+
+
 def test_direct_plan_merge_is_a_no_op():
     plan = pa.paged_attn_plan(_shape(B=1), 100, num_cus=256)
     assert plan.direct == 1
